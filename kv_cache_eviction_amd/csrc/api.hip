@@ -1,0 +1,352 @@
+// C ABI of the chunked H2O step: validation, state bookkeeping, workspace
+// carving and kernel orchestration.  All device work is enqueued on the
+// caller's stream; nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <string.h>
+
+#include <vector>
+
+#include "h2o.h"
+#include "h2o_launch.h"
+
+namespace {
+
+constexpr int kTimedKernels = 4;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t partial_off, partial_bytes;
+  size_t lse_off, lse_bytes;
+  size_t counters_off, counters_bytes;   // B*Hkv counters followed by the status word
+  size_t total;
+};
+
+int max_len(const h2o_config* c) { return c->max_chunk > c->max_prefill ? c->max_chunk : c->max_prefill; }
+
+Layout layout_of(const h2o_config* c) {
+  Layout L;
+  const size_t heads = static_cast<size_t>(c->batch) * c->n_kv_heads;
+  const size_t smax = static_cast<size_t>(max_len(c));
+  L.partial_off = 0;
+  L.partial_bytes = align_up(heads * h2o::score_row_splits_max() * (c->cache_slots + smax) * sizeof(float));
+  L.lse_off = L.partial_off + L.partial_bytes;
+  L.lse_bytes = align_up(static_cast<size_t>(c->batch) * c->n_q_heads * smax * sizeof(float));
+  L.counters_off = L.lse_off + L.lse_bytes;
+  L.counters_bytes = align_up((heads + 1) * sizeof(int32_t));
+  L.total = L.counters_off + L.counters_bytes;
+  return L;
+}
+
+struct TimedLaunch {
+  int kernel;
+  hipEvent_t start, stop;
+};
+
+}  // namespace
+
+struct h2o_cache {
+  h2o_config cfg;
+  void* k_cache;
+  void* v_cache;
+  float* scores;
+  int32_t* pos;
+  char* ws;
+  Layout lay;
+  int64_t T;
+  int filled;          // slots [0, filled) hold tokens, the rest are free; -1: unknown (adopted)
+  int32_t last_hip_error;
+  bool timing;
+  std::vector<TimedLaunch> pending;
+  std::vector<hipEvent_t> event_pool;
+  double total_ms[kTimedKernels];
+  int64_t launches[kTimedKernels];
+};
+
+namespace {
+
+hipEvent_t take_event(h2o_cache* c) {
+  if (!c->event_pool.empty()) {
+    hipEvent_t e = c->event_pool.back();
+    c->event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` on `st`; when timing is on, brackets it with events.
+template <class F>
+h2o_status timed(h2o_cache* c, int kid, hipStream_t st, F&& launch) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (c && c->timing) {
+    a = take_event(c);
+    b = take_event(c);
+    if (a && b && hipEventRecord(a, st) != hipSuccess) {
+      c->event_pool.push_back(a);
+      c->event_pool.push_back(b);
+      a = b = nullptr;
+    }
+  }
+  hipError_t e = launch();
+  if (a && b) {
+    if (hipEventRecord(b, st) == hipSuccess) {
+      c->pending.push_back({kid, a, b});
+    } else {
+      c->event_pool.push_back(a);
+      c->event_pool.push_back(b);
+    }
+  }
+  if (e != hipSuccess) {
+    if (c) c->last_hip_error = static_cast<int32_t>(e);
+    return H2O_ERR_HIP;
+  }
+  return H2O_OK;
+}
+
+h2o::StepShape shape_of(const h2o_cache* c, int s) {
+  const h2o_config& g = c->cfg;
+  h2o::StepShape sh;
+  sh.B = g.batch;
+  sh.Hq = g.n_q_heads;
+  sh.Hkv = g.n_kv_heads;
+  sh.D = g.head_dim;
+  sh.S = s;
+  sh.M = g.cache_slots;
+  sh.W = g.recent_window;
+  sh.n_cache = c->filled >= 0 ? c->filled : g.cache_slots;
+  sh.scale = g.softmax_scale > 0.f ? g.softmax_scale : 1.0f / sqrtf(static_cast<float>(g.head_dim));
+  return sh;
+}
+
+h2o_status run_step(h2o_cache* c, const void* q, const void* k, const void* v, int32_t s, void* out,
+                    float* lse, int32_t* slots_out, float* step_mass, void* k_old, void* v_old,
+                    hipStream_t st) {
+  const h2o::StepShape sh = shape_of(c, s);
+  float* lse_buf = lse ? lse : reinterpret_cast<float*>(c->ws + c->lay.lse_off);
+  float* partial = reinterpret_cast<float*>(c->ws + c->lay.partial_off);
+  int32_t* counters = reinterpret_cast<int32_t*>(c->ws + c->lay.counters_off);
+  int32_t* status = counters + static_cast<size_t>(c->cfg.batch) * c->cfg.n_kv_heads;
+  const int dtype = c->cfg.dtype;
+
+  h2o::AttnArgs aa{q, c->k_cache, c->v_cache, c->pos, k, v, out, lse_buf};
+  h2o_status r = timed(c, 0, st, [&] { return h2o::launch_attn_fwd(sh, aa, dtype, st); });
+  if (r != H2O_OK) return r;
+  const int R = h2o::score_row_splits(sh, dtype);
+  h2o::ScoreArgs sa{q, c->k_cache, k, lse_buf, partial, R};
+  r = timed(c, 1, st, [&] { return h2o::launch_score(sh, sa, dtype, st); });
+  if (r != H2O_OK) return r;
+  h2o::SelectArgs xa{c->k_cache, c->v_cache, c->scores, c->pos, k, v, partial, R,
+                     slots_out, step_mass, k_old, v_old, counters, status,
+                     static_cast<int32_t>(c->T)};
+  r = timed(c, 2, st, [&] { return h2o::launch_select_scatter(sh, xa, dtype, st); });
+  if (r != H2O_OK) return r;
+  c->T += s;
+  if (c->filled >= 0) c->filled = c->filled + s > c->cfg.cache_slots ? c->cfg.cache_slots : c->filled + s;
+  return H2O_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* h2o_status_str(h2o_status s) {
+  switch (s) {
+    case H2O_OK: return "ok";
+    case H2O_ERR_NULL: return "null pointer";
+    case H2O_ERR_CONFIG: return "invalid config";
+    case H2O_ERR_SHAPE: return "chunk length out of range";
+    case H2O_ERR_STATE: return "call not allowed in this cache state";
+    case H2O_ERR_WORKSPACE: return "workspace too small";
+    case H2O_ERR_HIP: return "HIP error";
+    case H2O_ERR_UNSUPPORTED: return "unsupported request";
+  }
+  return "unknown status";
+}
+
+h2o_status h2o_validate_config(const h2o_config* c) {
+  if (!c) return H2O_ERR_NULL;
+  if (c->batch < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1) return H2O_ERR_CONFIG;
+  if (c->n_q_heads % c->n_kv_heads != 0) return H2O_ERR_CONFIG;
+  if (c->head_dim != 64 && c->head_dim != 128) return H2O_ERR_CONFIG;
+  if (c->dtype != H2O_BF16 && c->dtype != H2O_FP32) return H2O_ERR_CONFIG;
+  if (c->cache_slots < 1 || c->cache_slots > 16384) return H2O_ERR_CONFIG;
+  if (c->recent_window < 0 || c->max_chunk < 1 || c->max_prefill < 1) return H2O_ERR_CONFIG;
+  if (c->max_prefill > c->cache_slots) return H2O_ERR_CONFIG;
+  if (static_cast<int64_t>(c->cache_slots) - c->recent_window < c->max_chunk) return H2O_ERR_CONFIG;
+  if (c->max_chunk > 65536 || c->max_prefill > 65536) return H2O_ERR_CONFIG;
+  if (!(c->softmax_scale == c->softmax_scale)) return H2O_ERR_CONFIG;   // NaN
+  // every tensor offset must fit in int64 and every chunk tensor below 2^31 elements
+  const int64_t big = static_cast<int64_t>(c->batch) * c->n_q_heads * max_len(c) * c->head_dim;
+  if (big >= (int64_t{1} << 31)) return H2O_ERR_CONFIG;
+  return H2O_OK;
+}
+
+size_t h2o_workspace_bytes(const h2o_config* c) {
+  if (h2o_validate_config(c) != H2O_OK) return 0;
+  return layout_of(c).total;
+}
+
+h2o_status h2o_cache_init(const h2o_config* cfg, void* k_cache, void* v_cache, float* scores,
+                          int32_t* positions, void* workspace, size_t workspace_bytes, int32_t adopt,
+                          int64_t tokens_seen, void* stream, h2o_cache** out) {
+  if (!cfg || !k_cache || !v_cache || !scores || !positions || !workspace || !out) return H2O_ERR_NULL;
+  *out = nullptr;
+  h2o_status r = h2o_validate_config(cfg);
+  if (r != H2O_OK) return r;
+  if (tokens_seen < 0 || (!adopt && tokens_seen != 0) || tokens_seen > INT32_MAX) return H2O_ERR_STATE;
+  const Layout lay = layout_of(cfg);
+  if (workspace_bytes < lay.total) return H2O_ERR_WORKSPACE;
+  h2o_cache* c = new h2o_cache();
+  c->cfg = *cfg;
+  c->k_cache = k_cache;
+  c->v_cache = v_cache;
+  c->scores = scores;
+  c->pos = positions;
+  c->ws = static_cast<char*>(workspace);
+  c->lay = lay;
+  c->T = tokens_seen;
+  c->filled = adopt ? -1 : 0;
+  c->last_hip_error = 0;
+  c->timing = false;
+  for (int i = 0; i < kTimedKernels; ++i) {
+    c->total_ms[i] = 0.0;
+    c->launches[i] = 0;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t n_slots = static_cast<int64_t>(cfg->batch) * cfg->n_kv_heads * cfg->cache_slots;
+  const int64_t n_cnt = static_cast<int64_t>(cfg->batch) * cfg->n_kv_heads + 1;
+  int32_t* counters = reinterpret_cast<int32_t*>(c->ws + lay.counters_off);
+  r = timed(c, 3, st, [&] {
+    return h2o::launch_reset(adopt ? nullptr : scores, adopt ? nullptr : positions, adopt ? 0 : n_slots,
+                             counters, n_cnt, st);
+  });
+  if (r != H2O_OK) {
+    delete c;
+    return r;
+  }
+  *out = c;
+  return H2O_OK;
+}
+
+h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k, const void* v, int32_t n, void* out,
+                       float* lse, void* stream) {
+  if (!c || !q || !k || !v || !out) return H2O_ERR_NULL;
+  if (n < 1 || n > c->cfg.max_prefill) return H2O_ERR_SHAPE;
+  if (c->T != 0) return H2O_ERR_STATE;
+  return run_step(c, q, k, v, n, out, lse, nullptr, nullptr, nullptr, nullptr,
+                  static_cast<hipStream_t>(stream));
+}
+
+h2o_status h2o_chunk_step(h2o_cache* c, const void* q, const void* k_new, const void* v_new, int32_t s,
+                          void* out, float* lse, int32_t* slots_out, float* step_mass, void* k_old,
+                          void* v_old, void* stream) {
+  if (!c || !q || !k_new || !v_new || !out) return H2O_ERR_NULL;
+  if ((k_old == nullptr) != (v_old == nullptr)) return H2O_ERR_NULL;
+  if (s < 1 || s > c->cfg.max_chunk) return H2O_ERR_SHAPE;
+  if (c->T + s > INT32_MAX) return H2O_ERR_STATE;
+  return run_step(c, q, k_new, v_new, s, out, lse, slots_out, step_mass, k_old, v_old,
+                  static_cast<hipStream_t>(stream));
+}
+
+h2o_status h2o_get_scores(const h2o_cache* c, float* scores_out, int32_t* positions_out, void* stream) {
+  if (!c || !scores_out) return H2O_ERR_NULL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t n = static_cast<size_t>(c->cfg.batch) * c->cfg.n_kv_heads * c->cfg.cache_slots;
+  hipError_t e = hipMemcpyAsync(scores_out, c->scores, n * sizeof(float), hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess && positions_out)
+    e = hipMemcpyAsync(positions_out, c->pos, n * sizeof(int32_t), hipMemcpyDeviceToDevice, st);
+  if (e != hipSuccess) {
+    const_cast<h2o_cache*>(c)->last_hip_error = static_cast<int32_t>(e);
+    return H2O_ERR_HIP;
+  }
+  return H2O_OK;
+}
+
+int64_t h2o_tokens_seen(const h2o_cache* c) { return c ? c->T : -1; }
+
+h2o_status h2o_device_status(h2o_cache* c, void* stream, int32_t* flags) {
+  if (!c || !flags) return H2O_ERR_NULL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* status = reinterpret_cast<int32_t*>(c->ws + c->lay.counters_off) +
+                    static_cast<size_t>(c->cfg.batch) * c->cfg.n_kv_heads;
+  int32_t host = 0;
+  hipError_t e = hipMemcpyAsync(&host, status, sizeof(int32_t), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e == hipSuccess && host != 0) {
+    const int32_t zero = 0;
+    e = hipMemcpyAsync(status, &zero, sizeof(int32_t), hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+  }
+  if (e != hipSuccess) {
+    c->last_hip_error = static_cast<int32_t>(e);
+    return H2O_ERR_HIP;
+  }
+  *flags = host;
+  return H2O_OK;
+}
+
+h2o_status h2o_set_timing(h2o_cache* c, int32_t enable) {
+  if (!c) return H2O_ERR_NULL;
+  c->timing = enable != 0;
+  return H2O_OK;
+}
+
+h2o_status h2o_get_timing(h2o_cache* c, int32_t kernel_id, double* total_ms, int64_t* launches) {
+  if (!c || !total_ms || !launches) return H2O_ERR_NULL;
+  if (kernel_id < 0 || kernel_id >= kTimedKernels) return H2O_ERR_SHAPE;
+  for (const TimedLaunch& t : c->pending) {
+    hipError_t e = hipEventSynchronize(t.stop);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.start, t.stop);
+    if (e != hipSuccess) {
+      c->last_hip_error = static_cast<int32_t>(e);
+      return H2O_ERR_HIP;
+    }
+    c->total_ms[t.kernel] += ms;
+    c->launches[t.kernel] += 1;
+    c->event_pool.push_back(t.start);
+    c->event_pool.push_back(t.stop);
+  }
+  c->pending.clear();
+  *total_ms = c->total_ms[kernel_id];
+  *launches = c->launches[kernel_id];
+  return H2O_OK;
+}
+
+void h2o_cache_destroy(h2o_cache* c) {
+  if (!c) return;
+  for (const TimedLaunch& t : c->pending) {
+    (void)hipEventSynchronize(t.stop);
+    (void)hipEventDestroy(t.start);
+    (void)hipEventDestroy(t.stop);
+  }
+  for (hipEvent_t e : c->event_pool) (void)hipEventDestroy(e);
+  delete c;
+}
+
+int32_t h2o_last_hip_error(const h2o_cache* c) { return c ? c->last_hip_error : 0; }
+
+size_t h2o_backward_workspace_bytes(const h2o_config* cfg, int32_t s) {
+  (void)cfg;
+  (void)s;
+  return 0;
+}
+
+h2o_status h2o_chunk_backward(const h2o_config* cfg, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* positions, const void* k_new,
+                              const void* v_new, int32_t s, const void* out, const float* lse,
+                              const void* d_out, void* dq, void* dk_cache, void* dv_cache,
+                              void* dk_new, void* dv_new, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  (void)cfg; (void)q; (void)k_cache; (void)v_cache; (void)positions; (void)k_new; (void)v_new;
+  (void)s; (void)out; (void)lse; (void)d_out; (void)dq; (void)dk_cache; (void)dv_cache;
+  (void)dk_new; (void)dv_new; (void)workspace; (void)workspace_bytes; (void)stream;
+  return H2O_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

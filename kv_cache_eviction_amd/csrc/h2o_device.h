@@ -1,0 +1,65 @@
+// Device-side helpers shared by the gfx950 kernels of the H2O step:
+// vector types for the CDNA4 bf16 MFMA operands, fragment loads, and the
+// small math primitives (exp2 on v_exp_f32, packed bf16 conversion).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace h2o {
+
+typedef uint16_t bf16_t;  // storage type of bf16 tensors (bit pattern)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// v_mfma_f32_32x32x16_bf16 (CDNA4).  Lane l supplies A[row l%32][k 8(l/32)..+8]
+// and B[k 8(l/32)..+8][col l%32]; the 16 accumulators of lane l hold
+// C[8(r/4) + 4(l/32) + r%4][l%32], r = 0..15.
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const bf16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ u32x4 load_u32x4(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void store_u32x4(void* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(f32x8 v) {
+  return __builtin_convertvector(v, bf16x8);
+}
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v) {
+  return __builtin_convertvector(v, bf16x4);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  return z;
+}
+
+// Value of lane (l ^ 32): the other half of a 32x32 MFMA accumulator column.
+__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32); }
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+}  // namespace h2o

@@ -1,0 +1,68 @@
+// Host-side launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace h2o {
+
+// Shapes of one step.  Cache tensors are [B,Hkv,M,D]; chunk tensors
+// [B,H*,S,D]; `n_cache` leading slots are scanned (slots beyond hold nothing).
+struct StepShape {
+  int B, Hq, Hkv, D, S, M, W;
+  int n_cache;
+  float scale;      // softmax scale applied to q.k
+};
+
+struct AttnArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* pos;
+  const void* k_new;
+  const void* v_new;
+  void* out;
+  float* lse;
+};
+
+struct ScoreArgs {
+  const void* q;
+  const void* k_cache;
+  const void* k_new;
+  const float* lse;
+  float* partial;   // [B*Hkv][R][M + S]
+  int R;            // row splits
+};
+
+struct SelectArgs {
+  void* k_cache;
+  void* v_cache;
+  float* scores;
+  int32_t* pos;
+  const void* k_new;
+  const void* v_new;
+  const float* partial;
+  int R;
+  int32_t* slots_out;   // nullable
+  float* step_mass;     // nullable
+  void* k_old;          // nullable
+  void* v_old;          // nullable
+  int32_t* counters;    // [B*Hkv], zero between launches
+  int32_t* status;      // device status word
+  int32_t T;            // tokens seen before the chunk
+};
+
+enum Dtype { kBF16 = 0, kFP32 = 1 };
+
+hipError_t launch_attn_fwd(const StepShape& sh, const AttnArgs& a, int dtype, hipStream_t st);
+hipError_t launch_score(const StepShape& sh, const ScoreArgs& a, int dtype, hipStream_t st);
+hipError_t launch_select_scatter(const StepShape& sh, const SelectArgs& a, int dtype, hipStream_t st);
+hipError_t launch_reset(float* scores, int32_t* pos, int64_t n_slots, int32_t* counters,
+                        int64_t n_counters, hipStream_t st);
+
+// Row splits the score kernel uses for a step of this shape (host heuristic).
+int score_row_splits(const StepShape& sh, int dtype);
+// Upper bound of score_row_splits over every S <= s_max (workspace sizing).
+int score_row_splits_max();
+
+}  // namespace h2o

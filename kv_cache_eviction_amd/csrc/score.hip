@@ -1,0 +1,265 @@
+// H2O score accumulation (step 2 of h2o_chunk_step): the attention mass
+// every key received in this step, summed over the chunk's queries and the
+// G query heads of its KV group -- the "summed attention weights" served
+// alongside the SDPA kernel ("Learning how to Forget: Fine-tuning for
+// Long-Context Sparse Attention", arXiv 2608.19920, §1 ¶4 and the docshare
+// FAQ answer on H2O; the score itself is the heavy-hitter oracle of its
+// reference [72]).
+//
+// P = exp(z - lse) is recomputed from Q, K and the forward's lse (the
+// forward's online softmax cannot normalise a column before every row is
+// done), and reduced over rows without atomics: each workgroup owns a tile
+// of 256 key columns and one contiguous range of query rows (a "row split"),
+// and writes one partial sum per column.  The select kernel adds the R
+// partials of a column in a fixed order, so results are deterministic.
+//
+// bf16 path: S = Q K^T on v_mfma_f32_32x32x16_bf16 with the wave's 64 keys
+// as the B operand held in registers for the whole kernel and 32-row query
+// blocks as the A operand, staged in LDS and shared by the 4 waves.  Each
+// accumulator column belongs to one key, so the column sum is one fp32 add
+// per element inside the lane plus one exchange with lane l^32 at the end.
+#include "h2o_device.h"
+#include "h2o_launch.h"
+
+namespace h2o {
+namespace {
+
+constexpr int kCT = 256;        // key columns per workgroup (4 waves x 64)
+constexpr int kRowSplitsMax = 16;
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void score_bf16_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc,
+    const bf16_t* __restrict__ Kn, const float* __restrict__ lse,
+    float* __restrict__ partial, int Hq, int Hkv, int S, int M, int n_cache,
+    float c2, int n_heads, int n_ct, int n_tiles, int R) {
+  constexpr int DS = D / 16;
+  constexpr int QLD = D + 8;
+  constexpr int CPR = D / 8;
+  constexpr int NCH = 32 * CPR / 256;   // 16-byte chunks per thread per row block
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[32 * QLD];
+  __shared__ float s_lse2[32];
+  __shared__ int s_irow[32];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hf = lane >> 5, col = lane & 31;
+  const int bh = blockIdx.x % n_heads;
+  const int rest = static_cast<int>(blockIdx.x) / n_heads;
+  const int tile = rest % n_tiles, split = rest / n_tiles;
+  const int b = bh / Hkv, kvh = bh - b * Hkv;
+  const int G = Hq / Hkv;
+  const bool is_cache = tile < n_ct;
+  const int base = (is_cache ? tile : tile - n_ct) * kCT;
+  const int lim = is_cache ? n_cache : S;
+  const bf16_t* khead = is_cache ? Kc + static_cast<size_t>(bh) * M * D
+                                 : Kn + static_cast<size_t>(bh) * S * D;
+  const int key0 = base + wave * 64;          // first key of this wave
+
+  // The wave's 64 keys: B operand (lane: key column, d 8hf..+8).
+  bf16x8 kf[2][DS];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = key0 + kb * 32 + col;
+    const bool ok = key < lim;
+    const bf16_t* krow = khead + static_cast<size_t>(ok ? key : 0) * D;
+#pragma unroll
+    for (int st = 0; st < DS; ++st) {
+      const bf16x8 v = load_bf16x8(krow + 16 * st + 8 * hf);
+      kf[kb][st] = ok ? v : bf16x8{};
+    }
+  }
+
+  const int n_rows = G * S;
+  const int n_rblk = (n_rows + 31) >> 5;
+  const int blk_lo = static_cast<int>(static_cast<int64_t>(split) * n_rblk / R);
+  const int blk_hi = static_cast<int>(static_cast<int64_t>(split + 1) * n_rblk / R);
+  const bf16_t* qhead = Q + static_cast<size_t>(b * Hq + kvh * G) * S * D;  // rows g*S + i
+  const float* lhead = lse + static_cast<size_t>(b * Hq + kvh * G) * S;
+
+  // A row block contributes to chunk keys only if one of its queries i >= key0.
+  auto block_needed = [&](int blk) {
+    if (is_cache) return true;
+    const int r0 = blk * 32, r1 = min(r0 + 31, n_rows - 1);
+    if (r0 / S != r1 / S) return true;        // spans two heads: i reaches S-1
+    return (r1 % S) >= base;                  // max query of the block vs first key of the tile
+  };
+
+  u32x4 qreg[NCH];
+  float lreg = 0.f;
+  int ireg = -1;
+  auto load_blk = [&](int blk) {
+    const int r0 = blk * 32;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int idx = c * 256 + tid, row = idx / CPR, dc = idx % CPR;
+      const int r = r0 + row;
+      qreg[c] = (r < n_rows) ? load_u32x4(qhead + static_cast<size_t>(r) * D + dc * 8)
+                             : u32x4{0, 0, 0, 0};
+    }
+    if (tid < 32) {
+      const int r = r0 + tid;
+      lreg = (r < n_rows) ? lhead[r] * kLog2e : __builtin_huge_valf();
+      ireg = (r < n_rows) ? r % S : -1;
+    }
+  };
+  auto store_blk = [&]() {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int idx = c * 256 + tid, row = idx / CPR, dc = idx % CPR;
+      store_u32x4(&Qs[row * QLD + dc * 8], qreg[c]);
+    }
+    if (tid < 32) {
+      s_lse2[tid] = lreg;
+      s_irow[tid] = ireg;
+    }
+  };
+
+  float cs0 = 0.f, cs1 = 0.f;     // column sums of this lane's two key columns
+  int blk = blk_lo;
+  while (blk < blk_hi && !block_needed(blk)) ++blk;
+  if (blk < blk_hi) load_blk(blk);
+  while (blk < blk_hi) {
+    __syncthreads();
+    store_blk();
+    __syncthreads();
+    int nxt = blk + 1;
+    while (nxt < blk_hi && !block_needed(nxt)) ++nxt;
+    if (nxt < blk_hi) load_blk(nxt);
+
+    if (key0 < lim) {
+      f32x16 a0 = zero16(), a1 = zero16();
+#pragma unroll
+      for (int st = 0; st < DS; ++st) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qs[col * QLD + 16 * st + 8 * hf]);
+        a0 = mfma32x32x16(qa, kf[0][st], a0);
+        a1 = mfma32x32x16(qa, kf[1][st], a1);
+      }
+      // accumulator register r of lane l: query row 8(r/4) + 4hf + r%4 of the block
+      const bool causal = !is_cache;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * hf + (r & 3);
+        const float l2 = s_lse2[row];
+        float p0 = fast_exp2(fmaf(a0[r], c2, -l2));
+        float p1 = fast_exp2(fmaf(a1[r], c2, -l2));
+        if (causal) {
+          const int qi = s_irow[row];
+          p0 = (key0 + col <= qi) ? p0 : 0.f;
+          p1 = (key0 + 32 + col <= qi) ? p1 : 0.f;
+        }
+        cs0 += p0;
+        cs1 += p1;
+      }
+    }
+    blk = nxt;
+  }
+  cs0 += xor32(cs0);
+  cs1 += xor32(cs1);
+  if (hf == 0) {
+    float* out = partial + (static_cast<size_t>(bh) * R + split) * (M + S) + (is_cache ? 0 : M);
+    const int k0 = key0 + col, k1 = key0 + 32 + col;
+    if (k0 < lim) out[k0] = cs0;
+    if (k1 < lim) out[k1] = cs1;
+  }
+}
+
+// fp32: one thread per key column, query rows streamed through LDS.
+template <int D>
+__global__ __launch_bounds__(64) void score_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ Kc, const float* __restrict__ Kn,
+    const float* __restrict__ lse, float* __restrict__ partial, int Hq, int Hkv, int S, int M,
+    int n_cache, float c2, int n_heads, int n_ct, int n_tiles) {
+  constexpr int RT = 16;
+  __shared__ float Qs[RT][D];
+  __shared__ float ls[RT];
+  __shared__ int is[RT];
+  const int lane = threadIdx.x;
+  const int bh = blockIdx.x % n_heads;
+  const int tile = static_cast<int>(blockIdx.x) / n_heads;
+  const int b = bh / Hkv, kvh = bh - b * Hkv;
+  const int G = Hq / Hkv;
+  const bool is_cache = tile < n_ct;
+  const int key = (is_cache ? tile : tile - n_ct) * 64 + lane;
+  const int lim = is_cache ? n_cache : S;
+  const bool ok = key < lim;
+  const float* krow = (is_cache ? Kc + static_cast<size_t>(bh) * M * D : Kn + static_cast<size_t>(bh) * S * D) +
+                      static_cast<size_t>(ok ? key : 0) * D;
+  float k[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) k[e] = krow[e];
+  const int n_rows = G * S;
+  const float* qhead = Q + static_cast<size_t>(b * Hq + kvh * G) * S * D;
+  const float* lhead = lse + static_cast<size_t>(b * Hq + kvh * G) * S;
+  float cs = 0.f;
+  for (int r0 = 0; r0 < n_rows; r0 += RT) {
+    __syncthreads();
+    for (int idx = lane; idx < RT * D; idx += 64) {
+      const int rr = idx / D, e = idx % D;
+      Qs[rr][e] = (r0 + rr < n_rows) ? qhead[static_cast<size_t>(r0 + rr) * D + e] : 0.f;
+    }
+    if (lane < RT) {
+      const int r = r0 + lane;
+      ls[lane] = (r < n_rows) ? lhead[r] * kLog2e : __builtin_huge_valf();
+      is[lane] = (r < n_rows) ? r % S : -1;
+    }
+    __syncthreads();
+    for (int rr = 0; rr < RT; ++rr) {
+      if (!is_cache && key > is[rr]) continue;
+      float z = 0.f;
+#pragma unroll
+      for (int e = 0; e < D; ++e) z = fmaf(Qs[rr][e], k[e], z);
+      cs += fast_exp2(fmaf(z, c2, -ls[rr]));
+    }
+  }
+  if (ok) partial[static_cast<size_t>(bh) * (M + S) + (is_cache ? 0 : M) + key] = cs;
+}
+
+}  // namespace
+
+int score_row_splits_max() { return kRowSplitsMax; }
+
+int score_row_splits(const StepShape& sh, int dtype) {
+  if (dtype != kBF16) return 1;
+  const int n_heads = sh.B * sh.Hkv;
+  const int n_tiles = (sh.n_cache + kCT - 1) / kCT + (sh.S + kCT - 1) / kCT;
+  const int n_rblk = (sh.Hq / sh.Hkv * sh.S + 31) / 32;
+  const int target = 1024;   // about 4 workgroups per CU
+  int R = (target + n_heads * n_tiles - 1) / (n_heads * n_tiles);
+  R = R < 1 ? 1 : R;
+  R = R > kRowSplitsMax ? kRowSplitsMax : R;
+  R = R > n_rblk ? n_rblk : R;
+  return R;
+}
+
+hipError_t launch_score(const StepShape& sh, const ScoreArgs& a, int dtype, hipStream_t st) {
+  const int n_heads = sh.B * sh.Hkv;
+  const float c2 = sh.scale * kLog2e;
+  if (dtype == kBF16) {
+    const int n_ct = (sh.n_cache + kCT - 1) / kCT;
+    const int n_tiles = n_ct + (sh.S + kCT - 1) / kCT;
+    const dim3 grid(n_heads * n_tiles * a.R), block(256);
+#define H2O_LAUNCH_SCORE(DD)                                                                      \
+  hipLaunchKernelGGL(score_bf16_kernel<DD>, grid, block, 0, st, static_cast<const bf16_t*>(a.q), \
+                     static_cast<const bf16_t*>(a.k_cache), static_cast<const bf16_t*>(a.k_new), \
+                     a.lse, a.partial, sh.Hq, sh.Hkv, sh.S, sh.M, sh.n_cache, c2, n_heads, n_ct, \
+                     n_tiles, a.R)
+    if (sh.D == 128) H2O_LAUNCH_SCORE(128);
+    else H2O_LAUNCH_SCORE(64);
+#undef H2O_LAUNCH_SCORE
+  } else {
+    const int n_ct = (sh.n_cache + 63) / 64;
+    const int n_tiles = n_ct + (sh.S + 63) / 64;
+    const dim3 grid(n_heads * n_tiles), block(64);
+#define H2O_LAUNCH_SCORE32(DD)                                                                  \
+  hipLaunchKernelGGL(score_f32_kernel<DD>, grid, block, 0, st, static_cast<const float*>(a.q), \
+                     static_cast<const float*>(a.k_cache), static_cast<const float*>(a.k_new), \
+                     a.lse, a.partial, sh.Hq, sh.Hkv, sh.S, sh.M, sh.n_cache, c2, n_heads, n_ct, \
+                     n_tiles)
+    if (sh.D == 128) H2O_LAUNCH_SCORE32(128);
+    else H2O_LAUNCH_SCORE32(64);
+#undef H2O_LAUNCH_SCORE32
+  }
+  return hipGetLastError();
+}
+
+}  // namespace h2o

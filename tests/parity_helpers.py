@@ -1,0 +1,190 @@
+"""Helpers of the GPU parity tests: drive the C ABI through the Python
+binding, snapshot the device state and compare one step with the fp64
+oracle started from that same state (teacher forcing).
+
+Tolerances (floating point, bf16 inputs with fp32 accumulation):
+* attention output: max |dO| <= 2e-2 and ||dO||_2 / ||O_ref||_2 <= 5e-3 over
+  the checked heads;
+* logsumexp: max |d lse| <= 1e-3 (fp32 row sums of exact bf16 products);
+* scores and step masses: relative error <= 1e-3 on every filled slot
+  (masses with a 1e-9 absolute floor for contributions that underflow);
+* eviction: the written-slot set equals the oracle's, except where the
+  oracle's score gap at the cut is below 1e-5, in which case every slot on
+  which they differ must lie within 1e-5 of the cut score;
+* K/V rows, positions and slot ids: bit-exact where the slot sets agree.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from kv_cache_eviction_amd import workloads as wl
+from oracle import h2o_oracle as orc
+
+O_MAX_ABS = 2e-2
+O_REL_RMS = 5e-3
+LSE_MAX_ABS = 1e-3
+SCORE_REL = 1e-3
+TIE_GAP = 1e-5
+
+
+def h2o_mod():
+    from kv_cache_eviction_amd import h2o
+    return h2o
+
+
+def cfg_of(w: wl.Workload, **kw):
+    h2o = h2o_mod()
+    d = dict(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,
+             cache_slots=w.cache_slots, recent_window=w.recent_window, max_chunk=w.chunk,
+             max_prefill=w.prefill, dtype=w.dtype)
+    d.update(kw)
+    return h2o.H2OConfig(**d)
+
+
+def to_device(a: np.ndarray) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+class Snapshot:
+    """Host copy of the device state; per-(b, head) float64 views on demand."""
+
+    def __init__(self, cache):
+        torch.cuda.synchronize()
+        self.K = cache.k_cache.cpu()
+        self.V = cache.v_cache.cpu()
+        self.sigma = cache.scores.cpu()
+        self.pos = cache.positions.cpu()
+        self.T = cache.tokens_seen
+
+    def head(self, b, h):
+        """State of one (b, KV head) as oracle arrays with leading [1, 1] dims."""
+        f = lambda t: t[b:b + 1, h:h + 1].double().numpy()
+        return dict(K=f(self.K), V=f(self.V), sigma=f(self.sigma),
+                    pos=self.pos[b:b + 1, h:h + 1].numpy().astype(np.int64))
+
+
+def snapshot(cache) -> Snapshot:
+    return Snapshot(cache)
+
+
+def out_errors(got: np.ndarray, ref: np.ndarray):
+    diff = got - ref
+    max_abs = float(np.abs(diff).max())
+    rel_rms = float(np.linalg.norm(diff) / max(np.linalg.norm(ref), 1e-30))
+    return max_abs, rel_rms
+
+
+def compare_targets(R_gpu, R_ref, sig_acc, evicted_ref, gap):
+    """Slot sets agree, or differ only within the near-tie band at the cut.
+    Returns the set of slots on which they differ."""
+    a, r = set(int(x) for x in R_gpu), set(int(x) for x in R_ref)
+    assert len(a) == len(R_gpu), "duplicate target slots"
+    if a == r:
+        assert list(R_gpu) == sorted(R_gpu)
+        return set()
+    assert gap < TIE_GAP, f"eviction differs with cut gap {gap:.3e} >= {TIE_GAP}"
+    cut = sig_acc[evicted_ref[-1]]
+    diff = a ^ r
+    for m in diff:
+        assert abs(sig_acc[m] - cut) < TIE_GAP, f"slot {m} differs but is {abs(sig_acc[m]-cut):.3e} from the cut"
+    return diff
+
+
+def run_and_check_step(cache, cfg, q_np, k_np, v_np, heads, W, scale=None, prefill=False):
+    """One GPU step (prefill or chunk step) checked against the oracle on the
+    (b, kv head) pairs in `heads`.  Returns a dict of error figures."""
+    h2o = h2o_mod()
+    B, Hq, S, d = q_np.shape
+    Hkv = k_np.shape[1]
+    G = Hq // Hkv
+    M = cfg.cache_slots
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    before = snapshot(cache)
+    q_t, k_t, v_t = to_device(q_np), to_device(k_np), to_device(v_np)
+    out = torch.empty_like(q_t)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    slots = torch.empty((B, Hkv, S), dtype=torch.int32, device="cuda")
+    mass = torch.empty((B, Hkv, M + S), dtype=torch.float32, device="cuda")
+    k_old = torch.empty_like(k_t)
+    v_old = torch.empty_like(v_t)
+    if prefill:
+        cache.prefill(q_t, k_t, v_t, out, lse)
+    else:
+        cache.chunk_step(q_t, k_t, v_t, out, lse, slots, mass, k_old, v_old)
+    after = snapshot(cache)
+    assert after.T == before.T + S
+    out_g, lse_g = to_f64(out), to_f64(lse)
+    slots_g = slots.cpu().numpy()
+    mass_g = to_f64(mass)
+    kold_g, vold_g = to_f64(k_old), to_f64(v_old)
+    qf, kf, vf = wl.stored_to_f64(q_np), wl.stored_to_f64(k_np), wl.stored_to_f64(v_np)
+    errs = dict(o_max_abs=0.0, o_rel_rms=0.0, lse_max_abs=0.0, score_rel=0.0, mass_rel=0.0,
+                tie_exempt=0, min_gap=math.inf)
+    o_got, o_ref = [], []
+    for (b, h) in heads:
+        hs = slice(h * G, (h + 1) * G)
+        st = before.head(b, h)
+        now = after.head(b, h)
+        ref = orc.chunk_step(st["K"], st["V"], st["sigma"], st["pos"], before.T,
+                             qf[b:b + 1, hs], kf[b:b + 1, h:h + 1], vf[b:b + 1, h:h + 1], W, scale)
+        o_got.append(out_g[b, hs])
+        o_ref.append(ref["out"][0])
+        errs["lse_max_abs"] = max(errs["lse_max_abs"], float(np.abs(lse_g[b, hs] - ref["lse"][0]).max()))
+        valid = st["pos"][0, 0] >= 0
+        sig_acc = st["sigma"][0, 0] + ref["delta_sigma"][0, 0]
+        R_ref = ref["targets"][0, 0]
+        gap = ref["cut_gap"][0, 0]
+        errs["min_gap"] = min(errs["min_gap"], gap)
+        if prefill:
+            R_gpu = np.sort(np.flatnonzero(now["pos"][0, 0] >= before.T))
+            diff = compare_targets(R_gpu, R_ref, sig_acc, ref["evicted"][0][0], gap)
+        else:
+            R_gpu = slots_g[b, h]
+            diff = compare_targets(R_gpu, R_ref, sig_acc, ref["evicted"][0][0], gap)
+            # the step's mass: filled slots and chunk keys
+            dm = mass_g[b, h, :M]
+            dref = ref["delta_sigma"][0, 0][valid]
+            rel = (np.abs(dm[valid] - dref) - 1e-9) / np.maximum(dref, 1e-30)
+            mu_rel = (np.abs(mass_g[b, h, M:] - ref["mu"][0, 0]) - 1e-9) / ref["mu"][0, 0]
+            errs["mass_rel"] = max(errs["mass_rel"], float(rel.max(initial=0.0)), float(mu_rel.max()))
+            assert (dm[~valid] == 0).all()
+            # overwritten rows (delta): zeros where a free slot was filled
+            for j, m in enumerate(R_gpu):
+                if m in diff:
+                    continue
+                was_free = st["pos"][0, 0, m] < 0
+                exp_k = 0.0 if was_free else st["K"][0, 0, m]
+                exp_v = 0.0 if was_free else st["V"][0, 0, m]
+                assert np.array_equal(kold_g[b, h, j], np.broadcast_to(exp_k, (d,)))
+                assert np.array_equal(vold_g[b, h, j], np.broadcast_to(exp_v, (d,)))
+        errs["tie_exempt"] += len(diff)
+        keep = np.ones(M, dtype=bool)
+        for m in diff:
+            keep[m] = False
+        # new state: positions and K/V rows exact, scores within SCORE_REL
+        np.testing.assert_array_equal(now["pos"][0, 0][keep], ref["pos"][0, 0][keep])
+        np.testing.assert_array_equal(now["K"][0, 0][keep], ref["K"][0, 0][keep])
+        np.testing.assert_array_equal(now["V"][0, 0][keep], ref["V"][0, 0][keep])
+        nv = keep & (ref["pos"][0, 0] >= 0)
+        srel = np.abs(now["sigma"][0, 0][nv] - ref["sigma"][0, 0][nv]) / ref["sigma"][0, 0][nv]
+        errs["score_rel"] = max(errs["score_rel"], float(srel.max(initial=0.0)))
+    errs["o_max_abs"], errs["o_rel_rms"] = out_errors(np.stack(o_got), np.stack(o_ref))
+    return errs
+
+
+def assert_within(errs, what=""):
+    assert errs["o_max_abs"] <= O_MAX_ABS, (what, errs)
+    assert errs["o_rel_rms"] <= O_REL_RMS, (what, errs)
+    assert errs["lse_max_abs"] <= LSE_MAX_ABS, (what, errs)
+    assert errs["score_rel"] <= SCORE_REL, (what, errs)
+    assert errs["mass_rel"] <= SCORE_REL, (what, errs)

@@ -1,0 +1,92 @@
+"""Host-only checks of the C ABI library: it loads, exports every symbol that
+include/h2o.h declares, and validates configs (no GPU call is made)."""
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib_module():
+    from kv_cache_eviction_amd import build_lib
+    if not os.path.exists(build_lib.LIB):
+        build_lib.build(verbose=False)
+    from kv_cache_eviction_amd import h2o
+    return h2o
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "h2o.h")).read()
+    return sorted(set(re.findall(r"H2O_API\s+[\w\s\*]+?\b(h2o_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    h2o = _lib_module()
+    declared = _declared()
+    assert len(declared) >= 15
+    assert sorted(h2o.EXPORTED) == declared
+    for name in declared:
+        assert hasattr(h2o._lib, name), name
+
+
+def _cfg(**kw):
+    h2o = _lib_module()
+    base = dict(batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, cache_slots=2048,
+                recent_window=256, max_chunk=1024, max_prefill=2048, dtype="bf16")
+    base.update(kw)
+    return h2o.H2OConfig(**base)
+
+
+def test_named_workload_configs_validate():
+    h2o = _lib_module()
+    from kv_cache_eviction_amd.workloads import WORKLOADS
+    for w in WORKLOADS.values():
+        cfg = h2o.H2OConfig(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.cache_slots,
+                            w.recent_window, w.chunk, w.prefill, w.dtype)
+        assert h2o.h2o_validate_config(cfg) == h2o.H2O_OK, w.name
+        assert h2o.h2o_workspace_bytes(cfg) > 0
+
+
+@pytest.mark.parametrize("kw", [
+    dict(n_q_heads=30),                 # Hq % Hkv != 0
+    dict(head_dim=96),
+    dict(dtype_code=9),
+    dict(recent_window=1500),           # M - W < max_chunk
+    dict(max_prefill=4096),             # > M
+    dict(cache_slots=20000),
+    dict(batch=0),
+    dict(max_chunk=0),
+    dict(recent_window=-1),
+    dict(softmax_scale=math.nan),
+])
+def test_invalid_configs_are_rejected(kw):
+    h2o = _lib_module()
+    if "dtype_code" in kw:
+        c = _cfg().c()
+        c.dtype = kw["dtype_code"]
+        import ctypes
+        assert h2o._lib.h2o_validate_config(ctypes.byref(c)) == h2o.H2O_ERR_CONFIG
+        assert h2o._lib.h2o_workspace_bytes(ctypes.byref(c)) == 0
+        return
+    cfg = _cfg(**kw)
+    assert h2o.h2o_validate_config(cfg) == h2o.H2O_ERR_CONFIG
+    assert h2o.h2o_workspace_bytes(cfg) == 0
+
+
+def test_null_config_and_status_strings():
+    h2o = _lib_module()
+    assert h2o._lib.h2o_validate_config(None) == h2o.H2O_ERR_NULL
+    for s in range(8):
+        assert h2o.status_str(s) and h2o.status_str(s) != "unknown status"
+    assert h2o.status_str(99) == "unknown status"
+
+
+def test_null_handle_calls_fail_cleanly():
+    h2o = _lib_module()
+    assert h2o._lib.h2o_prefill(None, None, None, None, 4, None, None, None) == h2o.H2O_ERR_NULL
+    assert h2o._lib.h2o_chunk_step(None, None, None, None, 4, None, None, None, None, None, None,
+                                   None) == h2o.H2O_ERR_NULL
+    assert h2o._lib.h2o_tokens_seen(None) == -1
+    assert h2o._lib.h2o_last_hip_error(None) == 0

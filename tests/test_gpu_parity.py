@@ -1,0 +1,275 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Every checked step is teacher-forced: the oracle starts from the GPU's own
+state before the step (exact in float64), so one near-tie at an eviction cut
+cannot fork the rest of the comparison.  Sizes span several tiles and ragged
+tails; the named workloads run at full size with sampled steps and heads.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from kv_cache_eviction_amd import workloads as wl
+from oracle import h2o_oracle as orc
+from tests.parity_helpers import (assert_within, cfg_of, run_and_check_step, snapshot, to_device,
+                                  to_f64, h2o_mod)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _run(w: wl.Workload, seed: int, check_steps, heads, cfg_kw=None, max_steps=None):
+    """Runs workload `w` on the GPU; checks the listed chunk indices (0 = prefill)."""
+    h2o = h2o_mod()
+    cfg = cfg_of(w, **(cfg_kw or {}))
+    cache = h2o.H2OCache(cfg)
+    hh = wl.heavy_hitters(w, seed)
+    n_chunks = w.n_chunks if max_steps is None else min(w.n_chunks, max_steps + 1)
+    worst = {}
+    for c in range(n_chunks):
+        q, k, v = wl.chunk_inputs(w, seed, c, hh=hh)
+        if c in check_steps:
+            _say(f"[{w.name}] check chunk {c}")
+            errs = run_and_check_step(cache, cfg, q, k, v, heads, w.recent_window, prefill=(c == 0))
+            assert_within(errs, f"{w.name} chunk {c}")
+            for key, val in errs.items():
+                worst[key] = max(worst.get(key, 0), val) if key != "min_gap" else min(worst.get(key, math.inf), val)
+        else:
+            qt, kt, vt = to_device(q), to_device(k), to_device(v)
+            if c == 0:
+                cache.prefill(qt, kt, vt)
+            else:
+                cache.chunk_step(qt, kt, vt)
+    torch.cuda.synchronize()
+    assert h2o.h2o_device_status(cache.handle) == 0
+    _say(f"[{w.name}] worst errors {worst}")
+    return cache, worst
+
+
+def _all_heads(w):
+    return [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)]
+
+
+def test_tiny_fp32_every_step():
+    w = wl.workload("tiny")
+    _run(w, 0, set(range(w.n_chunks)), _all_heads(w))
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_tiny_fp32_other_seeds(seed):
+    w = wl.workload("tiny")
+    _run(w, seed, set(range(w.n_chunks)), _all_heads(w))
+
+
+SMALL_BF16 = {
+    # several tiles and ragged tails: S, N_C, M not multiples of 32/64
+    "g4_d128_ragged": dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, prefill=200, chunk=100,
+                           total_len=200 + 100 * 5, cache_slots=320, recent_window=40, qk_std=1.0),
+    "g1_d64": dict(batch=1, n_q_heads=3, n_kv_heads=3, head_dim=64, prefill=130, chunk=70,
+                   total_len=130 + 70 * 5, cache_slots=260, recent_window=17, qk_std=1.0),
+    "g8_d128_fill": dict(batch=1, n_q_heads=16, n_kv_heads=2, head_dim=128, prefill=64, chunk=96,
+                         total_len=64 + 96 * 7, cache_slots=512, recent_window=64, qk_std=1.0),
+    "g2_small_chunks": dict(batch=3, n_q_heads=4, n_kv_heads=2, head_dim=128, prefill=96, chunk=5,
+                            total_len=96 + 5 * 12, cache_slots=100, recent_window=9, qk_std=1.0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL_BF16))
+def test_small_bf16_every_step(name):
+    w = wl.workload("llama8b_64k", **SMALL_BF16[name])
+    _run(w, 3, set(range(w.n_chunks)), _all_heads(w))
+
+
+def test_cache_holding_everything_is_exact_causal_attention():
+    """M >= L: no eviction ever, the output is causal attention over the sequence."""
+    h2o = h2o_mod()
+    w = wl.workload("llama8b_64k", batch=1, n_q_heads=8, n_kv_heads=2, prefill=160, chunk=96,
+                    total_len=160 + 96 * 4, cache_slots=640, recent_window=32, qk_std=1.0)
+    cfg = cfg_of(w)
+    cache = h2o.H2OCache(cfg)
+    outs, qs, ks, vs = [], [], [], []
+    for c in range(w.n_chunks):
+        q, k, v = wl.chunk_inputs(w, 5, c)
+        qt, kt, vt = to_device(q), to_device(k), to_device(v)
+        outs.append(cache.prefill(qt, kt, vt) if c == 0 else cache.chunk_step(qt, kt, vt))
+        qs.append(qt.float().cpu()); ks.append(kt.float().cpu()); vs.append(vt.float().cpu())
+    out = torch.cat([o.float().cpu() for o in outs], dim=2).double()
+    q = torch.cat(qs, 2).double()
+    G = w.group
+    k = torch.cat(ks, 2).double().repeat_interleave(G, dim=1)
+    v = torch.cat(vs, 2).double().repeat_interleave(G, dim=1)
+    ref = F.scaled_dot_product_attention(q, k, v, is_causal=True)
+    err = (out - ref).abs().max().item()
+    rel = ((out - ref).norm() / ref.norm()).item()
+    _say(f"exact-attention max abs {err:.3e} rel rms {rel:.3e}")
+    assert err <= 2e-2 and rel <= 5e-3
+    # every key's score is its full causal column mass
+    L = q.shape[2]
+    z = (q @ k.transpose(-1, -2)) / math.sqrt(w.head_dim)
+    z = z.masked_fill(~torch.ones(L, L, dtype=torch.bool).tril(), float("-inf"))
+    colmass = torch.softmax(z, -1).sum(2).reshape(1, w.n_kv_heads, G, L).sum(2)
+    torch.cuda.synchronize()
+    sig = cache.scores.double().cpu()[:, :, :L]
+    assert (cache.positions.cpu()[:, :, :L] == torch.arange(L, dtype=torch.int32)).all()
+    assert ((sig - colmass).abs() / colmass).max().item() <= 1e-3
+
+
+def test_llama8b_64k_sampled_steps():
+    w = wl.workload("llama8b_64k")
+    _run(w, 0, {0, 1, 31, 62}, [(0, 0), (0, 5)])
+
+
+def test_llama8b_128k_sampled_steps():
+    w = wl.workload("llama8b_128k")
+    _run(w, 0, {1, 2, 3, 64, 126}, [(0, 3)])
+
+
+def test_decode_b32_sampled_steps():
+    w = wl.workload("decode_b32")
+    _run(w, 0, {1, 128, 256}, [(0, 0), (17, 5), (31, 7)])
+
+
+def test_widegqa_forward_sampled_steps():
+    w = wl.workload("widegqa_128k")
+    _run(w, 0, {1, 2, 3, 62}, [(0, 2)])
+
+
+def _small_run(seed=7, steps=6):
+    h2o = h2o_mod()
+    w = wl.workload("llama8b_64k", **SMALL_BF16["g4_d128_ragged"])
+    cfg = cfg_of(w)
+    cache = h2o.H2OCache(cfg)
+    outs = []
+    for c in range(min(w.n_chunks, steps)):
+        q, k, v = (to_device(x) for x in wl.chunk_inputs(w, seed, c))
+        outs.append((cache.prefill(q, k, v) if c == 0 else cache.chunk_step(q, k, v)).cpu())
+    torch.cuda.synchronize()
+    return w, cfg, cache, outs
+
+
+def test_bitwise_deterministic():
+    _, _, a, oa = _small_run()
+    _, _, b, ob = _small_run()
+    for x, y in zip(oa, ob):
+        assert torch.equal(x, y)
+    for t in ("k_cache", "v_cache", "scores", "positions"):
+        assert torch.equal(getattr(a, t).cpu(), getattr(b, t).cpu()), t
+
+
+def test_resume_from_snapshot_equals_uninterrupted():
+    h2o = h2o_mod()
+    w, cfg, ref, ref_outs = _small_run(steps=6)
+    # run 3 chunks, snapshot, destroy, adopt into fresh buffers, continue
+    cache = h2o.H2OCache(cfg)
+    outs = []
+    for c in range(3):
+        q, k, v = (to_device(x) for x in wl.chunk_inputs(w, 7, c))
+        outs.append((cache.prefill(q, k, v) if c == 0 else cache.chunk_step(q, k, v)).cpu())
+    torch.cuda.synchronize()
+    state = tuple(t.clone() for t in (cache.k_cache, cache.v_cache, cache.scores, cache.positions))
+    T = cache.tokens_seen
+    cache.close()
+    resumed = h2o.H2OCache(cfg, adopt_state=state, tokens_seen=T)
+    for c in range(3, 6):
+        q, k, v = (to_device(x) for x in wl.chunk_inputs(w, 7, c))
+        outs.append(resumed.chunk_step(q, k, v).cpu())
+    torch.cuda.synchronize()
+    for x, y in zip(outs, ref_outs):
+        assert torch.equal(x, y)
+    for t in ("k_cache", "v_cache", "scores", "positions"):
+        assert torch.equal(getattr(resumed, t).cpu(), getattr(ref, t).cpu()), t
+
+
+def test_planted_exact_ties_evict_lowest_slots():
+    """All candidates tie exactly: with Q = 0 every key gets the same mass, so
+    the victims must be the lowest-index candidates, bit-exact."""
+    h2o = h2o_mod()
+    B, Hq, Hkv, d, M, S, W = 1, 4, 2, 128, 256, 32, 64
+    cfg = h2o.H2OConfig(B, Hq, Hkv, d, M, W, S, M, "bf16")
+    T = 1000
+    pos = torch.empty((B, Hkv, M), dtype=torch.int32)
+    for h in range(Hkv):
+        pos[0, h] = torch.randperm(M, generator=torch.Generator().manual_seed(h)).to(torch.int32) + (T - M)
+    k_cache = torch.randn((B, Hkv, M, d), generator=torch.Generator().manual_seed(9)).to(torch.bfloat16)
+    state = (k_cache.cuda(), torch.randn_like(k_cache.float()).to(torch.bfloat16).cuda(),
+             torch.full((B, Hkv, M), 2.5, dtype=torch.float32).cuda(), pos.cuda())
+    cache = h2o.H2OCache(cfg, adopt_state=state, tokens_seen=T)
+    q = torch.zeros((B, Hq, S, d), dtype=torch.bfloat16, device="cuda")
+    k = torch.randn((B, Hkv, S, d), device="cuda").to(torch.bfloat16)
+    v = torch.randn((B, Hkv, S, d), device="cuda").to(torch.bfloat16)
+    slots = torch.empty((B, Hkv, S), dtype=torch.int32, device="cuda")
+    cache.chunk_step(q, k, v, slots_out=slots)
+    torch.cuda.synchronize()
+    for h in range(Hkv):
+        cand = np.flatnonzero(pos[0, h].numpy() < T - W)
+        assert slots[0, h].cpu().numpy().tolist() == sorted(cand[:S].tolist())
+
+
+def test_mass_per_step_is_chunk_times_group():
+    h2o = h2o_mod()
+    w = wl.workload("llama8b_64k", **SMALL_BF16["g8_d128_fill"])
+    cfg = cfg_of(w)
+    cache = h2o.H2OCache(cfg)
+    for c in range(w.n_chunks):
+        q, k, v = (to_device(x) for x in wl.chunk_inputs(w, 11, c))
+        if c == 0:
+            cache.prefill(q, k, v)
+            continue
+        mass = torch.empty((1, w.n_kv_heads, w.cache_slots + w.chunk), device="cuda")
+        cache.chunk_step(q, k, v, step_mass=mass)
+        tot = mass.double().sum(-1).cpu()
+        assert torch.allclose(tot, torch.full_like(tot, w.chunk * w.group), rtol=1e-5), tot
+
+
+def test_error_paths_leave_state_unchanged():
+    h2o = h2o_mod()
+    w = wl.workload("llama8b_64k", **SMALL_BF16["g2_small_chunks"])
+    cfg = cfg_of(w)
+    cache = h2o.H2OCache(cfg)
+    q, k, v = (to_device(x) for x in wl.chunk_inputs(w, 1, 0))
+    cache.prefill(q, k, v)
+    with pytest.raises(h2o.H2OError) as e:
+        cache.prefill(q, k, v)                   # second prefill
+    assert e.value.status == h2o.H2O_ERR_STATE
+    q1, k1, v1 = (to_device(x) for x in wl.chunk_inputs(w, 1, 1))
+    big = torch.zeros((w.batch, w.n_q_heads, w.chunk + 1, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    bigkv = torch.zeros((w.batch, w.n_kv_heads, w.chunk + 1, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(h2o.H2OError) as e:
+        cache.chunk_step(big, bigkv, bigkv)      # s > max_chunk
+    assert e.value.status == h2o.H2O_ERR_SHAPE
+    rc = h2o._lib.h2o_chunk_step(cache.handle, None, None, None, 4, None, None, None, None, None, None, None)
+    assert rc == h2o.H2O_ERR_NULL
+    assert cache.tokens_seen == w.prefill
+    cache.chunk_step(q1, k1, v1)
+    assert cache.tokens_seen == w.prefill + w.chunk
+
+
+def test_infeasible_adopted_state_sets_device_status():
+    h2o = h2o_mod()
+    B, Hq, Hkv, d, M, S, W = 1, 2, 1, 64, 64, 16, 8
+    cfg = h2o.H2OConfig(B, Hq, Hkv, d, M, W, S, M, "bf16")
+    T = 100
+    # every slot inside the recent window: nothing is evictable
+    pos = torch.full((B, Hkv, M), T - 1, dtype=torch.int32)
+    state = (torch.zeros((B, Hkv, M, d), dtype=torch.bfloat16).cuda(),
+             torch.zeros((B, Hkv, M, d), dtype=torch.bfloat16).cuda(),
+             torch.ones((B, Hkv, M), dtype=torch.float32).cuda(), pos.cuda())
+    before = tuple(t.clone() for t in state)
+    cache = h2o.H2OCache(cfg, adopt_state=state, tokens_seen=T)
+    q = torch.randn((B, Hq, S, d), device="cuda").to(torch.bfloat16)
+    k = torch.randn((B, Hkv, S, d), device="cuda").to(torch.bfloat16)
+    cache.chunk_step(q, k, k.clone())
+    assert h2o.h2o_device_status(cache.handle) == 1
+    assert h2o.h2o_device_status(cache.handle) == 0         # cleared by the read
+    for a, b in zip(before, state):
+        assert torch.equal(a, b)
