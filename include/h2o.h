@@ -138,8 +138,9 @@ H2O_API h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k,
  *     free slot was filled) -- the buffer delta of LHF Fig. 1(c).
  * Errors: H2O_ERR_NULL; H2O_ERR_SHAPE unless 1 <= s <= max_chunk.
  * If a state adopted through h2o_cache_init has fewer evictable slots than
- * the step needs, that (b, head) is left unchanged and bit 0 of the device
- * status word is set (see h2o_device_status). */
+ * the step needs, no slot of that (b, head) is written (K/V and positions
+ * unchanged; its scores have received the step's mass) and bit 0 of the
+ * device status word is set (see h2o_device_status). */
 H2O_API h2o_status h2o_chunk_step(h2o_cache* c, const void* q, const void* k_new,
                           const void* v_new, int32_t s, void* out, float* lse,
                           int32_t* slots_out, float* step_mass, void* k_old,

@@ -21,7 +21,9 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   size_t partial_off, partial_bytes;
   size_t lse_off, lse_bytes;
-  size_t counters_off, counters_bytes;   // B*Hkv counters followed by the status word
+  size_t counters_off, counters_bytes;   // B*Hkv counters, the status word, then tile counters
+  size_t n_counters;                     // ints cleared at init
+  size_t tiles_per_head;                 // score-kernel column tiles per head (upper bound)
   size_t total;
 };
 
@@ -36,7 +38,9 @@ Layout layout_of(const h2o_config* c) {
   L.lse_off = L.partial_off + L.partial_bytes;
   L.lse_bytes = align_up(static_cast<size_t>(c->batch) * c->n_q_heads * smax * sizeof(float));
   L.counters_off = L.lse_off + L.lse_bytes;
-  L.counters_bytes = align_up((heads + 1) * sizeof(int32_t));
+  L.tiles_per_head = (c->cache_slots + 63) / 64 + (smax + 63) / 64;
+  L.n_counters = heads + 1 + heads * L.tiles_per_head;
+  L.counters_bytes = align_up(L.n_counters * sizeof(int32_t));
   L.total = L.counters_off + L.counters_bytes;
   return L;
 }
@@ -137,7 +141,8 @@ h2o_status run_step(h2o_cache* c, const void* q, const void* k, const void* v, i
   h2o_status r = timed(c, 0, st, [&] { return h2o::launch_attn_fwd(sh, aa, dtype, st); });
   if (r != H2O_OK) return r;
   const int R = h2o::score_row_splits(sh, dtype);
-  h2o::ScoreArgs sa{q, c->k_cache, k, lse_buf, partial, R};
+  int32_t* tile_counters = status + 1;
+  h2o::ScoreArgs sa{q, c->k_cache, k, lse_buf, partial, c->scores, c->pos, tile_counters, R};
   r = timed(c, 1, st, [&] { return h2o::launch_score(sh, sa, dtype, st); });
   if (r != H2O_OK) return r;
   h2o::SelectArgs xa{c->k_cache, c->v_cache, c->scores, c->pos, k, v, partial, R,
@@ -178,7 +183,7 @@ h2o_status h2o_validate_config(const h2o_config* c) {
   if (c->recent_window < 0 || c->max_chunk < 1 || c->max_prefill < 1) return H2O_ERR_CONFIG;
   if (c->max_prefill > c->cache_slots) return H2O_ERR_CONFIG;
   if (static_cast<int64_t>(c->cache_slots) - c->recent_window < c->max_chunk) return H2O_ERR_CONFIG;
-  if (c->max_chunk > 65536 || c->max_prefill > 65536) return H2O_ERR_CONFIG;
+  if (c->max_chunk > 16384 || c->max_prefill > 16384) return H2O_ERR_CONFIG;
   if (!(c->softmax_scale == c->softmax_scale)) return H2O_ERR_CONFIG;   // NaN
   // every tensor offset must fit in int64 and every chunk tensor below 2^31 elements
   const int64_t big = static_cast<int64_t>(c->batch) * c->n_q_heads * max_len(c) * c->head_dim;
@@ -219,7 +224,7 @@ h2o_status h2o_cache_init(const h2o_config* cfg, void* k_cache, void* v_cache, f
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t n_slots = static_cast<int64_t>(cfg->batch) * cfg->n_kv_heads * cfg->cache_slots;
-  const int64_t n_cnt = static_cast<int64_t>(cfg->batch) * cfg->n_kv_heads + 1;
+  const int64_t n_cnt = static_cast<int64_t>(lay.n_counters);
   int32_t* counters = reinterpret_cast<int32_t*>(c->ws + lay.counters_off);
   r = timed(c, 3, st, [&] {
     return h2o::launch_reset(adopt ? nullptr : scores, adopt ? nullptr : positions, adopt ? 0 : n_slots,

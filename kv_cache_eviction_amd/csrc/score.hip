@@ -8,14 +8,19 @@
 //
 // P = exp(z - lse) is recomputed from Q, K and the forward's lse (the
 // forward's online softmax cannot normalise a column before every row is
-// done), and reduced over rows without atomics: each workgroup owns a tile
-// of 256 key columns and one contiguous range of query rows (a "row split"),
-// and writes one partial sum per column.  The select kernel adds the R
-// partials of a column in a fixed order, so results are deterministic.
+// done), and reduced over rows without atomics on the sums: each workgroup
+// owns a tile of 256 key columns and one contiguous range of query rows (a
+// "row split") and writes one partial sum per column.  The last workgroup of
+// a column tile to finish (a per-tile arrival counter) adds the R partials
+// in split order -- deterministic -- and writes the step's mass: filled
+// cache slots get score += mass, and the masses of the tile (0 for free
+// slots; mu_j for chunk key j) go to row 0 of the partial buffer, which the
+// select kernel reads.
 //
 // bf16 path: S = Q K^T on v_mfma_f32_32x32x16_bf16 with the wave's 64 keys
-// as the B operand held in registers for the whole kernel and 32-row query
-// blocks as the A operand, staged in LDS and shared by the 4 waves.  Each
+// as the B operand held in registers for the whole kernel and 64-row query
+// blocks as the A operand, staged in a double-buffered LDS ring shared by
+// the 4 waves and prefetched two blocks ahead through registers.  Each
 // accumulator column belongs to one key, so the column sum is one fp32 add
 // per element inside the lane plus one exchange with lane l^32 at the end.
 #include "h2o_device.h"
@@ -25,21 +30,47 @@ namespace h2o {
 namespace {
 
 constexpr int kCT = 256;        // key columns per workgroup (4 waves x 64)
+constexpr int kRB = 64;         // query rows per staged block (2 MFMA row blocks)
 constexpr int kRowSplitsMax = 16;
+
+// Last-arrival finalize of one column tile: sums the R partials of each
+// column in split order, updates the scores of filled slots and stores the
+// step's masses into partial row 0.
+__device__ void finalize_tile(float* __restrict__ ph, size_t PS, int R, bool is_cache, int base,
+                              int lim, int M, float* __restrict__ sc_h,
+                              const int32_t* __restrict__ pos_h) {
+  for (int c = threadIdx.x; c < kCT; c += blockDim.x) {
+    const int key = base + c;
+    if (key >= lim) break;
+    const size_t x = (is_cache ? 0 : static_cast<size_t>(M)) + key;
+    float s = 0.f;
+    for (int r = 0; r < R; ++r) s += ph[r * PS + x];
+    if (is_cache) {
+      if (pos_h[key] >= 0) {
+        sc_h[key] += s;
+      } else {
+        s = 0.f;
+      }
+    }
+    ph[x] = s;
+  }
+}
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc,
     const bf16_t* __restrict__ Kn, const float* __restrict__ lse,
-    float* __restrict__ partial, int Hq, int Hkv, int S, int M, int n_cache,
-    float c2, int n_heads, int n_ct, int n_tiles, int R) {
+    float* __restrict__ partial, float* __restrict__ scores, const int32_t* __restrict__ pos,
+    int32_t* __restrict__ tile_cnt, int Hq, int Hkv, int S, int M, int n_cache, float c2,
+    int n_heads, int n_ct, int n_tiles, int R) {
   constexpr int DS = D / 16;
   constexpr int QLD = D + 8;
   constexpr int CPR = D / 8;
-  constexpr int NCH = 32 * CPR / 256;   // 16-byte chunks per thread per row block
-  __shared__ __attribute__((aligned(16))) bf16_t Qs[32 * QLD];
-  __shared__ float s_lse2[32];
-  __shared__ int s_irow[32];
+  constexpr int NCH = kRB * CPR / 256;  // 16-byte chunks per thread per row block
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][kRB * QLD];
+  __shared__ float s_lse2[2][kRB];
+  __shared__ int s_irow[2][kRB];
+  __shared__ int s_last;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hf = lane >> 5, col = lane & 31;
@@ -70,105 +101,151 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
   }
 
   const int n_rows = G * S;
-  const int n_rblk = (n_rows + 31) >> 5;
-  const int blk_lo = static_cast<int>(static_cast<int64_t>(split) * n_rblk / R);
-  const int blk_hi = static_cast<int>(static_cast<int64_t>(split + 1) * n_rblk / R);
+  const int n_blk = (n_rows + kRB - 1) / kRB;
+  const int blk_lo = static_cast<int>(static_cast<int64_t>(split) * n_blk / R);
+  const int blk_hi = static_cast<int>(static_cast<int64_t>(split + 1) * n_blk / R);
   const bf16_t* qhead = Q + static_cast<size_t>(b * Hq + kvh * G) * S * D;  // rows g*S + i
   const float* lhead = lse + static_cast<size_t>(b * Hq + kvh * G) * S;
 
-  // A row block contributes to chunk keys only if one of its queries i >= key0.
+  // A row block contributes to chunk keys only if one of its queries i >= base.
   auto block_needed = [&](int blk) {
     if (is_cache) return true;
-    const int r0 = blk * 32, r1 = min(r0 + 31, n_rows - 1);
-    if (r0 / S != r1 / S) return true;        // spans two heads: i reaches S-1
-    return (r1 % S) >= base;                  // max query of the block vs first key of the tile
+    const int r0 = blk * kRB, r1 = min(r0 + kRB - 1, n_rows - 1);
+    if (r0 / S != r1 / S) return true;
+    return (r1 % S) >= base;
+  };
+  auto next_needed = [&](int blk) {
+    ++blk;
+    while (blk < blk_hi && !block_needed(blk)) ++blk;
+    return blk;
   };
 
-  u32x4 qreg[NCH];
-  float lreg = 0.f;
-  int ireg = -1;
-  auto load_blk = [&](int blk) {
-    const int r0 = blk * 32;
+  struct Stage {
+    u32x4 q[NCH];
+    float l;
+    int i;
+  };
+  auto load_blk = [&](int blk, Stage& s) {
+    const int r0 = blk * kRB;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int idx = c * 256 + tid, row = idx / CPR, dc = idx % CPR;
       const int r = r0 + row;
-      qreg[c] = (r < n_rows) ? load_u32x4(qhead + static_cast<size_t>(r) * D + dc * 8)
-                             : u32x4{0, 0, 0, 0};
+      s.q[c] = (r < n_rows) ? load_u32x4(qhead + static_cast<size_t>(r) * D + dc * 8)
+                            : u32x4{0, 0, 0, 0};
     }
-    if (tid < 32) {
+    if (tid < kRB) {
       const int r = r0 + tid;
-      lreg = (r < n_rows) ? lhead[r] * kLog2e : __builtin_huge_valf();
-      ireg = (r < n_rows) ? r % S : -1;
+      s.l = (r < n_rows) ? lhead[r] * kLog2e : __builtin_huge_valf();
+      s.i = (r < n_rows) ? r % S : -1;
     }
   };
-  auto store_blk = [&]() {
+  auto store_blk = [&](const Stage& s, int buf) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int idx = c * 256 + tid, row = idx / CPR, dc = idx % CPR;
-      store_u32x4(&Qs[row * QLD + dc * 8], qreg[c]);
+      store_u32x4(&Qs[buf][row * QLD + dc * 8], s.q[c]);
     }
-    if (tid < 32) {
-      s_lse2[tid] = lreg;
-      s_irow[tid] = ireg;
+    if (tid < kRB) {
+      s_lse2[buf][tid] = s.l;
+      s_irow[buf][tid] = s.i;
     }
   };
 
   float cs0 = 0.f, cs1 = 0.f;     // column sums of this lane's two key columns
-  int blk = blk_lo;
-  while (blk < blk_hi && !block_needed(blk)) ++blk;
-  if (blk < blk_hi) load_blk(blk);
-  while (blk < blk_hi) {
-    __syncthreads();
-    store_blk();
-    __syncthreads();
-    int nxt = blk + 1;
-    while (nxt < blk_hi && !block_needed(nxt)) ++nxt;
-    if (nxt < blk_hi) load_blk(nxt);
-
+  // Ping-pong register stages: while block `cur` is computed from LDS buffer
+  // `buf`, one stage holds block n1 (stored to the other buffer after the
+  // MFMAs) and the other block n2; each stage's loads get two blocks of
+  // compute to land.
+  Stage st0, st1;
+  int cur = next_needed(blk_lo - 1);
+  int n1 = cur < blk_hi ? next_needed(cur) : blk_hi;
+  int n2 = n1 < blk_hi ? next_needed(n1) : blk_hi;
+  if (cur < blk_hi) {
+    load_blk(cur, st0);
+    store_blk(st0, 0);
+  }
+  if (n1 < blk_hi) load_blk(n1, st0);
+  if (n2 < blk_hi) load_blk(n2, st1);
+  __syncthreads();
+  int buf = 0;
+  auto iter = [&](Stage& st) {
     if (key0 < lim) {
-      f32x16 a0 = zero16(), a1 = zero16();
 #pragma unroll
-      for (int st = 0; st < DS; ++st) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qs[col * QLD + 16 * st + 8 * hf]);
-        a0 = mfma32x32x16(qa, kf[0][st], a0);
-        a1 = mfma32x32x16(qa, kf[1][st], a1);
-      }
-      // accumulator register r of lane l: query row 8(r/4) + 4hf + r%4 of the block
-      const bool causal = !is_cache;
+      for (int half = 0; half < 2; ++half) {
+        f32x16 a0 = zero16(), a1 = zero16();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 8 * (r >> 2) + 4 * hf + (r & 3);
-        const float l2 = s_lse2[row];
-        float p0 = fast_exp2(fmaf(a0[r], c2, -l2));
-        float p1 = fast_exp2(fmaf(a1[r], c2, -l2));
-        if (causal) {
-          const int qi = s_irow[row];
-          p0 = (key0 + col <= qi) ? p0 : 0.f;
-          p1 = (key0 + 32 + col <= qi) ? p1 : 0.f;
+        for (int q = 0; q < DS; ++q) {
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(
+              &Qs[buf][(half * 32 + col) * QLD + 16 * q + 8 * hf]);
+          a0 = mfma32x32x16(qa, kf[0][q], a0);
+          a1 = mfma32x32x16(qa, kf[1][q], a1);
         }
-        cs0 += p0;
-        cs1 += p1;
+        // accumulator register r of lane l: query row 8(r/4) + 4hf + r%4 of this half block
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = half * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const float l2 = s_lse2[buf][row];
+          float p0 = fast_exp2(fmaf(a0[r], c2, -l2));
+          float p1 = fast_exp2(fmaf(a1[r], c2, -l2));
+          if (!is_cache) {
+            const int qi = s_irow[buf][row];
+            p0 = (key0 + col <= qi) ? p0 : 0.f;
+            p1 = (key0 + 32 + col <= qi) ? p1 : 0.f;
+          }
+          cs0 += p0;
+          cs1 += p1;
+        }
       }
     }
-    blk = nxt;
+    if (n1 < blk_hi) store_blk(st, buf ^ 1);      // st holds block n1
+    const int n3 = n2 < blk_hi ? next_needed(n2) : blk_hi;
+    if (n3 < blk_hi) load_blk(n3, st);             // st now carries block n3
+    __syncthreads();
+    cur = n1;
+    n1 = n2;
+    n2 = n3;
+    buf ^= 1;
+  };
+  while (cur < blk_hi) {
+    iter(st0);
+    if (cur >= blk_hi) break;
+    iter(st1);
   }
   cs0 += xor32(cs0);
   cs1 += xor32(cs1);
+  const size_t PS = static_cast<size_t>(M) + S;
+  float* ph = partial + static_cast<size_t>(bh) * R * PS;
   if (hf == 0) {
-    float* out = partial + (static_cast<size_t>(bh) * R + split) * (M + S) + (is_cache ? 0 : M);
+    float* out = ph + static_cast<size_t>(split) * PS + (is_cache ? 0 : M);
     const int k0 = key0 + col, k1 = key0 + 32 + col;
     if (k0 < lim) out[k0] = cs0;
     if (k1 < lim) out[k1] = cs1;
   }
+  // the last of the R workgroups of this column tile finalizes it
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    int* cnt = tile_cnt + static_cast<size_t>(bh) * n_tiles + tile;
+    const int prev = atomicAdd(cnt, 1);
+    s_last = prev == R - 1;
+    if (s_last) *cnt = 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  finalize_tile(ph, PS, R, is_cache, base, lim, M, scores + static_cast<size_t>(bh) * M,
+                pos + static_cast<size_t>(bh) * M);
 }
 
-// fp32: one thread per key column, query rows streamed through LDS.
+// fp32: one thread per key column, query rows streamed through LDS; one row
+// split, so each workgroup finalizes its own columns.
 template <int D>
 __global__ __launch_bounds__(64) void score_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ Kc, const float* __restrict__ Kn,
-    const float* __restrict__ lse, float* __restrict__ partial, int Hq, int Hkv, int S, int M,
-    int n_cache, float c2, int n_heads, int n_ct, int n_tiles) {
+    const float* __restrict__ lse, float* __restrict__ partial, float* __restrict__ scores,
+    const int32_t* __restrict__ pos, int Hq, int Hkv, int S, int M, int n_cache, float c2,
+    int n_heads, int n_ct, int n_tiles) {
   constexpr int RT = 16;
   __shared__ float Qs[RT][D];
   __shared__ float ls[RT];
@@ -211,23 +288,39 @@ __global__ __launch_bounds__(64) void score_f32_kernel(
       cs += fast_exp2(fmaf(z, c2, -ls[rr]));
     }
   }
-  if (ok) partial[static_cast<size_t>(bh) * (M + S) + (is_cache ? 0 : M) + key] = cs;
+  if (!ok) return;
+  float* out = partial + static_cast<size_t>(bh) * (M + S);
+  if (is_cache) {
+    if (pos[static_cast<size_t>(bh) * M + key] >= 0) {
+      scores[static_cast<size_t>(bh) * M + key] += cs;
+    } else {
+      cs = 0.f;
+    }
+    out[key] = cs;
+  } else {
+    out[M + key] = cs;
+  }
 }
 
 }  // namespace
 
 int score_row_splits_max() { return kRowSplitsMax; }
 
+int score_tiles(const StepShape& sh, int dtype) {
+  const int ct = dtype == kBF16 ? kCT : 64;
+  return (sh.n_cache + ct - 1) / ct + (sh.S + ct - 1) / ct;
+}
+
 int score_row_splits(const StepShape& sh, int dtype) {
   if (dtype != kBF16) return 1;
   const int n_heads = sh.B * sh.Hkv;
-  const int n_tiles = (sh.n_cache + kCT - 1) / kCT + (sh.S + kCT - 1) / kCT;
-  const int n_rblk = (sh.Hq / sh.Hkv * sh.S + 31) / 32;
-  const int target = 1024;   // about 4 workgroups per CU
-  int R = (target + n_heads * n_tiles - 1) / (n_heads * n_tiles);
+  const int n_tiles = score_tiles(sh, dtype);
+  const int n_blk = (sh.Hq / sh.Hkv * sh.S + kRB - 1) / kRB;
+  const int target = 512;   // two resident workgroups per CU
+  int R = target / (n_heads * n_tiles);
   R = R < 1 ? 1 : R;
   R = R > kRowSplitsMax ? kRowSplitsMax : R;
-  R = R > n_rblk ? n_rblk : R;
+  R = R > n_blk ? n_blk : R;
   return R;
 }
 
@@ -241,8 +334,8 @@ hipError_t launch_score(const StepShape& sh, const ScoreArgs& a, int dtype, hipS
 #define H2O_LAUNCH_SCORE(DD)                                                                      \
   hipLaunchKernelGGL(score_bf16_kernel<DD>, grid, block, 0, st, static_cast<const bf16_t*>(a.q), \
                      static_cast<const bf16_t*>(a.k_cache), static_cast<const bf16_t*>(a.k_new), \
-                     a.lse, a.partial, sh.Hq, sh.Hkv, sh.S, sh.M, sh.n_cache, c2, n_heads, n_ct, \
-                     n_tiles, a.R)
+                     a.lse, a.partial, a.scores, a.pos, a.tile_counters, sh.Hq, sh.Hkv, sh.S,     \
+                     sh.M, sh.n_cache, c2, n_heads, n_ct, n_tiles, a.R)
     if (sh.D == 128) H2O_LAUNCH_SCORE(128);
     else H2O_LAUNCH_SCORE(64);
 #undef H2O_LAUNCH_SCORE
@@ -253,8 +346,8 @@ hipError_t launch_score(const StepShape& sh, const ScoreArgs& a, int dtype, hipS
 #define H2O_LAUNCH_SCORE32(DD)                                                                  \
   hipLaunchKernelGGL(score_f32_kernel<DD>, grid, block, 0, st, static_cast<const float*>(a.q), \
                      static_cast<const float*>(a.k_cache), static_cast<const float*>(a.k_new), \
-                     a.lse, a.partial, sh.Hq, sh.Hkv, sh.S, sh.M, sh.n_cache, c2, n_heads, n_ct, \
-                     n_tiles)
+                     a.lse, a.partial, a.scores, a.pos, sh.Hq, sh.Hkv, sh.S, sh.M, sh.n_cache,  \
+                     c2, n_heads, n_ct, n_tiles)
     if (sh.D == 128) H2O_LAUNCH_SCORE32(128);
     else H2O_LAUNCH_SCORE32(64);
 #undef H2O_LAUNCH_SCORE32

@@ -11,15 +11,20 @@
 // smallest (score, slot index); chunk token j goes to the j-th smallest
 // target slot.
 //
-// One workgroup handles a share of the chunk's rows for one (b, KV head).
-// Every workgroup of a head recomputes the same selection from the same
-// inputs (deterministic), copies its share of K/V rows, then counts itself
-// done on a per-head counter; the last one to finish writes the new scores
-// and positions (no workgroup still reads them at that point) and clears the
-// counter for the next launch.  Scores are mapped to order-preserving 32-bit
-// keys; the n_e-th smallest candidate is found by a 4-pass, 8-bit LDS radix
-// select; equal scores resolve to the lowest slot by an exclusive scan over
-// slot order.
+// The score kernel has already added this step's mass to every filled slot.
+// One workgroup handles a share of the chunk's rows for one (b, KV head): it
+// issues the loads of its chunk rows first, then recomputes the same
+// selection as every other workgroup of the head (deterministic), then
+// stores its rows into their slots.  It counts itself done on a per-head
+// counter; the last one to finish writes scores and positions of the
+// targets (no workgroup still reads them at that point) and clears the
+// counter for the next launch.
+//
+// Selection: scores map to order-preserving 32-bit keys; the bits all
+// candidates share are found with an AND/OR reduction and skipped, then the
+// n_e-th smallest key is found by 8-bit LDS radix passes over the remaining
+// bits; equal keys resolve to the lowest slot by an exclusive scan over slot
+// order.
 #include "h2o_device.h"
 #include "h2o_launch.h"
 
@@ -28,8 +33,8 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWavesSel = kThreads / 64;
-constexpr int kRowsPerPart = 64;
-constexpr int kMaxParts = 64;
+constexpr int kRowChunks = 4;        // 16-byte chunks per thread per matrix (K or V) prefetched
+constexpr int kMaxParts = 256;      // S <= 16384 rows of at most 512 bytes
 
 enum : uint8_t { kFree = 0, kCand = 1, kKeep = 2, kTarget = 4 };
 
@@ -69,76 +74,116 @@ __device__ int block_excl_scan(int v, int* tmp, int& total) {
   return before + incl - v;
 }
 
+// Block-wide AND and OR of v (utmp holds 2*kWavesSel words of LDS).
+__device__ void block_and_or(uint32_t v_and, uint32_t v_or, uint32_t* utmp, uint32_t& r_and,
+                             uint32_t& r_or) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    v_and &= static_cast<uint32_t>(__shfl_xor(static_cast<int>(v_and), o));
+    v_or |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(v_or), o));
+  }
+  __syncthreads();
+  if (lane == 0) {
+    utmp[wave] = v_and;
+    utmp[kWavesSel + wave] = v_or;
+  }
+  __syncthreads();
+  r_and = 0xffffffffu;
+  r_or = 0u;
+#pragma unroll
+  for (int w = 0; w < kWavesSel; ++w) {
+    r_and &= utmp[w];
+    r_or |= utmp[kWavesSel + w];
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void select_scatter_kernel(
     char* __restrict__ kc, char* __restrict__ vc, float* __restrict__ scores,
     int32_t* __restrict__ pos, const char* __restrict__ kn, const char* __restrict__ vn,
-    const float* __restrict__ partial, int R, int32_t* __restrict__ slots_out,
+    const float* __restrict__ mass, int R, int32_t* __restrict__ slots_out,
     float* __restrict__ step_mass, char* __restrict__ k_old, char* __restrict__ v_old,
     int32_t* __restrict__ counters, int32_t* __restrict__ status, int T, int W, int S, int M,
-    int n_cache, int row_bytes, int n_heads, int n_parts) {
+    int n_cache, int row_bytes, int rows_per, int n_heads, int n_parts) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  float* s_sig = reinterpret_cast<float*>(smem);                 // [M]
-  int* s_R = reinterpret_cast<int*>(smem + 4 * static_cast<size_t>(M));   // [S]
+  uint32_t* s_key = reinterpret_cast<uint32_t*>(smem);                        // [M]
+  int* s_R = reinterpret_cast<int*>(smem + 4 * static_cast<size_t>(M));      // [S]
   uint8_t* s_fl = reinterpret_cast<uint8_t*>(smem + 4 * static_cast<size_t>(M) + 4 * static_cast<size_t>(S));
   __shared__ uint32_t hist[256];
   __shared__ int s_tmp[kWavesSel];
+  __shared__ uint32_t s_utmp[2 * kWavesSel];
   __shared__ int s_sel[2];
   __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int bh = blockIdx.x % n_heads;
   const int part = static_cast<int>(blockIdx.x) / n_heads;
-  const size_t PS = static_cast<size_t>(M) + S;        // partial row length
-  const float* ph = partial + static_cast<size_t>(bh) * R * PS;
+  const size_t PS = static_cast<size_t>(M) + S;
+  const float* mh = mass + static_cast<size_t>(bh) * R * PS;     // row 0 of the head
   float* sc_h = scores + static_cast<size_t>(bh) * M;
   int32_t* pos_h = pos + static_cast<size_t>(bh) * M;
 
-  // 1. scores after this step's mass; slot classes
+  // 0. issue the loads of this workgroup's chunk rows (independent of the selection)
+  const int j0 = min(S, part * rows_per), j1 = min(S, j0 + rows_per);
+  const int cpr = row_bytes / 16;
+  const int n_chunks = (j1 - j0) * cpr;
+  u32x4 kr[kRowChunks], vr[kRowChunks];
+#pragma unroll
+  for (int i = 0; i < kRowChunks; ++i) {
+    const int idx = tid + i * kThreads;
+    if (idx < n_chunks) {
+      const size_t src = (static_cast<size_t>(bh) * S + j0) * row_bytes + 16 * static_cast<size_t>(idx);
+      kr[i] = load_u32x4(kn + src);
+      vr[i] = load_u32x4(vn + src);
+    }
+  }
+
+  // 1. slot classes and keys; AND/OR of the candidate keys
   int my_free = 0, my_cand = 0;
+  uint32_t k_and = 0xffffffffu, k_or = 0u;
   for (int m = tid; m < M; m += kThreads) {
     const int p = pos_h[m];
-    float s = sc_h[m];
-    uint8_t fl;
-    if (p < 0) {
-      fl = kFree;
-    } else {
-      fl = (p < T - W) ? kCand : kKeep;
-      if (m < n_cache) {
-        float ds = 0.f;
-        for (int r = 0; r < R; ++r) ds += ph[static_cast<size_t>(r) * PS + m];
-        s += ds;
-      }
-    }
-    s_sig[m] = s;
+    const uint32_t key = order_key(sc_h[m]);
+    const uint8_t fl = p < 0 ? kFree : ((p < T - W) ? kCand : kKeep);
+    s_key[m] = key;
     s_fl[m] = fl;
     my_free += fl == kFree;
     my_cand += fl == kCand;
+    if (fl == kCand) {
+      k_and &= key;
+      k_or |= key;
+    }
   }
   int n_free, n_cand;
   block_excl_scan(my_free, s_tmp, n_free);
   block_excl_scan(my_cand, s_tmp, n_cand);
   const int n_f = min(S, n_free);
   const int n_e = S - n_f;
-  if (n_cand < n_e) {                      // infeasible adopted state: leave it untouched
+  if (n_cand < n_e) {                      // infeasible adopted state: no slot is written
     if (part == 0 && tid == 0) atomicOr(status, 1);
     return;
   }
 
-  // 2. radix select of the n_e-th smallest candidate score (bit pattern)
+  // 2. radix select of the n_e-th smallest candidate key
   uint32_t thr = 0;
   int k_eq = 0;
   if (n_e > 0) {
-    uint32_t prefix = 0, pmask = 0;
+    uint32_t all_and, all_or;
+    block_and_or(k_and, k_or, s_utmp, all_and, all_or);
+    const uint32_t differ = all_and ^ all_or;           // bits not shared by every candidate
+    uint32_t prefix = all_and & ~differ, pmask = ~differ;
     int kk = n_e;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
+    int top = differ ? 31 - __builtin_clz(differ) : -1;  // highest differing bit
+    while (top >= 0) {
+      const int shift = top >= 7 ? top - 7 : 0;
+      const uint32_t dmask = (top >= 7 ? 0xffu : ((1u << (top + 1)) - 1u)) << shift;
       __syncthreads();
       if (tid < 256) hist[tid] = 0;
       __syncthreads();
       for (int m = tid; m < M; m += kThreads) {
         if (s_fl[m] != kCand) continue;
-        const uint32_t u = order_key(s_sig[m]);
-        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+        const uint32_t u = s_key[m];
+        if ((u & pmask) == prefix) atomicAdd(&hist[(u & dmask) >> shift], 1u);
       }
       __syncthreads();
       if (tid < 64) {
@@ -154,11 +199,12 @@ __global__ __launch_bounds__(kThreads) void select_scatter_kernel(
       }
       __syncthreads();
       prefix |= static_cast<uint32_t>(s_sel[0]) << shift;
-      pmask |= 0xffu << shift;
+      pmask |= dmask;
       kk -= s_sel[1];
+      top = shift - 1;
     }
     thr = prefix;
-    k_eq = kk;      // how many candidates scoring exactly thr are taken (lowest slots)
+    k_eq = kk;      // how many candidates with key == thr are taken (lowest slots)
   }
 
   // 3. targets in ascending slot order: each thread owns a contiguous slot range
@@ -168,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void select_scatter_kernel(
   for (int m = lo; m < hi; ++m) {
     const uint8_t fl = s_fl[m];
     c_free += fl == kFree;
-    c_eq += (n_e > 0 && fl == kCand && order_key(s_sig[m]) == thr);
+    c_eq += (n_e > 0 && fl == kCand && s_key[m] == thr);
   }
   int dummy;
   int fr = block_excl_scan(c_free, s_tmp, dummy);
@@ -181,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void select_scatter_kernel(
       t = fr < n_f;
       ++fr;
     } else if (fl == kCand && n_e > 0) {
-      const uint32_t u = order_key(s_sig[m]);
+      const uint32_t u = s_key[m];
       t = (u < thr) || (u == thr && eq < k_eq);
       eq += u == thr;
     }
@@ -193,53 +239,47 @@ __global__ __launch_bounds__(kThreads) void select_scatter_kernel(
     if ((s_fl[m] & kTarget) && j < S) s_R[j++] = m;
   __syncthreads();
 
-  // 4. scatter this workgroup's share of the chunk's rows
-  const int rows_per = (S + n_parts - 1) / n_parts;
-  const int j0 = min(S, part * rows_per), j1 = min(S, j0 + rows_per);
-  const int cpr = row_bytes / 16;
-  for (int idx = tid; idx < (j1 - j0) * cpr; idx += kThreads) {
-    const int jj = j0 + idx / cpr, c = idx % cpr;
-    const int slot = s_R[jj];
-    const size_t src = (static_cast<size_t>(bh) * S + jj) * row_bytes + 16 * c;
-    const size_t dst = (static_cast<size_t>(bh) * M + slot) * row_bytes + 16 * c;
-    const bool was_free = (s_fl[slot] & 3) == kFree;
-    if (k_old) {
-      const u32x4 z = {0, 0, 0, 0};
-      store_u32x4(k_old + src, was_free ? z : load_u32x4(kc + dst));
-      store_u32x4(v_old + src, was_free ? z : load_u32x4(vc + dst));
+  // 4. store this workgroup's chunk rows into their slots (old rows to the delta)
+#pragma unroll
+  for (int i = 0; i < kRowChunks; ++i) {
+    const int idx = tid + i * kThreads;
+    if (idx < n_chunks) {
+      const int jj = j0 + idx / cpr, c = idx % cpr;
+      const int slot = s_R[jj];
+      const size_t src = (static_cast<size_t>(bh) * S + jj) * row_bytes + 16 * c;
+      const size_t dst = (static_cast<size_t>(bh) * M + slot) * row_bytes + 16 * c;
+      if (k_old) {
+        const bool was_free = (s_fl[slot] & 3) == kFree;
+        const u32x4 z = {0, 0, 0, 0};
+        store_u32x4(k_old + src, was_free ? z : load_u32x4(kc + dst));
+        store_u32x4(v_old + src, was_free ? z : load_u32x4(vc + dst));
+      }
+      store_u32x4(kc + dst, kr[i]);
+      store_u32x4(vc + dst, vr[i]);
     }
-    store_u32x4(kc + dst, load_u32x4(kn + src));
-    store_u32x4(vc + dst, load_u32x4(vn + src));
   }
 
-  // 5. the last workgroup of this head writes scores, positions and outputs
+  // 5. the last workgroup of this head writes the targets' scores and positions
+  __threadfence();
   __syncthreads();
   if (tid == 0) {
-    __threadfence();
     const int prev = atomicAdd(&counters[bh], 1);
     s_last = prev == n_parts - 1;
+    if (s_last) counters[bh] = 0;
   }
   __syncthreads();
   if (!s_last) return;
-  if (tid == 0) counters[bh] = 0;
-  for (int m = tid; m < M; m += kThreads) {
-    const uint8_t fl = s_fl[m];
-    if (!(fl & kTarget) && (fl & 3) != kFree) sc_h[m] = s_sig[m];
-    if (step_mass) {
-      float ds = 0.f;
-      if ((fl & 3) != kFree && m < n_cache)
-        for (int r = 0; r < R; ++r) ds += ph[static_cast<size_t>(r) * PS + m];
-      step_mass[static_cast<size_t>(bh) * PS + m] = ds;
-    }
-  }
   for (int jj = tid; jj < S; jj += kThreads) {
     const int slot = s_R[jj];
-    float mu = 0.f;
-    for (int r = 0; r < R; ++r) mu += ph[static_cast<size_t>(r) * PS + M + jj];
+    const float mu = mh[M + jj];
     sc_h[slot] = mu;
     pos_h[slot] = T + jj;
     if (slots_out) slots_out[static_cast<size_t>(bh) * S + jj] = slot;
     if (step_mass) step_mass[static_cast<size_t>(bh) * PS + M + jj] = mu;
+  }
+  if (step_mass) {
+    for (int m = tid; m < M; m += kThreads)
+      step_mass[static_cast<size_t>(bh) * PS + m] = m < n_cache ? mh[m] : 0.f;
   }
 }
 
@@ -255,11 +295,18 @@ __global__ void reset_kernel(float* scores, int32_t* pos, int64_t n, int32_t* co
 
 }  // namespace
 
+int select_rows_per_part(int row_bytes) {
+  // each thread prefetches kRowChunks 16-byte chunks of K and of V
+  return kThreads * kRowChunks * 16 / row_bytes;
+}
+
 hipError_t launch_select_scatter(const StepShape& sh, const SelectArgs& a, int dtype, hipStream_t st) {
   const int n_heads = sh.B * sh.Hkv;
-  int n_parts = (sh.S + kRowsPerPart - 1) / kRowsPerPart;
-  n_parts = n_parts < 1 ? 1 : (n_parts > kMaxParts ? kMaxParts : n_parts);
   const int row_bytes = sh.D * (dtype == kBF16 ? 2 : 4);
+  int rows_per = select_rows_per_part(row_bytes);
+  int n_parts = (sh.S + rows_per - 1) / rows_per;
+  if (n_parts > kMaxParts) return hipErrorInvalidValue;   // excluded by config validation
+  n_parts = n_parts < 1 ? 1 : n_parts;
   const size_t lds = 4 * static_cast<size_t>(sh.M) + 4 * static_cast<size_t>(sh.S) +
                      static_cast<size_t>(sh.M) + 16;
   if (lds > 64 * 1024) {
@@ -269,10 +316,10 @@ hipError_t launch_select_scatter(const StepShape& sh, const SelectArgs& a, int d
   }
   hipLaunchKernelGGL(select_scatter_kernel, dim3(n_heads * n_parts), dim3(kThreads), lds, st,
                      static_cast<char*>(a.k_cache), static_cast<char*>(a.v_cache), a.scores, a.pos,
-                     static_cast<const char*>(a.k_new), static_cast<const char*>(a.v_new), a.partial,
+                     static_cast<const char*>(a.k_new), static_cast<const char*>(a.v_new), a.mass,
                      a.R, a.slots_out, a.step_mass, static_cast<char*>(a.k_old),
                      static_cast<char*>(a.v_old), a.counters, a.status, a.T, sh.W, sh.S, sh.M,
-                     sh.n_cache, row_bytes, n_heads, n_parts);
+                     sh.n_cache, row_bytes, rows_per, n_heads, n_parts);
   return hipGetLastError();
 }
 
