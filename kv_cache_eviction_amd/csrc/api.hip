@@ -21,9 +21,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   size_t partial_off, partial_bytes;
   size_t lse_off, lse_bytes;
-  size_t counters_off, counters_bytes;   // B*Hkv counters, the status word, then tile counters
+  size_t counters_off, counters_bytes;   // the device status word
   size_t n_counters;                     // ints cleared at init
-  size_t tiles_per_head;                 // score-kernel column tiles per head (upper bound)
   size_t total;
 };
 
@@ -38,8 +37,7 @@ Layout layout_of(const h2o_config* c) {
   L.lse_off = L.partial_off + L.partial_bytes;
   L.lse_bytes = align_up(static_cast<size_t>(c->batch) * c->n_q_heads * smax * sizeof(float));
   L.counters_off = L.lse_off + L.lse_bytes;
-  L.tiles_per_head = (c->cache_slots + 63) / 64 + (smax + 63) / 64;
-  L.n_counters = heads + 1 + heads * L.tiles_per_head;
+  L.n_counters = 1;
   L.counters_bytes = align_up(L.n_counters * sizeof(int32_t));
   L.total = L.counters_off + L.counters_bytes;
   return L;
@@ -133,21 +131,18 @@ h2o_status run_step(h2o_cache* c, const void* q, const void* k, const void* v, i
   const h2o::StepShape sh = shape_of(c, s);
   float* lse_buf = lse ? lse : reinterpret_cast<float*>(c->ws + c->lay.lse_off);
   float* partial = reinterpret_cast<float*>(c->ws + c->lay.partial_off);
-  int32_t* counters = reinterpret_cast<int32_t*>(c->ws + c->lay.counters_off);
-  int32_t* status = counters + static_cast<size_t>(c->cfg.batch) * c->cfg.n_kv_heads;
+  int32_t* status = reinterpret_cast<int32_t*>(c->ws + c->lay.counters_off);
   const int dtype = c->cfg.dtype;
 
   h2o::AttnArgs aa{q, c->k_cache, c->v_cache, c->pos, k, v, out, lse_buf};
   h2o_status r = timed(c, 0, st, [&] { return h2o::launch_attn_fwd(sh, aa, dtype, st); });
   if (r != H2O_OK) return r;
   const int R = h2o::score_row_splits(sh, dtype);
-  int32_t* tile_counters = status + 1;
-  h2o::ScoreArgs sa{q, c->k_cache, k, lse_buf, partial, c->scores, c->pos, tile_counters, R};
+  h2o::ScoreArgs sa{q, c->k_cache, k, lse_buf, partial, R};
   r = timed(c, 1, st, [&] { return h2o::launch_score(sh, sa, dtype, st); });
   if (r != H2O_OK) return r;
   h2o::SelectArgs xa{c->k_cache, c->v_cache, c->scores, c->pos, k, v, partial, R,
-                     slots_out, step_mass, k_old, v_old, counters, status,
-                     static_cast<int32_t>(c->T)};
+                     slots_out, step_mass, k_old, v_old, status, static_cast<int32_t>(c->T)};
   r = timed(c, 2, st, [&] { return h2o::launch_select_scatter(sh, xa, dtype, st); });
   if (r != H2O_OK) return r;
   c->T += s;
@@ -277,8 +272,7 @@ int64_t h2o_tokens_seen(const h2o_cache* c) { return c ? c->T : -1; }
 h2o_status h2o_device_status(h2o_cache* c, void* stream, int32_t* flags) {
   if (!c || !flags) return H2O_ERR_NULL;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  int32_t* status = reinterpret_cast<int32_t*>(c->ws + c->lay.counters_off) +
-                    static_cast<size_t>(c->cfg.batch) * c->cfg.n_kv_heads;
+  int32_t* status = reinterpret_cast<int32_t*>(c->ws + c->lay.counters_off);
   int32_t host = 0;
   hipError_t e = hipMemcpyAsync(&host, status, sizeof(int32_t), hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);

@@ -10,22 +10,32 @@
 // describe no kernel; the design below is this library's own, for CDNA4.
 //
 // bf16 path (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
-//   * A workgroup is 4 waves; wave w owns one row block = 32 consecutive
-//     queries of one query head.  Row blocks are numbered (query block, head
-//     in group), so the waves of a workgroup share their query range and
-//     therefore their causal extent and every K/V tile.
-//   * The kernel computes S^T = K Q^T: K (64-key tiles) is the A operand read
-//     from LDS, the wave's 32 queries are the B operand held in registers for
-//     the whole kernel.  Each lane then owns one query column, so the row
-//     softmax needs no cross-lane work except one exchange with lane l^32.
+//   * A workgroup is 8 waves in two groups of 4.  Wave w of a group owns one
+//     row block = 32 consecutive queries of one query head; row blocks are
+//     numbered (query block, head in group), so the 4 row blocks of a
+//     workgroup share their query range, causal extent and K/V tiles.  The
+//     two groups split the 64-key tiles between them (even / odd tiles) and
+//     merge their softmax states through LDS at the end; with two waves per
+//     SIMD, one wave's softmax arithmetic overlaps the other's MFMAs.
+//   * The kernel computes S^T = K Q^T: K is the A operand read from LDS, the
+//     wave's 32 queries are the B operand held in registers for the whole
+//     kernel.  Each lane then owns one query column, so the row softmax
+//     needs no cross-lane work except one exchange with lane l^32.
 //   * K rows are stored in LDS in MFMA-row order, chosen so that accumulator
 //     register r of lane l holds key 16(l/32) + r.  The probabilities then
-//     feed O^T = V^T P^T as the B operand straight from registers, and V^T
-//     (transposed into LDS when the tile is staged) is the A operand.
+//     feed O^T = V^T P^T as the B operand straight from registers.  V stays
+//     row-major in LDS and the A operand V^T is read with the gfx950 LDS
+//     transpose load (ds_read_b64_tr_b16): in each 16-lane group, lane i
+//     receives element i%4 of the 8-byte pieces addressed by lanes
+//     4r + i/4, r = 0..3 -- four consecutive keys of one d column.
+//   * 16-byte chunks of every LDS row are XOR-swizzled (per row) so that the
+//     K reads (16 rows, one chunk) and the transpose reads (4 rows, 2-4
+//     chunks) hit distinct banks.
 //   * Online softmax in the log2 domain (exp2 on v_exp_f32); the O rescale
 //     is skipped when no lane's running maximum moved.
-//   * Tiles are staged through registers: the next tile's global loads are
-//     issued before the current tile's MFMAs.
+//   * Tiles pass through registers into a double-buffered LDS ring: the
+//     loads of the next pair of tiles are issued before the current pair is
+//     computed, and one barrier per pair separates the stages.
 //   * blockIdx -> (head, row group) keeps every workgroup of one (b, KV head)
 //     on one XCD when B*Hkv is a multiple of 8 (dispatch is round-robin over
 //     the 8 XCDs), so that head's K/V stays in that XCD's L2; the row groups
@@ -38,8 +48,9 @@
 namespace h2o {
 namespace {
 
-constexpr int kKT = 64;     // keys per LDS tile
-constexpr int kWaves = 4;   // row blocks (waves) per workgroup
+constexpr int kKT = 64;        // keys per LDS tile
+constexpr int kRowBlocks = 4;  // row blocks (32 queries of one head) per workgroup
+constexpr int kFwdThreads = 512;
 
 // Key k (0..31) of a 32-key block -> LDS row = MFMA A-operand row that reads
 // it.  Row 8q + 4h + r holds key 16h + 4q + r, so that accumulator register
@@ -48,47 +59,49 @@ __device__ __forceinline__ int krow_of_key(int k) {
   return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3);
 }
 
-// Column of element (d, key) in the transposed V tile: 8-key groups are
-// XOR-swizzled by (d/8) % 8 to spread the transposing stores over banks;
-// every aligned 8-key group stays contiguous (one 16-byte read).
-__device__ __forceinline__ int vt_col(int d, int k) {
-  return ((((k >> 3) ^ (d >> 3)) & 7) << 3) | (k & 7);
+// Swizzled 16-byte chunk of a K row / V row (CPR chunks per row).
+template <int CPR>
+__device__ __forceinline__ int k_chunk(int row, int c) { return c ^ (row & (CPR - 1)); }
+template <int CPR>
+__device__ __forceinline__ int v_chunk(int row, int c) {
+  return c ^ ((row & 3) << (CPR == 16 ? 2 : 1));
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(
+__global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc,
     const bf16_t* __restrict__ Vc, const int32_t* __restrict__ pos,
     const bf16_t* __restrict__ Kn, const bf16_t* __restrict__ Vn,
     bf16_t* __restrict__ O, float* __restrict__ lse, int Hq, int Hkv, int S,
     int M, int n_cache, float c2, int n_heads, int wg_per_head) {
-  constexpr int DS = D / 16;          // MFMA k-steps over d
-  constexpr int DB = D / 32;          // 32-row blocks of O^T
-  constexpr int KLD = D + 8;          // K tile row stride (elements)
-  constexpr int VLD = kKT + 8;        // V^T tile row stride (elements)
-  constexpr int CPR = D / 8;          // 16-byte chunks per key row
-  constexpr int NCH = kKT * CPR / 256;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[kKT * KLD];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[D * VLD];
-  __shared__ uint64_t s_valid;
+  constexpr int DS = D / 16;              // MFMA k-steps over d
+  constexpr int DB = D / 32;              // 32-row blocks of O^T
+  constexpr int CPR = D / 8;              // 16-byte chunks per row
+  constexpr int TILE = kKT * D;           // elements per K or V tile
+  constexpr int NCH = 2 * 2 * kKT * CPR / kFwdThreads;   // chunks per thread per tile pair
+  // [stage][group][K,V][TILE]
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * 2 * 2 * TILE];
+  __shared__ uint64_t s_valid[2][2];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, col = lane & 31;
+  const int grp = wave >> 2, rbw = wave & 3;
   const int bh = blockIdx.x % n_heads;
   const int wgi = wg_per_head - 1 - static_cast<int>(blockIdx.x) / n_heads;
   const int b = bh / Hkv, kvh = bh - b * Hkv;
   const int G = Hq / Hkv;
   const int n_rb = G * ((S + 31) >> 5);
-  const int rb = wgi * kWaves + wave;
+  const int rb = wgi * kRowBlocks + rbw;
   const bool active = rb < n_rb;
   const int g = active ? rb % G : 0;
   const int qb = active ? rb / G : 0;
   const int qi = qb * 32 + col;
   const int hq = kvh * G + g;
-  const int rb_last = min(wgi * kWaves + kWaves - 1, n_rb - 1);
+  const int rb_last = min(wgi * kRowBlocks + kRowBlocks - 1, n_rb - 1);
   const int n_chunk_keys = min(S, (rb_last / G + 1) * 32);
   const int n_ct = (n_cache + kKT - 1) / kKT;
   const int n_tiles = n_ct + (n_chunk_keys + kKT - 1) / kKT;
+  const int n_pairs = (n_tiles + 1) >> 1;
 
   const bf16_t* kc_head = Kc + static_cast<size_t>(bh) * M * D;
   const bf16_t* vc_head = Vc + static_cast<size_t>(bh) * M * D;
@@ -112,125 +125,181 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(
   for (int db = 0; db < DB; ++db) o[db] = zero16();
   float m_run = kNegInf, l_run = 0.f;
 
-  u32x4 kreg[NCH], vreg[NCH];
-  int preg = 0;
-  auto load_tile = [&](int t) {
-    const bool is_cache = t < n_ct;
-    const int base = is_cache ? t * kKT : (t - n_ct) * kKT;
-    const int lim = is_cache ? n_cache : S;
-    const bf16_t* ks = is_cache ? kc_head : kn_head;
-    const bf16_t* vs = is_cache ? vc_head : vn_head;
+  // ---- staging: tile pair p = tiles (2p, 2p+1); chunk c = tid + 512 r
+  u32x4 reg[NCH];
+  int preg = -1;
+  auto tile_src = [&](int t, int& base, int& lim, bool& is_cache) {
+    is_cache = t < n_ct;
+    base = is_cache ? t * kKT : (t - n_ct) * kKT;
+    lim = is_cache ? n_cache : S;
+  };
+  auto load_pair = [&](int p) {
 #pragma unroll
     for (int r = 0; r < NCH; ++r) {
-      const int c = r * 256 + tid, key = c / CPR, dc = c % CPR;
-      if (base + key < lim) {
-        kreg[r] = load_u32x4(ks + static_cast<size_t>(base + key) * D + dc * 8);
-        vreg[r] = load_u32x4(vs + static_cast<size_t>(base + key) * D + dc * 8);
-      } else {
-        kreg[r] = u32x4{0, 0, 0, 0};
-        vreg[r] = u32x4{0, 0, 0, 0};
-      }
+      const int c = tid + kFwdThreads * r;
+      const int ch = c % CPR, row = (c / CPR) % kKT, mat = (c / (CPR * kKT)) & 1, tt = c / (2 * CPR * kKT);
+      const int t = 2 * p + tt;
+      int base, lim;
+      bool is_cache;
+      tile_src(t, base, lim, is_cache);
+      const bf16_t* src = mat ? (is_cache ? vc_head : vn_head) : (is_cache ? kc_head : kn_head);
+      const int key = base + row;
+      reg[r] = (t < n_tiles && key < lim) ? load_u32x4(src + static_cast<size_t>(key) * D + ch * 8)
+                                          : u32x4{0, 0, 0, 0};
     }
-    if (wave == 0) {
+    if (wave < 2) {                       // wave tt fetches the positions of tile 2p+tt
+      const int t = 2 * p + wave;
+      int base, lim;
+      bool is_cache;
+      tile_src(t, base, lim, is_cache);
       const int key = base + lane;
-      preg = (key < lim) ? (is_cache ? pos_head[key] : 0) : -1;
+      preg = (t < n_tiles && key < lim) ? (is_cache ? pos_head[key] : 0) : -1;
     }
   };
-  auto store_tile = [&]() {
+  auto store_pair = [&](int stage) {
 #pragma unroll
     for (int r = 0; r < NCH; ++r) {
-      const int c = r * 256 + tid, key = c / CPR, dc = c % CPR;
-      const int krow = (key & ~31) | krow_of_key(key & 31);
-      store_u32x4(&Ks[krow * KLD + dc * 8], kreg[r]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = dc * 8 + e;
-        const uint32_t w = vreg[r][e >> 1];
-        Vt[d * VLD + vt_col(d, key)] = static_cast<bf16_t>((e & 1) ? (w >> 16) : (w & 0xffffu));
+      const int c = tid + kFwdThreads * r;
+      const int ch = c % CPR, row = (c / CPR) % kKT, mat = (c / (CPR * kKT)) & 1, tt = c / (2 * CPR * kKT);
+      bf16_t* dst = lds + ((stage * 2 + tt) * 2 + mat) * TILE;
+      if (mat == 0) {
+        const int krow = (row & ~31) | krow_of_key(row & 31);
+        store_u32x4(dst + krow * D + 8 * k_chunk<CPR>(krow, ch), reg[r]);
+      } else {
+        store_u32x4(dst + row * D + 8 * v_chunk<CPR>(row, ch), reg[r]);
       }
     }
-    if (wave == 0) {
+    if (wave < 2) {
       const uint64_t m = __ballot(preg >= 0);
-      if (lane == 0) s_valid = m;
+      if (lane == 0) s_valid[stage][wave] = m;
     }
   };
 
-  if (n_tiles > 0) load_tile(0);
-  for (int t = 0; t < n_tiles; ++t) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < n_tiles) load_tile(t + 1);
-    if (!active) continue;
-    const bool is_cache = t < n_ct;
-    const int base = is_cache ? t * kKT : (t - n_ct) * kKT;
-    if (!is_cache && base > qb * 32 + 31) continue;   // beyond this wave's causal extent
+  // per-lane parts of the transpose-read addresses (see the V^T operand below)
+  const int tr_j = lane & 15, tr_r = tr_j >> 2, tr_q = tr_j & 3, tr_dg = (lane >> 4) & 1;
 
-    f32x16 s0 = zero16(), s1 = zero16();
+  if (n_pairs > 0) {
+    load_pair(0);
+    store_pair(0);
+    if (n_pairs > 1) load_pair(1);
+  }
+  __syncthreads();
+  for (int p = 0; p < n_pairs; ++p) {
+    const int stage = p & 1;
+    const int t = 2 * p + grp;
+    int base, lim;
+    bool is_cache;
+    tile_src(t, base, lim, is_cache);
+    const bool work = active && t < n_tiles && (is_cache || base <= qb * 32 + 31);
+    if (work) {
+      const bf16_t* Kt = lds + ((stage * 2 + grp) * 2 + 0) * TILE;
+      const bf16_t* Vt = lds + ((stage * 2 + grp) * 2 + 1) * TILE;
+      f32x16 s0 = zero16(), s1 = zero16();
 #pragma unroll
-    for (int st = 0; st < DS; ++st) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&Ks[col * KLD + 16 * st + 8 * hf]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&Ks[(32 + col) * KLD + 16 * st + 8 * hf]);
-      s0 = mfma32x32x16(a0, qf[st], s0);
-      s1 = mfma32x32x16(a1, qf[st], s1);
-    }
-    const uint64_t vm = s_valid;
-    const bool causal = !is_cache && (base + kKT - 1 > qb * 32);
-    if (vm != ~0ull || causal) {
-      const uint32_t bits0 = static_cast<uint32_t>(vm >> (16 * hf)) & 0xffffu;
-      const uint32_t bits1 = static_cast<uint32_t>(vm >> (32 + 16 * hf)) & 0xffffu;
-      const int lim_i = causal ? qi - base - 16 * hf : 1 << 30;   // key offset bound
+      for (int st = 0; st < DS; ++st) {
+        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(Kt + col * D + 8 * k_chunk<CPR>(col, 2 * st + hf));
+        const bf16x8 a1 =
+            *reinterpret_cast<const bf16x8*>(Kt + (32 + col) * D + 8 * k_chunk<CPR>(32 + col, 2 * st + hf));
+        s0 = mfma32x32x16(a0, qf[st], s0);
+        s1 = mfma32x32x16(a1, qf[st], s1);
+      }
+      const uint64_t vm = s_valid[stage][grp];
+      const bool causal = !is_cache && (base + kKT - 1 > qb * 32);
+      if (vm != ~0ull || causal) {
+        const uint32_t bits0 = static_cast<uint32_t>(vm >> (16 * hf)) & 0xffffu;
+        const uint32_t bits1 = static_cast<uint32_t>(vm >> (32 + 16 * hf)) & 0xffffu;
+        const int lim_i = causal ? qi - base - 16 * hf : 1 << 30;   // key offset bound
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool ok0 = ((bits0 >> r) & 1u) && (r <= lim_i);
+          const bool ok1 = ((bits1 >> r) & 1u) && (32 + r <= lim_i);
+          s0[r] = ok0 ? s0[r] : kNegInf;
+          s1[r] = ok1 ? s1[r] : kNegInf;
+        }
+      }
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+      mx = fmaxf(mx, xor32(mx));
+      const float m_new = fmaxf(m_run, mx * c2);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      float rs = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const bool ok0 = ((bits0 >> r) & 1u) && (r <= lim_i);
-        const bool ok1 = ((bits1 >> r) & 1u) && (32 + r <= lim_i);
-        s0[r] = ok0 ? s0[r] : kNegInf;
-        s1[r] = ok1 ? s1[r] : kNegInf;
+        s0[r] = fast_exp2(fmaf(s0[r], c2, -m_use));
+        s1[r] = fast_exp2(fmaf(s1[r], c2, -m_use));
+        rs += s0[r] + s1[r];
       }
-    }
-    float mx = kNegInf;
+      l_run = fmaf(l_run, alpha, rs);
+      m_run = m_new;
+      if (__ballot(alpha != 1.f)) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-    mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m_run, mx * c2);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    float rs = 0.f;
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s0[r] = fast_exp2(fmaf(s0[r], c2, -m_use));
-      s1[r] = fast_exp2(fmaf(s1[r], c2, -m_use));
-      rs += s0[r] + s1[r];
-    }
-    l_run = fmaf(l_run, alpha, rs);
-    m_run = m_new;
-    if (__ballot(alpha != 1.f)) {
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      }
+      // O^T += V^T P^T; MFMA (kb,u) covers keys 32kb + 16(l/32) + 8u + e.  The
+      // A operand V^T comes from two transpose reads: lane j = 4r + q of a
+      // 16-lane group addresses V[key0 + r][d0 + 4q .. +4).
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-    }
-    // O^T += V^T P^T; MFMA (kb,u) covers keys 32kb + 16(l/32) + 8u + e.
+        for (int u = 0; u < 2; ++u) {
+          const f32x16& sv = kb ? s1 : s0;
+          f32x8 pv;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+          for (int e = 0; e < 8; ++e) pv[e] = sv[8 * u + e];
+          const bf16x8 pb = to_bf16x8(pv);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const f32x16& s = kb ? s1 : s0;
-        f32x8 pv;
+          for (int db = 0; db < DB; ++db) {
+            const int d = db * 32 + tr_dg * 16 + 4 * tr_q;
+            bf16x4 h0, h1;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = s[8 * u + e];
-        const bf16x8 pb = to_bf16x8(pv);
-        const int key = kb * 32 + 16 * hf + 8 * u;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int d = db * 32 + col;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Vt[d * VLD + vt_col(d, key)]);
-          o[db] = mfma32x32x16(a, pb, o[db]);
+            for (int t2 = 0; t2 < 2; ++t2) {
+              const int key = kb * 32 + 16 * hf + 8 * u + 4 * t2 + tr_r;
+              const bf16x4 v = lds_read_tr16(Vt + key * D + 8 * v_chunk<CPR>(key, d >> 3) + (d & 7));
+              if (t2 == 0) h0 = v; else h1 = v;
+            }
+            const bf16x8 a = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+            o[db] = mfma32x32x16(a, pb, o[db]);
+          }
         }
       }
     }
+    // stage the next pair into the other buffer, prefetch the one after
+    if (p + 1 < n_pairs) store_pair(stage ^ 1);
+    if (p + 2 < n_pairs) load_pair(p + 2);
+    __syncthreads();
   }
-  if (!active) return;
+
+  // ---- merge the two groups' softmax states (group 1 -> LDS -> group 0)
+  float* xch = reinterpret_cast<float*>(lds);            // [DB*16 + 2][kRowBlocks*64]
+  const int slot = rbw * 64 + lane;
+  constexpr int NX = kRowBlocks * 64;
+  if (grp == 1) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xch[(db * 16 + r) * NX + slot] = o[db][r];
+    xch[(DB * 16) * NX + slot] = m_run;
+    xch[(DB * 16 + 1) * NX + slot] = l_run;
+  }
+  __syncthreads();
+  if (grp == 1 || !active) return;
+  {
+    const float m1 = xch[(DB * 16) * NX + slot];
+    const float l1 = xch[(DB * 16 + 1) * NX + slot];
+    const float m = fmaxf(m_run, m1);
+    const float mu = (m == kNegInf) ? 0.f : m;
+    const float a0 = fast_exp2(m_run - mu), a1 = fast_exp2(m1 - mu);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + xch[(db * 16 + r) * NX + slot] * a1;
+    l_run = l_run * a0 + l1 * a1;
+    m_run = m;
+  }
   const float l_tot = l_run + xor32(l_run);
   if (qi >= S) return;
   const float inv = 1.f / l_tot;
@@ -331,8 +400,8 @@ hipError_t launch_attn_fwd(const StepShape& sh, const AttnArgs& a, int dtype, hi
   const float c2 = sh.scale * kLog2e;
   if (dtype == kBF16) {
     const int n_rb = G * ((sh.S + 31) / 32);
-    const int wgp = (n_rb + kWaves - 1) / kWaves;
-    const dim3 grid(n_heads * wgp), block(256);
+    const int wgp = (n_rb + kRowBlocks - 1) / kRowBlocks;
+    const dim3 grid(n_heads * wgp), block(kFwdThreads);
 #define H2O_LAUNCH_FWD(DD)                                                                          \
   hipLaunchKernelGGL(attn_fwd_bf16_kernel<DD>, grid, block, 0, st,                                  \
                      static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k_cache),        \

@@ -31,6 +31,14 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ds_read_b64_tr_b16 (gfx950) from a pointer into __shared__ memory: in each
+// 16-lane group, lane i receives element i%4 of the 8-byte pieces addressed
+// by lanes 4r + i/4, r = 0..3.
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+__device__ __forceinline__ bf16x4 lds_read_tr16(const bf16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
+}
+
 __device__ __forceinline__ bf16x8 load_bf16x8(const bf16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }

@@ -30,27 +30,23 @@ struct ScoreArgs {
   const void* k_cache;
   const void* k_new;
   const float* lse;
-  float* partial;          // [B*Hkv][R][M + S]; row 0 holds the finalized masses
-  float* scores;           // filled slots gain the step's mass
-  const int32_t* pos;
-  int32_t* tile_counters;  // [B*Hkv][score_tiles], zero between launches
+  float* partial;          // [B*Hkv][R][M + S]: per-split column sums
   int R;                   // row splits
 };
 
 struct SelectArgs {
   void* k_cache;
   void* v_cache;
-  float* scores;          // already hold the step's mass (score kernel)
+  float* scores;
   int32_t* pos;
   const void* k_new;
   const void* v_new;
-  const float* mass;      // [B*Hkv][R][M + S]: row 0 = step mass per slot, then mu_j
-  int R;                  // row stride of `mass` per head
+  const float* partial;   // [B*Hkv][R][M + S]: per-split masses of cache slots, then chunk keys
+  int R;
   int32_t* slots_out;   // nullable
   float* step_mass;     // nullable
   void* k_old;          // nullable
   void* v_old;          // nullable
-  int32_t* counters;    // [B*Hkv], zero between launches
   int32_t* status;      // device status word
   int32_t T;            // tokens seen before the chunk
 };
@@ -65,8 +61,6 @@ hipError_t launch_reset(float* scores, int32_t* pos, int64_t n_slots, int32_t* c
 
 // Row splits the score kernel uses for a step of this shape (host heuristic).
 int score_row_splits(const StepShape& sh, int dtype);
-// Column tiles of the score kernel (one arrival counter each).
-int score_tiles(const StepShape& sh, int dtype);
 // Upper bound of score_row_splits over every S <= s_max (workspace sizing).
 int score_row_splits_max();
 

@@ -8,14 +8,10 @@
 //
 // P = exp(z - lse) is recomputed from Q, K and the forward's lse (the
 // forward's online softmax cannot normalise a column before every row is
-// done), and reduced over rows without atomics on the sums: each workgroup
-// owns a tile of 256 key columns and one contiguous range of query rows (a
-// "row split") and writes one partial sum per column.  The last workgroup of
-// a column tile to finish (a per-tile arrival counter) adds the R partials
-// in split order -- deterministic -- and writes the step's mass: filled
-// cache slots get score += mass, and the masses of the tile (0 for free
-// slots; mu_j for chunk key j) go to row 0 of the partial buffer, which the
-// select kernel reads.
+// done), and reduced over rows without atomics: each workgroup owns a tile
+// of 256 key columns and one contiguous range of query rows (a "row split")
+// and writes one partial sum per column.  The select kernel adds the R
+// partials of a column in split order, so the result is deterministic.
 //
 // bf16 path: S = Q K^T on v_mfma_f32_32x32x16_bf16 with the wave's 64 keys
 // as the B operand held in registers for the whole kernel and 64-row query
@@ -33,35 +29,11 @@ constexpr int kCT = 256;        // key columns per workgroup (4 waves x 64)
 constexpr int kRB = 64;         // query rows per staged block (2 MFMA row blocks)
 constexpr int kRowSplitsMax = 16;
 
-// Last-arrival finalize of one column tile: sums the R partials of each
-// column in split order, updates the scores of filled slots and stores the
-// step's masses into partial row 0.
-__device__ void finalize_tile(float* __restrict__ ph, size_t PS, int R, bool is_cache, int base,
-                              int lim, int M, float* __restrict__ sc_h,
-                              const int32_t* __restrict__ pos_h) {
-  for (int c = threadIdx.x; c < kCT; c += blockDim.x) {
-    const int key = base + c;
-    if (key >= lim) break;
-    const size_t x = (is_cache ? 0 : static_cast<size_t>(M)) + key;
-    float s = 0.f;
-    for (int r = 0; r < R; ++r) s += ph[r * PS + x];
-    if (is_cache) {
-      if (pos_h[key] >= 0) {
-        sc_h[key] += s;
-      } else {
-        s = 0.f;
-      }
-    }
-    ph[x] = s;
-  }
-}
-
 template <int D>
 __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc,
     const bf16_t* __restrict__ Kn, const float* __restrict__ lse,
-    float* __restrict__ partial, float* __restrict__ scores, const int32_t* __restrict__ pos,
-    int32_t* __restrict__ tile_cnt, int Hq, int Hkv, int S, int M, int n_cache, float c2,
+    float* __restrict__ partial, int Hq, int Hkv, int S, int M, int n_cache, float c2,
     int n_heads, int n_ct, int n_tiles, int R) {
   constexpr int DS = D / 16;
   constexpr int QLD = D + 8;
@@ -70,7 +42,6 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
   __shared__ __attribute__((aligned(16))) bf16_t Qs[2][kRB * QLD];
   __shared__ float s_lse2[2][kRB];
   __shared__ int s_irow[2][kRB];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hf = lane >> 5, col = lane & 31;
@@ -215,27 +186,12 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
   cs0 += xor32(cs0);
   cs1 += xor32(cs1);
   const size_t PS = static_cast<size_t>(M) + S;
-  float* ph = partial + static_cast<size_t>(bh) * R * PS;
   if (hf == 0) {
-    float* out = ph + static_cast<size_t>(split) * PS + (is_cache ? 0 : M);
+    float* out = partial + (static_cast<size_t>(bh) * R + split) * PS + (is_cache ? 0 : M);
     const int k0 = key0 + col, k1 = key0 + 32 + col;
     if (k0 < lim) out[k0] = cs0;
     if (k1 < lim) out[k1] = cs1;
   }
-  // the last of the R workgroups of this column tile finalizes it
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    int* cnt = tile_cnt + static_cast<size_t>(bh) * n_tiles + tile;
-    const int prev = atomicAdd(cnt, 1);
-    s_last = prev == R - 1;
-    if (s_last) *cnt = 0;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  finalize_tile(ph, PS, R, is_cache, base, lim, M, scores + static_cast<size_t>(bh) * M,
-                pos + static_cast<size_t>(bh) * M);
 }
 
 // fp32: one thread per key column, query rows streamed through LDS; one row
@@ -243,9 +199,8 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
 template <int D>
 __global__ __launch_bounds__(64) void score_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ Kc, const float* __restrict__ Kn,
-    const float* __restrict__ lse, float* __restrict__ partial, float* __restrict__ scores,
-    const int32_t* __restrict__ pos, int Hq, int Hkv, int S, int M, int n_cache, float c2,
-    int n_heads, int n_ct, int n_tiles) {
+    const float* __restrict__ lse, float* __restrict__ partial, int Hq, int Hkv, int S, int M,
+    int n_cache, float c2, int n_heads, int n_ct, int n_tiles) {
   constexpr int RT = 16;
   __shared__ float Qs[RT][D];
   __shared__ float ls[RT];
@@ -288,18 +243,7 @@ __global__ __launch_bounds__(64) void score_f32_kernel(
       cs += fast_exp2(fmaf(z, c2, -ls[rr]));
     }
   }
-  if (!ok) return;
-  float* out = partial + static_cast<size_t>(bh) * (M + S);
-  if (is_cache) {
-    if (pos[static_cast<size_t>(bh) * M + key] >= 0) {
-      scores[static_cast<size_t>(bh) * M + key] += cs;
-    } else {
-      cs = 0.f;
-    }
-    out[key] = cs;
-  } else {
-    out[M + key] = cs;
-  }
+  if (ok) partial[static_cast<size_t>(bh) * (M + S) + (is_cache ? 0 : M) + key] = cs;
 }
 
 }  // namespace
@@ -334,8 +278,8 @@ hipError_t launch_score(const StepShape& sh, const ScoreArgs& a, int dtype, hipS
 #define H2O_LAUNCH_SCORE(DD)                                                                      \
   hipLaunchKernelGGL(score_bf16_kernel<DD>, grid, block, 0, st, static_cast<const bf16_t*>(a.q), \
                      static_cast<const bf16_t*>(a.k_cache), static_cast<const bf16_t*>(a.k_new), \
-                     a.lse, a.partial, a.scores, a.pos, a.tile_counters, sh.Hq, sh.Hkv, sh.S,     \
-                     sh.M, sh.n_cache, c2, n_heads, n_ct, n_tiles, a.R)
+                     a.lse, a.partial, sh.Hq, sh.Hkv, sh.S, sh.M, sh.n_cache, c2, n_heads, n_ct, \
+                     n_tiles, a.R)
     if (sh.D == 128) H2O_LAUNCH_SCORE(128);
     else H2O_LAUNCH_SCORE(64);
 #undef H2O_LAUNCH_SCORE
@@ -346,8 +290,8 @@ hipError_t launch_score(const StepShape& sh, const ScoreArgs& a, int dtype, hipS
 #define H2O_LAUNCH_SCORE32(DD)                                                                  \
   hipLaunchKernelGGL(score_f32_kernel<DD>, grid, block, 0, st, static_cast<const float*>(a.q), \
                      static_cast<const float*>(a.k_cache), static_cast<const float*>(a.k_new), \
-                     a.lse, a.partial, a.scores, a.pos, sh.Hq, sh.Hkv, sh.S, sh.M, sh.n_cache,  \
-                     c2, n_heads, n_ct, n_tiles)
+                     a.lse, a.partial, sh.Hq, sh.Hkv, sh.S, sh.M, sh.n_cache, c2, n_heads, n_ct, \
+                     n_tiles)
     if (sh.D == 128) H2O_LAUNCH_SCORE32(128);
     else H2O_LAUNCH_SCORE32(64);
 #undef H2O_LAUNCH_SCORE32

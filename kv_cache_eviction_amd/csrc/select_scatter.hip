@@ -11,30 +11,27 @@
 // smallest (score, slot index); chunk token j goes to the j-th smallest
 // target slot.
 //
-// The score kernel has already added this step's mass to every filled slot.
-// One workgroup handles a share of the chunk's rows for one (b, KV head): it
-// issues the loads of its chunk rows first, then recomputes the same
-// selection as every other workgroup of the head (deterministic), then
-// stores its rows into their slots.  It counts itself done on a per-head
-// counter; the last one to finish writes scores and positions of the
-// targets (no workgroup still reads them at that point) and clears the
-// counter for the next launch.
-//
-// Selection: scores map to order-preserving 32-bit keys; the bits all
-// candidates share are found with an AND/OR reduction and skipped, then the
-// n_e-th smallest key is found by 8-bit LDS radix passes over the remaining
-// bits; equal keys resolve to the lowest slot by an exclusive scan over slot
-// order.
+// One 1024-thread workgroup owns one (b, KV head): no other workgroup reads
+// or writes that head's scores, positions or slots, so the kernel needs no
+// inter-workgroup synchronisation.  It
+//   1. adds the score kernel's R per-split masses to the filled slots'
+//      scores (fixed split order: deterministic);
+//   2. selects the targets: scores map to order-preserving 32-bit keys, the
+//      bits every candidate shares are found with an AND/OR reduction and
+//      skipped, and 8-bit LDS radix passes over the remaining bits find the
+//      n_e-th smallest key; equal keys resolve to the lowest slot through an
+//      exclusive scan in slot order;
+//   3. writes scores and positions, then copies the chunk's K/V rows into
+//      their slots (the first rows' loads were issued before the selection).
 #include "h2o_device.h"
 #include "h2o_launch.h"
 
 namespace h2o {
 namespace {
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 1024;
 constexpr int kWavesSel = kThreads / 64;
-constexpr int kRowChunks = 4;        // 16-byte chunks per thread per matrix (K or V) prefetched
-constexpr int kMaxParts = 256;      // S <= 16384 rows of at most 512 bytes
+constexpr int kPre = 4;        // 16-byte chunks of K and of V each thread prefetches
 
 enum : uint8_t { kFree = 0, kCand = 1, kKeep = 2, kTarget = 4 };
 
@@ -44,6 +41,9 @@ enum : uint8_t { kFree = 0, kCand = 1, kKeep = 2, kTarget = 4 };
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
@@ -74,7 +74,7 @@ __device__ int block_excl_scan(int v, int* tmp, int& total) {
   return before + incl - v;
 }
 
-// Block-wide AND and OR of v (utmp holds 2*kWavesSel words of LDS).
+// Block-wide AND and OR (utmp holds 2*kWavesSel words of LDS).
 __device__ void block_and_or(uint32_t v_and, uint32_t v_or, uint32_t* utmp, uint32_t& r_and,
                              uint32_t& r_or) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -101,10 +101,9 @@ __device__ void block_and_or(uint32_t v_and, uint32_t v_or, uint32_t* utmp, uint
 __global__ __launch_bounds__(kThreads) void select_scatter_kernel(
     char* __restrict__ kc, char* __restrict__ vc, float* __restrict__ scores,
     int32_t* __restrict__ pos, const char* __restrict__ kn, const char* __restrict__ vn,
-    const float* __restrict__ mass, int R, int32_t* __restrict__ slots_out,
+    const float* __restrict__ partial, int R, int32_t* __restrict__ slots_out,
     float* __restrict__ step_mass, char* __restrict__ k_old, char* __restrict__ v_old,
-    int32_t* __restrict__ counters, int32_t* __restrict__ status, int T, int W, int S, int M,
-    int n_cache, int row_bytes, int rows_per, int n_heads, int n_parts) {
+    int32_t* __restrict__ status, int T, int W, int S, int M, int n_cache, int row_bytes) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   uint32_t* s_key = reinterpret_cast<uint32_t*>(smem);                        // [M]
   int* s_R = reinterpret_cast<int*>(smem + 4 * static_cast<size_t>(M));      // [S]
@@ -113,38 +112,33 @@ __global__ __launch_bounds__(kThreads) void select_scatter_kernel(
   __shared__ int s_tmp[kWavesSel];
   __shared__ uint32_t s_utmp[2 * kWavesSel];
   __shared__ int s_sel[2];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int bh = blockIdx.x % n_heads;
-  const int part = static_cast<int>(blockIdx.x) / n_heads;
+  const int bh = blockIdx.x;
   const size_t PS = static_cast<size_t>(M) + S;
-  const float* mh = mass + static_cast<size_t>(bh) * R * PS;     // row 0 of the head
+  const float* ph = partial + static_cast<size_t>(bh) * R * PS;
   float* sc_h = scores + static_cast<size_t>(bh) * M;
   int32_t* pos_h = pos + static_cast<size_t>(bh) * M;
 
-  // 0. issue the loads of this workgroup's chunk rows (independent of the selection)
-  const int j0 = min(S, part * rows_per), j1 = min(S, j0 + rows_per);
-  const int cpr = row_bytes / 16;
-  const int n_chunks = (j1 - j0) * cpr;
-  u32x4 kr[kRowChunks], vr[kRowChunks];
-#pragma unroll
-  for (int i = 0; i < kRowChunks; ++i) {
-    const int idx = tid + i * kThreads;
-    if (idx < n_chunks) {
-      const size_t src = (static_cast<size_t>(bh) * S + j0) * row_bytes + 16 * static_cast<size_t>(idx);
-      kr[i] = load_u32x4(kn + src);
-      vr[i] = load_u32x4(vn + src);
-    }
-  }
-
-  // 1. slot classes and keys; AND/OR of the candidate keys
+  // 1. scores after this step's mass; slot classes; AND/OR of candidate keys
   int my_free = 0, my_cand = 0;
   uint32_t k_and = 0xffffffffu, k_or = 0u;
+#pragma unroll 4
   for (int m = tid; m < M; m += kThreads) {
     const int p = pos_h[m];
-    const uint32_t key = order_key(sc_h[m]);
-    const uint8_t fl = p < 0 ? kFree : ((p < T - W) ? kCand : kKeep);
+    float s = sc_h[m];
+    float ds = 0.f;
+    if (m < n_cache)
+      for (int r = 0; r < R; ++r) ds += ph[static_cast<size_t>(r) * PS + m];
+    uint8_t fl = kFree;
+    if (p >= 0) {
+      s += ds;
+      fl = (p < T - W) ? kCand : kKeep;
+    } else {
+      ds = 0.f;
+    }
+    if (step_mass) step_mass[static_cast<size_t>(bh) * PS + m] = ds;
+    const uint32_t key = order_key(s);
     s_key[m] = key;
     s_fl[m] = fl;
     my_free += fl == kFree;
@@ -154,13 +148,28 @@ __global__ __launch_bounds__(kThreads) void select_scatter_kernel(
       k_or |= key;
     }
   }
+  // prefetch the first chunk rows while the selection runs
+  const int cpr = row_bytes / 16;
+  const int n_chunks = S * cpr;
+  u32x4 kr[kPre], vr[kPre];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) {
+    const int idx = tid + i * kThreads;
+    if (idx < n_chunks) {
+      const size_t src = static_cast<size_t>(bh) * S * row_bytes + 16 * static_cast<size_t>(idx);
+      kr[i] = load_u32x4(kn + src);
+      vr[i] = load_u32x4(vn + src);
+    }
+  }
   int n_free, n_cand;
   block_excl_scan(my_free, s_tmp, n_free);
   block_excl_scan(my_cand, s_tmp, n_cand);
   const int n_f = min(S, n_free);
   const int n_e = S - n_f;
   if (n_cand < n_e) {                      // infeasible adopted state: no slot is written
-    if (part == 0 && tid == 0) atomicOr(status, 1);
+    for (int m = tid; m < M; m += kThreads)
+      if (s_fl[m] != kFree) sc_h[m] = key_value(s_key[m]);
+    if (tid == 0) atomicOr(status, 1);
     return;
   }
 
@@ -232,6 +241,7 @@ __global__ __launch_bounds__(kThreads) void select_scatter_kernel(
       eq += u == thr;
     }
     if (t) s_fl[m] = fl | kTarget;
+    else if (fl != kFree) sc_h[m] = key_value(s_key[m]);    // kept filled slot: new score
     c_t += t;
   }
   int j = block_excl_scan(c_t, s_tmp, dummy);
@@ -239,47 +249,52 @@ __global__ __launch_bounds__(kThreads) void select_scatter_kernel(
     if ((s_fl[m] & kTarget) && j < S) s_R[j++] = m;
   __syncthreads();
 
-  // 4. store this workgroup's chunk rows into their slots (old rows to the delta)
-#pragma unroll
-  for (int i = 0; i < kRowChunks; ++i) {
-    const int idx = tid + i * kThreads;
-    if (idx < n_chunks) {
-      const int jj = j0 + idx / cpr, c = idx % cpr;
-      const int slot = s_R[jj];
-      const size_t src = (static_cast<size_t>(bh) * S + jj) * row_bytes + 16 * c;
-      const size_t dst = (static_cast<size_t>(bh) * M + slot) * row_bytes + 16 * c;
-      if (k_old) {
-        const bool was_free = (s_fl[slot] & 3) == kFree;
-        const u32x4 z = {0, 0, 0, 0};
-        store_u32x4(k_old + src, was_free ? z : load_u32x4(kc + dst));
-        store_u32x4(v_old + src, was_free ? z : load_u32x4(vc + dst));
-      }
-      store_u32x4(kc + dst, kr[i]);
-      store_u32x4(vc + dst, vr[i]);
-    }
-  }
-
-  // 5. the last workgroup of this head writes the targets' scores and positions
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = atomicAdd(&counters[bh], 1);
-    s_last = prev == n_parts - 1;
-    if (s_last) counters[bh] = 0;
-  }
-  __syncthreads();
-  if (!s_last) return;
+  // 4. targets: score = mass from the chunk's own queries, position T + j
   for (int jj = tid; jj < S; jj += kThreads) {
     const int slot = s_R[jj];
-    const float mu = mh[M + jj];
+    float mu = 0.f;
+    for (int r = 0; r < R; ++r) mu += ph[static_cast<size_t>(r) * PS + M + jj];
     sc_h[slot] = mu;
     pos_h[slot] = T + jj;
     if (slots_out) slots_out[static_cast<size_t>(bh) * S + jj] = slot;
     if (step_mass) step_mass[static_cast<size_t>(bh) * PS + M + jj] = mu;
   }
-  if (step_mass) {
-    for (int m = tid; m < M; m += kThreads)
-      step_mass[static_cast<size_t>(bh) * PS + m] = m < n_cache ? mh[m] : 0.f;
+
+  // 5. copy the chunk's K/V rows into their slots (old rows to the delta)
+  auto put = [&](int idx, const u32x4& kv, const u32x4& vv) {
+    const int jj = idx / cpr, c = idx - jj * cpr;
+    const int slot = s_R[jj];
+    const size_t src = (static_cast<size_t>(bh) * S + jj) * row_bytes + 16 * c;
+    const size_t dst = (static_cast<size_t>(bh) * M + slot) * row_bytes + 16 * c;
+    if (k_old) {
+      const bool was_free = (s_fl[slot] & 3) == kFree;
+      const u32x4 z = {0, 0, 0, 0};
+      store_u32x4(k_old + src, was_free ? z : load_u32x4(kc + dst));
+      store_u32x4(v_old + src, was_free ? z : load_u32x4(vc + dst));
+    }
+    store_u32x4(kc + dst, kv);
+    store_u32x4(vc + dst, vv);
+  };
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) {
+    const int idx = tid + i * kThreads;
+    if (idx < n_chunks) put(idx, kr[i], vr[i]);
+  }
+  for (int base = kPre * kThreads; base < n_chunks; base += kPre * kThreads) {
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+      const int idx = base + tid + i * kThreads;
+      if (idx < n_chunks) {
+        const size_t src = static_cast<size_t>(bh) * S * row_bytes + 16 * static_cast<size_t>(idx);
+        kr[i] = load_u32x4(kn + src);
+        vr[i] = load_u32x4(vn + src);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+      const int idx = base + tid + i * kThreads;
+      if (idx < n_chunks) put(idx, kr[i], vr[i]);
+    }
   }
 }
 
@@ -295,31 +310,25 @@ __global__ void reset_kernel(float* scores, int32_t* pos, int64_t n, int32_t* co
 
 }  // namespace
 
-int select_rows_per_part(int row_bytes) {
-  // each thread prefetches kRowChunks 16-byte chunks of K and of V
-  return kThreads * kRowChunks * 16 / row_bytes;
+size_t select_lds_bytes(int M, int S) {
+  return 4 * static_cast<size_t>(M) + 4 * static_cast<size_t>(S) + static_cast<size_t>(M) + 16;
 }
 
 hipError_t launch_select_scatter(const StepShape& sh, const SelectArgs& a, int dtype, hipStream_t st) {
   const int n_heads = sh.B * sh.Hkv;
   const int row_bytes = sh.D * (dtype == kBF16 ? 2 : 4);
-  int rows_per = select_rows_per_part(row_bytes);
-  int n_parts = (sh.S + rows_per - 1) / rows_per;
-  if (n_parts > kMaxParts) return hipErrorInvalidValue;   // excluded by config validation
-  n_parts = n_parts < 1 ? 1 : n_parts;
-  const size_t lds = 4 * static_cast<size_t>(sh.M) + 4 * static_cast<size_t>(sh.S) +
-                     static_cast<size_t>(sh.M) + 16;
+  const size_t lds = select_lds_bytes(sh.M, sh.S);
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_scatter_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(select_scatter_kernel, dim3(n_heads * n_parts), dim3(kThreads), lds, st,
+  hipLaunchKernelGGL(select_scatter_kernel, dim3(n_heads), dim3(kThreads), lds, st,
                      static_cast<char*>(a.k_cache), static_cast<char*>(a.v_cache), a.scores, a.pos,
-                     static_cast<const char*>(a.k_new), static_cast<const char*>(a.v_new), a.mass,
+                     static_cast<const char*>(a.k_new), static_cast<const char*>(a.v_new), a.partial,
                      a.R, a.slots_out, a.step_mass, static_cast<char*>(a.k_old),
-                     static_cast<char*>(a.v_old), a.counters, a.status, a.T, sh.W, sh.S, sh.M,
-                     sh.n_cache, row_bytes, rows_per, n_heads, n_parts);
+                     static_cast<char*>(a.v_old), a.status, a.T, sh.W, sh.S, sh.M, sh.n_cache,
+                     row_bytes);
   return hipGetLastError();
 }
 
