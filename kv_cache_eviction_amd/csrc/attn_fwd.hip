@@ -125,48 +125,70 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   for (int db = 0; db < DB; ++db) o[db] = zero16();
   float m_run = kNegInf, l_run = 0.f;
 
-  // ---- staging: tile pair p = tiles (2p, 2p+1); chunk c = tid + 512 r
+  // ---- staging: tile pair p = tiles (2p, 2p+1).  Chunk r of a thread is
+  // c = tid + 512 r; its tile (tt), matrix (K or V) and row follow from r at
+  // compile time, so every source pointer is a uniform per-tile value.
+  struct TileSrc {
+    const bf16_t* k;
+    const bf16_t* v;
+    int n;            // rows of the tile that exist (keys < lim)
+  };
+  auto tile_src = [&](int t) __attribute__((always_inline)) {
+    TileSrc r;
+    const bool is_cache = t < n_ct;
+    const int base = is_cache ? t * kKT : (t - n_ct) * kKT;
+    const int lim = t < n_tiles ? (is_cache ? n_cache : S) : base;
+    r.k = (is_cache ? kc_head : kn_head) + static_cast<size_t>(base) * D;
+    r.v = (is_cache ? vc_head : vn_head) + static_cast<size_t>(base) * D;
+    r.n = lim - base;
+    return r;
+  };
+  constexpr int RPT = NCH / 2;                  // chunks per thread per tile
+  constexpr int RPM = RPT / 2;                  // chunks per thread per matrix of a tile
+  const int ch = tid % CPR;                     // 16-byte chunk within the row
+  const int row0 = tid / CPR;                   // first row; chunk r adds (r % RPM) * (512 / CPR)
   u32x4 reg[NCH];
   int preg = -1;
-  auto tile_src = [&](int t, int& base, int& lim, bool& is_cache) {
-    is_cache = t < n_ct;
-    base = is_cache ? t * kKT : (t - n_ct) * kKT;
-    lim = is_cache ? n_cache : S;
-  };
-  auto load_pair = [&](int p) {
+  auto load_pair = [&](int p) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < NCH; ++r) {
-      const int c = tid + kFwdThreads * r;
-      const int ch = c % CPR, row = (c / CPR) % kKT, mat = (c / (CPR * kKT)) & 1, tt = c / (2 * CPR * kKT);
-      const int t = 2 * p + tt;
-      int base, lim;
-      bool is_cache;
-      tile_src(t, base, lim, is_cache);
-      const bf16_t* src = mat ? (is_cache ? vc_head : vn_head) : (is_cache ? kc_head : kn_head);
-      const int key = base + row;
-      reg[r] = (t < n_tiles && key < lim) ? load_u32x4(src + static_cast<size_t>(key) * D + ch * 8)
-                                          : u32x4{0, 0, 0, 0};
+    for (int tt = 0; tt < 2; ++tt) {
+      const TileSrc ts = tile_src(2 * p + tt);
+#pragma unroll
+      for (int mat = 0; mat < 2; ++mat) {
+#pragma unroll
+        for (int i = 0; i < RPM; ++i) {
+          const int row = row0 + i * (kFwdThreads / CPR);
+          const bf16_t* src = (mat ? ts.v : ts.k) + row * D + ch * 8;
+          reg[(tt * 2 + mat) * RPM + i] = row < ts.n ? load_u32x4(src) : u32x4{0, 0, 0, 0};
+        }
+      }
     }
     if (wave < 2) {                       // wave tt fetches the positions of tile 2p+tt
       const int t = 2 * p + wave;
-      int base, lim;
-      bool is_cache;
-      tile_src(t, base, lim, is_cache);
+      const bool is_cache = t < n_ct;
+      const int base = is_cache ? t * kKT : (t - n_ct) * kKT;
+      const int lim = t < n_tiles ? (is_cache ? n_cache : S) : base;
       const int key = base + lane;
-      preg = (t < n_tiles && key < lim) ? (is_cache ? pos_head[key] : 0) : -1;
+      preg = key < lim ? (is_cache ? pos_head[key] : 0) : -1;
     }
   };
-  auto store_pair = [&](int stage) {
+  auto store_pair = [&](int stage) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < NCH; ++r) {
-      const int c = tid + kFwdThreads * r;
-      const int ch = c % CPR, row = (c / CPR) % kKT, mat = (c / (CPR * kKT)) & 1, tt = c / (2 * CPR * kKT);
-      bf16_t* dst = lds + ((stage * 2 + tt) * 2 + mat) * TILE;
-      if (mat == 0) {
-        const int krow = (row & ~31) | krow_of_key(row & 31);
-        store_u32x4(dst + krow * D + 8 * k_chunk<CPR>(krow, ch), reg[r]);
-      } else {
-        store_u32x4(dst + row * D + 8 * v_chunk<CPR>(row, ch), reg[r]);
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int mat = 0; mat < 2; ++mat) {
+        bf16_t* dst = lds + ((stage * 2 + tt) * 2 + mat) * TILE;
+#pragma unroll
+        for (int i = 0; i < RPM; ++i) {
+          const int row = row0 + i * (kFwdThreads / CPR);
+          const u32x4 v = reg[(tt * 2 + mat) * RPM + i];
+          if (mat == 0) {
+            const int krow = (row & ~31) | krow_of_key(row & 31);
+            store_u32x4(dst + krow * D + 8 * k_chunk<CPR>(krow, ch), v);
+          } else {
+            store_u32x4(dst + row * D + 8 * v_chunk<CPR>(row, ch), v);
+          }
+        }
       }
     }
     if (wave < 2) {
@@ -187,9 +209,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   for (int p = 0; p < n_pairs; ++p) {
     const int stage = p & 1;
     const int t = 2 * p + grp;
-    int base, lim;
-    bool is_cache;
-    tile_src(t, base, lim, is_cache);
+    const bool is_cache = t < n_ct;
+    const int base = is_cache ? t * kKT : (t - n_ct) * kKT;
     const bool work = active && t < n_tiles && (is_cache || base <= qb * 32 + 31);
     if (work) {
       const bf16_t* Kt = lds + ((stage * 2 + grp) * 2 + 0) * TILE;

@@ -40,8 +40,8 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
   constexpr int CPR = D / 8;
   constexpr int NCH = kRB * CPR / 256;  // 16-byte chunks per thread per row block
   __shared__ __attribute__((aligned(16))) bf16_t Qs[2][kRB * QLD];
-  __shared__ float s_lse2[2][kRB];
-  __shared__ int s_irow[2][kRB];
+  __shared__ __attribute__((aligned(16))) float s_lse2[2][kRB];
+  __shared__ __attribute__((aligned(16))) int s_irow[2][kRB];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hf = lane >> 5, col = lane & 31;
@@ -79,13 +79,13 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
   const float* lhead = lse + static_cast<size_t>(b * Hq + kvh * G) * S;
 
   // A row block contributes to chunk keys only if one of its queries i >= base.
-  auto block_needed = [&](int blk) {
+  auto block_needed = [&](int blk) __attribute__((always_inline)) {
     if (is_cache) return true;
     const int r0 = blk * kRB, r1 = min(r0 + kRB - 1, n_rows - 1);
     if (r0 / S != r1 / S) return true;
     return (r1 % S) >= base;
   };
-  auto next_needed = [&](int blk) {
+  auto next_needed = [&](int blk) __attribute__((always_inline)) {
     ++blk;
     while (blk < blk_hi && !block_needed(blk)) ++blk;
     return blk;
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
     float l;
     int i;
   };
-  auto load_blk = [&](int blk, Stage& s) {
+  auto load_blk = [&](int blk, Stage& s) __attribute__((always_inline)) {
     const int r0 = blk * kRB;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
       s.i = (r < n_rows) ? r % S : -1;
     }
   };
-  auto store_blk = [&](const Stage& s, int buf) {
+  auto store_blk = [&](const Stage& s, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int idx = c * 256 + tid, row = idx / CPR, dc = idx % CPR;
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
   if (n2 < blk_hi) load_blk(n2, st1);
   __syncthreads();
   int buf = 0;
-  auto iter = [&](Stage& st) {
+  auto iter = [&](Stage& st) __attribute__((always_inline)) {
     if (key0 < lim) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -152,20 +152,27 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
           a0 = mfma32x32x16(qa, kf[0][q], a0);
           a1 = mfma32x32x16(qa, kf[1][q], a1);
         }
-        // accumulator register r of lane l: query row 8(r/4) + 4hf + r%4 of this half block
+        // accumulator register r of lane l: query row 8(r/4) + 4hf + r%4 of this half block;
+        // the 4 rows of each group of 4 registers are consecutive (one 16-byte LDS read)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = half * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const float l2 = s_lse2[buf][row];
-          float p0 = fast_exp2(fmaf(a0[r], c2, -l2));
-          float p1 = fast_exp2(fmaf(a1[r], c2, -l2));
-          if (!is_cache) {
-            const int qi = s_irow[buf][row];
-            p0 = (key0 + col <= qi) ? p0 : 0.f;
-            p1 = (key0 + 32 + col <= qi) ? p1 : 0.f;
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int row0 = half * 32 + 8 * a4 + 4 * hf;
+          const f32x4 l2v = *reinterpret_cast<const f32x4*>(&s_lse2[buf][row0]);
+          int4 qiv = {0, 0, 0, 0};
+          if (!is_cache) qiv = *reinterpret_cast<const int4*>(&s_irow[buf][row0]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * a4 + e;
+            float p0 = fast_exp2(fmaf(a0[r], c2, -l2v[e]));
+            float p1 = fast_exp2(fmaf(a1[r], c2, -l2v[e]));
+            if (!is_cache) {
+              const int qi = e == 0 ? qiv.x : e == 1 ? qiv.y : e == 2 ? qiv.z : qiv.w;
+              p0 = (key0 + col <= qi) ? p0 : 0.f;
+              p1 = (key0 + 32 + col <= qi) ? p1 : 0.f;
+            }
+            cs0 += p0;
+            cs1 += p1;
           }
-          cs0 += p0;
-          cs1 += p1;
         }
       }
     }

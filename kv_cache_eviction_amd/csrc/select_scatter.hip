@@ -32,6 +32,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWavesSel = kThreads / 64;
 constexpr int kPre = 4;        // 16-byte chunks of K and of V each thread prefetches
+constexpr int kMaxSplits = 16; // upper bound of the score kernel's row splits
 
 enum : uint8_t { kFree = 0, kCand = 1, kKeep = 2, kTarget = 4 };
 
@@ -123,13 +124,18 @@ __global__ __launch_bounds__(kThreads) void select_scatter_kernel(
   // 1. scores after this step's mass; slot classes; AND/OR of candidate keys
   int my_free = 0, my_cand = 0;
   uint32_t k_and = 0xffffffffu, k_or = 0u;
-#pragma unroll 4
+#pragma unroll 2
   for (int m = tid; m < M; m += kThreads) {
     const int p = pos_h[m];
     float s = sc_h[m];
+    // all R partials in flight at once: unconditional loads from valid rows
+    float part[kMaxSplits];
+#pragma unroll
+    for (int r = 0; r < kMaxSplits; ++r) part[r] = ph[static_cast<size_t>(min(r, R - 1)) * PS + m];
     float ds = 0.f;
-    if (m < n_cache)
-      for (int r = 0; r < R; ++r) ds += ph[static_cast<size_t>(r) * PS + m];
+#pragma unroll
+    for (int r = 0; r < kMaxSplits; ++r) ds += (r < R) ? part[r] : 0.f;
+    if (m >= n_cache) ds = 0.f;
     uint8_t fl = kFree;
     if (p >= 0) {
       s += ds;
@@ -154,12 +160,10 @@ __global__ __launch_bounds__(kThreads) void select_scatter_kernel(
   u32x4 kr[kPre], vr[kPre];
 #pragma unroll
   for (int i = 0; i < kPre; ++i) {
-    const int idx = tid + i * kThreads;
-    if (idx < n_chunks) {
-      const size_t src = static_cast<size_t>(bh) * S * row_bytes + 16 * static_cast<size_t>(idx);
-      kr[i] = load_u32x4(kn + src);
-      vr[i] = load_u32x4(vn + src);
-    }
+    const int idx = min(tid + i * kThreads, n_chunks - 1);    // clamped: loads stay unconditional
+    const size_t src = static_cast<size_t>(bh) * S * row_bytes + 16 * static_cast<size_t>(idx);
+    kr[i] = load_u32x4(kn + src);
+    vr[i] = load_u32x4(vn + src);
   }
   int n_free, n_cand;
   block_excl_scan(my_free, s_tmp, n_free);
@@ -252,8 +256,12 @@ __global__ __launch_bounds__(kThreads) void select_scatter_kernel(
   // 4. targets: score = mass from the chunk's own queries, position T + j
   for (int jj = tid; jj < S; jj += kThreads) {
     const int slot = s_R[jj];
+    float part[kMaxSplits];
+#pragma unroll
+    for (int r = 0; r < kMaxSplits; ++r) part[r] = ph[static_cast<size_t>(min(r, R - 1)) * PS + M + jj];
     float mu = 0.f;
-    for (int r = 0; r < R; ++r) mu += ph[static_cast<size_t>(r) * PS + M + jj];
+#pragma unroll
+    for (int r = 0; r < kMaxSplits; ++r) mu += (r < R) ? part[r] : 0.f;
     sc_h[slot] = mu;
     pos_h[slot] = T + jj;
     if (slots_out) slots_out[static_cast<size_t>(bh) * S + jj] = slot;
@@ -283,12 +291,10 @@ __global__ __launch_bounds__(kThreads) void select_scatter_kernel(
   for (int base = kPre * kThreads; base < n_chunks; base += kPre * kThreads) {
 #pragma unroll
     for (int i = 0; i < kPre; ++i) {
-      const int idx = base + tid + i * kThreads;
-      if (idx < n_chunks) {
-        const size_t src = static_cast<size_t>(bh) * S * row_bytes + 16 * static_cast<size_t>(idx);
-        kr[i] = load_u32x4(kn + src);
-        vr[i] = load_u32x4(vn + src);
-      }
+      const int idx = min(base + tid + i * kThreads, n_chunks - 1);
+      const size_t src = static_cast<size_t>(bh) * S * row_bytes + 16 * static_cast<size_t>(idx);
+      kr[i] = load_u32x4(kn + src);
+      vr[i] = load_u32x4(vn + src);
     }
 #pragma unroll
     for (int i = 0; i < kPre; ++i) {
