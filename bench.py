@@ -154,7 +154,7 @@ def main():
 
     # per-kernel times from the library's HIP events (same stream, same timed region)
     ktime = {}
-    for name in ("attn_fwd", "score", "select_scatter", "reset"):
+    for name in ("attn_fwd", "score", "select", "scatter", "reset"):
         tot, n = 0.0, 0
         for hd in timing_handles:
             ms, cnt = h2o.h2o_get_timing(hd, name)

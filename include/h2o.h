@@ -185,7 +185,7 @@ H2O_API h2o_status h2o_device_status(h2o_cache* c, void* stream, int32_t* flags)
 
 /* Per-kernel timing with HIP events recorded on the launch stream around
  * every kernel launch while enabled.  Kernel ids: 0 attention forward,
- * 1 score accumulation, 2 eviction select + scatter, 3 state reset.
+ * 1 score accumulation, 2 eviction select, 3 state reset, 4 K/V scatter.
  * h2o_get_timing synchronises on the last recorded event and returns the
  * summed milliseconds and launch count since timing was enabled. */
 H2O_API h2o_status h2o_set_timing(h2o_cache* c, int32_t enable);

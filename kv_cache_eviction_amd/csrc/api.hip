@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kTimedKernels = 4;
+constexpr int kTimedKernels = 5;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -21,6 +21,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   size_t partial_off, partial_bytes;
   size_t lse_off, lse_bytes;
+  size_t targets_off, targets_bytes;     // target slot list of the current step
   size_t counters_off, counters_bytes;   // the device status word
   size_t n_counters;                     // ints cleared at init
   size_t total;
@@ -36,7 +37,9 @@ Layout layout_of(const h2o_config* c) {
   L.partial_bytes = align_up(heads * h2o::score_row_splits_max() * (c->cache_slots + smax) * sizeof(float));
   L.lse_off = L.partial_off + L.partial_bytes;
   L.lse_bytes = align_up(static_cast<size_t>(c->batch) * c->n_q_heads * smax * sizeof(float));
-  L.counters_off = L.lse_off + L.lse_bytes;
+  L.targets_off = L.lse_off + L.lse_bytes;
+  L.targets_bytes = align_up(heads * smax * sizeof(int32_t));
+  L.counters_off = L.targets_off + L.targets_bytes;
   L.n_counters = 1;
   L.counters_bytes = align_up(L.n_counters * sizeof(int32_t));
   L.total = L.counters_off + L.counters_bytes;
@@ -141,9 +144,12 @@ h2o_status run_step(h2o_cache* c, const void* q, const void* k, const void* v, i
   h2o::ScoreArgs sa{q, c->k_cache, k, lse_buf, partial, R};
   r = timed(c, 1, st, [&] { return h2o::launch_score(sh, sa, dtype, st); });
   if (r != H2O_OK) return r;
-  h2o::SelectArgs xa{c->k_cache, c->v_cache, c->scores, c->pos, k, v, partial, R,
+  int32_t* targets = reinterpret_cast<int32_t*>(c->ws + c->lay.targets_off);
+  h2o::SelectArgs xa{c->k_cache, c->v_cache, c->scores, c->pos, k, v, partial, R, targets,
                      slots_out, step_mass, k_old, v_old, status, static_cast<int32_t>(c->T)};
-  r = timed(c, 2, st, [&] { return h2o::launch_select_scatter(sh, xa, dtype, st); });
+  r = timed(c, 2, st, [&] { return h2o::launch_select(sh, xa, st); });
+  if (r != H2O_OK) return r;
+  r = timed(c, 4, st, [&] { return h2o::launch_scatter(sh, xa, dtype, st); });
   if (r != H2O_OK) return r;
   c->T += s;
   if (c->filled >= 0) c->filled = c->filled + s > c->cfg.cache_slots ? c->cfg.cache_slots : c->filled + s;

@@ -43,6 +43,7 @@ struct SelectArgs {
   const void* v_new;
   const float* partial;   // [B*Hkv][R][M + S]: per-split masses of cache slots, then chunk keys
   int R;
+  int32_t* targets;     // [B*Hkv][S] workspace: target slot of row j (flagged if it was free)
   int32_t* slots_out;   // nullable
   float* step_mass;     // nullable
   void* k_old;          // nullable
@@ -55,7 +56,8 @@ enum Dtype { kBF16 = 0, kFP32 = 1 };
 
 hipError_t launch_attn_fwd(const StepShape& sh, const AttnArgs& a, int dtype, hipStream_t st);
 hipError_t launch_score(const StepShape& sh, const ScoreArgs& a, int dtype, hipStream_t st);
-hipError_t launch_select_scatter(const StepShape& sh, const SelectArgs& a, int dtype, hipStream_t st);
+hipError_t launch_select(const StepShape& sh, const SelectArgs& a, hipStream_t st);
+hipError_t launch_scatter(const StepShape& sh, const SelectArgs& a, int dtype, hipStream_t st);
 hipError_t launch_reset(float* scores, int32_t* pos, int64_t n_slots, int32_t* counters,
                         int64_t n_counters, hipStream_t st);
 

@@ -11,9 +11,9 @@
 // smallest (score, slot index); chunk token j goes to the j-th smallest
 // target slot.
 //
-// One 1024-thread workgroup owns one (b, KV head): no other workgroup reads
-// or writes that head's scores, positions or slots, so the kernel needs no
-// inter-workgroup synchronisation.  It
+// Two kernels.  The select kernel runs one 1024-thread workgroup per
+// (b, KV head): no other workgroup reads or writes that head's scores,
+// positions or slots, so it needs no inter-workgroup synchronisation.  It
 //   1. adds the score kernel's R per-split masses to the filled slots'
 //      scores (fixed split order: deterministic);
 //   2. selects the targets: scores map to order-preserving 32-bit keys, the
@@ -21,8 +21,10 @@
 //      skipped, and 8-bit LDS radix passes over the remaining bits find the
 //      n_e-th smallest key; equal keys resolve to the lowest slot through an
 //      exclusive scan in slot order;
-//   3. writes scores and positions, then copies the chunk's K/V rows into
-//      their slots (the first rows' loads were issued before the selection).
+//   3. writes scores, positions and the target list R (with a flag for
+//      targets that were free).
+// The scatter kernel then copies the chunk's K/V rows into their slots with
+// many workgroups per head (a pure bandwidth copy, 16-byte accesses).
 #include "h2o_device.h"
 #include "h2o_launch.h"
 
@@ -35,6 +37,7 @@ constexpr int kPre = 4;        // 16-byte chunks of K and of V each thread prefe
 constexpr int kMaxSplits = 16; // upper bound of the score kernel's row splits
 
 enum : uint8_t { kFree = 0, kCand = 1, kKeep = 2, kTarget = 4 };
+constexpr int32_t kWasFree = 0x40000000;   // flag bit of a target-list entry
 
 // Order-preserving key of a float: unsigned comparison of keys matches the
 // numeric order (scores are non-negative by construction; adopted states may
@@ -99,12 +102,11 @@ __device__ void block_and_or(uint32_t v_and, uint32_t v_or, uint32_t* utmp, uint
   }
 }
 
-__global__ __launch_bounds__(kThreads) void select_scatter_kernel(
-    char* __restrict__ kc, char* __restrict__ vc, float* __restrict__ scores,
-    int32_t* __restrict__ pos, const char* __restrict__ kn, const char* __restrict__ vn,
-    const float* __restrict__ partial, int R, int32_t* __restrict__ slots_out,
-    float* __restrict__ step_mass, char* __restrict__ k_old, char* __restrict__ v_old,
-    int32_t* __restrict__ status, int T, int W, int S, int M, int n_cache, int row_bytes) {
+__global__ __launch_bounds__(kThreads) void select_kernel(
+    float* __restrict__ scores, int32_t* __restrict__ pos, const float* __restrict__ partial,
+    int R, int32_t* __restrict__ targets, int32_t* __restrict__ slots_out,
+    float* __restrict__ step_mass, int32_t* __restrict__ status, int T, int W, int S, int M,
+    int n_cache) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   uint32_t* s_key = reinterpret_cast<uint32_t*>(smem);                        // [M]
   int* s_R = reinterpret_cast<int*>(smem + 4 * static_cast<size_t>(M));      // [S]
@@ -154,17 +156,6 @@ __global__ __launch_bounds__(kThreads) void select_scatter_kernel(
       k_or |= key;
     }
   }
-  // prefetch the first chunk rows while the selection runs
-  const int cpr = row_bytes / 16;
-  const int n_chunks = S * cpr;
-  u32x4 kr[kPre], vr[kPre];
-#pragma unroll
-  for (int i = 0; i < kPre; ++i) {
-    const int idx = min(tid + i * kThreads, n_chunks - 1);    // clamped: loads stay unconditional
-    const size_t src = static_cast<size_t>(bh) * S * row_bytes + 16 * static_cast<size_t>(idx);
-    kr[i] = load_u32x4(kn + src);
-    vr[i] = load_u32x4(vn + src);
-  }
   int n_free, n_cand;
   block_excl_scan(my_free, s_tmp, n_free);
   block_excl_scan(my_cand, s_tmp, n_cand);
@@ -173,6 +164,7 @@ __global__ __launch_bounds__(kThreads) void select_scatter_kernel(
   if (n_cand < n_e) {                      // infeasible adopted state: no slot is written
     for (int m = tid; m < M; m += kThreads)
       if (s_fl[m] != kFree) sc_h[m] = key_value(s_key[m]);
+    for (int jj = tid; jj < S; jj += kThreads) targets[static_cast<size_t>(bh) * S + jj] = -1;
     if (tid == 0) atomicOr(status, 1);
     return;
   }
@@ -264,43 +256,42 @@ __global__ __launch_bounds__(kThreads) void select_scatter_kernel(
     for (int r = 0; r < kMaxSplits; ++r) mu += (r < R) ? part[r] : 0.f;
     sc_h[slot] = mu;
     pos_h[slot] = T + jj;
+    const bool was_free = (s_fl[slot] & 3) == kFree;
+    targets[static_cast<size_t>(bh) * S + jj] = was_free ? (slot | kWasFree) : slot;
     if (slots_out) slots_out[static_cast<size_t>(bh) * S + jj] = slot;
     if (step_mass) step_mass[static_cast<size_t>(bh) * PS + M + jj] = mu;
   }
+}
 
-  // 5. copy the chunk's K/V rows into their slots (old rows to the delta)
-  auto put = [&](int idx, const u32x4& kv, const u32x4& vv) {
-    const int jj = idx / cpr, c = idx - jj * cpr;
-    const int slot = s_R[jj];
+// Copies chunk row j of every (b, KV head) into its target slot; the rows of
+// a head are spread over `parts` workgroups.  With k_old/v_old, the row a
+// target held before is saved first (zeros for a slot that was free).
+__global__ __launch_bounds__(256) void scatter_kernel(
+    char* __restrict__ kc, char* __restrict__ vc, const char* __restrict__ kn,
+    const char* __restrict__ vn, const int32_t* __restrict__ targets, char* __restrict__ k_old,
+    char* __restrict__ v_old, int S, int M, int row_bytes, int n_heads, int rows_per) {
+  const int bh = blockIdx.x % n_heads;
+  const int part = static_cast<int>(blockIdx.x) / n_heads;
+  const int cpr = row_bytes / 16;
+  const int j0 = part * rows_per, j1 = min(S, j0 + rows_per);
+  const int n = (j1 - j0) * cpr;
+  for (int idx = threadIdx.x; idx < n; idx += blockDim.x) {
+    const int jj = j0 + idx / cpr, c = idx % cpr;
+    const int t = targets[static_cast<size_t>(bh) * S + jj];
+    if (t < 0) continue;                          // infeasible head: nothing is written
+    const int slot = t & ~kWasFree;
     const size_t src = (static_cast<size_t>(bh) * S + jj) * row_bytes + 16 * c;
     const size_t dst = (static_cast<size_t>(bh) * M + slot) * row_bytes + 16 * c;
+    const u32x4 kv = load_u32x4(kn + src);
+    const u32x4 vv = load_u32x4(vn + src);
     if (k_old) {
-      const bool was_free = (s_fl[slot] & 3) == kFree;
       const u32x4 z = {0, 0, 0, 0};
+      const bool was_free = (t & kWasFree) != 0;
       store_u32x4(k_old + src, was_free ? z : load_u32x4(kc + dst));
       store_u32x4(v_old + src, was_free ? z : load_u32x4(vc + dst));
     }
     store_u32x4(kc + dst, kv);
     store_u32x4(vc + dst, vv);
-  };
-#pragma unroll
-  for (int i = 0; i < kPre; ++i) {
-    const int idx = tid + i * kThreads;
-    if (idx < n_chunks) put(idx, kr[i], vr[i]);
-  }
-  for (int base = kPre * kThreads; base < n_chunks; base += kPre * kThreads) {
-#pragma unroll
-    for (int i = 0; i < kPre; ++i) {
-      const int idx = min(base + tid + i * kThreads, n_chunks - 1);
-      const size_t src = static_cast<size_t>(bh) * S * row_bytes + 16 * static_cast<size_t>(idx);
-      kr[i] = load_u32x4(kn + src);
-      vr[i] = load_u32x4(vn + src);
-    }
-#pragma unroll
-    for (int i = 0; i < kPre; ++i) {
-      const int idx = base + tid + i * kThreads;
-      if (idx < n_chunks) put(idx, kr[i], vr[i]);
-    }
   }
 }
 
@@ -320,21 +311,32 @@ size_t select_lds_bytes(int M, int S) {
   return 4 * static_cast<size_t>(M) + 4 * static_cast<size_t>(S) + static_cast<size_t>(M) + 16;
 }
 
-hipError_t launch_select_scatter(const StepShape& sh, const SelectArgs& a, int dtype, hipStream_t st) {
+hipError_t launch_select(const StepShape& sh, const SelectArgs& a, hipStream_t st) {
   const int n_heads = sh.B * sh.Hkv;
-  const int row_bytes = sh.D * (dtype == kBF16 ? 2 : 4);
   const size_t lds = select_lds_bytes(sh.M, sh.S);
   if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_scatter_kernel),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(select_scatter_kernel, dim3(n_heads), dim3(kThreads), lds, st,
-                     static_cast<char*>(a.k_cache), static_cast<char*>(a.v_cache), a.scores, a.pos,
-                     static_cast<const char*>(a.k_new), static_cast<const char*>(a.v_new), a.partial,
-                     a.R, a.slots_out, a.step_mass, static_cast<char*>(a.k_old),
-                     static_cast<char*>(a.v_old), a.status, a.T, sh.W, sh.S, sh.M, sh.n_cache,
-                     row_bytes);
+  hipLaunchKernelGGL(select_kernel, dim3(n_heads), dim3(kThreads), lds, st, a.scores, a.pos,
+                     a.partial, a.R, a.targets, a.slots_out, a.step_mass, a.status, a.T, sh.W, sh.S,
+                     sh.M, sh.n_cache);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(const StepShape& sh, const SelectArgs& a, int dtype, hipStream_t st) {
+  const int n_heads = sh.B * sh.Hkv;
+  const int row_bytes = sh.D * (dtype == kBF16 ? 2 : 4);
+  // about 512 workgroups of 32 rows or more
+  int rows_per = (sh.S * n_heads + 511) / 512;
+  rows_per = rows_per < 16 ? 16 : rows_per;
+  const int parts = (sh.S + rows_per - 1) / rows_per;
+  hipLaunchKernelGGL(scatter_kernel, dim3(n_heads * parts), dim3(256), 0, st,
+                     static_cast<char*>(a.k_cache), static_cast<char*>(a.v_cache),
+                     static_cast<const char*>(a.k_new), static_cast<const char*>(a.v_new), a.targets,
+                     static_cast<char*>(a.k_old), static_cast<char*>(a.v_old), sh.S, sh.M, row_bytes,
+                     n_heads, rows_per);
   return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libh2o.so"
 H2O_OK, H2O_ERR_NULL, H2O_ERR_CONFIG, H2O_ERR_SHAPE, H2O_ERR_STATE = 0, 1, 2, 3, 4
 H2O_ERR_WORKSPACE, H2O_ERR_HIP, H2O_ERR_UNSUPPORTED = 5, 6, 7
 H2O_BF16, H2O_FP32 = 0, 1
-KERNEL_IDS = {"attn_fwd": 0, "score": 1, "select_scatter": 2, "reset": 3}
+KERNEL_IDS = {"attn_fwd": 0, "score": 1, "select": 2, "reset": 3, "scatter": 4}
 
 EXPORTED = [
     "h2o_validate_config", "h2o_workspace_bytes", "h2o_cache_init", "h2o_prefill",
