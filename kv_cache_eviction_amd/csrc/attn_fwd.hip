@@ -10,15 +10,13 @@
 // describe no kernel; the design below is this library's own, for CDNA4.
 //
 // bf16 path (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
-//   * A workgroup is 4 waves, one per SIMD.  Wave w owns one row block = 32
-//     consecutive queries of one query head; row blocks are numbered
-//     (query block, head in group), so the 4 row blocks of a workgroup share
-//     their query range, causal extent and K/V tiles.
-//   * Every wave runs two independent online-softmax chains, one over the
-//     even and one over the odd 64-key tiles, merged at the end.  Both chains
-//     sit in one instruction stream, so the MFMAs of one chain overlap the
-//     softmax arithmetic of the other without the waves of a SIMD having to
-//     fall out of step.
+//   * A workgroup is 8 waves in two groups of 4.  Wave w of a group owns one
+//     row block = 32 consecutive queries of one query head; row blocks are
+//     numbered (query block, head in group), so the 4 row blocks of a
+//     workgroup share their query range, causal extent and K/V tiles.  The
+//     two groups split the 64-key tiles between them (even / odd tiles) and
+//     merge their softmax states through LDS at the end; with two waves per
+//     SIMD, one wave's softmax arithmetic overlaps the other's MFMAs.
 //   * The kernel computes S^T = K Q^T: K is the A operand read from LDS, the
 //     wave's 32 queries are the B operand held in registers for the whole
 //     kernel.  Each lane then owns one query column, so the row softmax
@@ -35,15 +33,10 @@
 //     chunks) hit distinct banks.
 //   * Online softmax in the log2 domain (exp2 on v_exp_f32); the O rescale
 //     is skipped when no lane's running maximum moved.
-//   * Tile pairs go from global memory straight into a double-buffered LDS
-//     ring with the gfx950 direct-to-LDS load (global_load_lds_dwordx4: lane
-//     i of a wave writes bytes 16i..16i+15 of a 1 KB block); each lane picks
-//     the source chunk that belongs at its LDS position, so the swizzled
-//     layout costs nothing.  The next pair is requested before the current
-//     pair is computed, and one wait + barrier per pair separates stages.
-//     Rows past the end of a tile are clamped to a valid row and masked.
-//   * Which cache slots hold a token (position >= 0) is read once per
-//     workgroup into a bit mask in LDS.
+//   * Tiles pass through registers into a double-buffered LDS ring: the
+//     loads of the next pair of tiles are issued before the current pair is
+//     computed, and one barrier per pair separates the stages.  Loads are
+//     unconditional: rows past the end of a tile read its last row (masked).
 //   * blockIdx -> (head, row group) keeps every workgroup of one (b, KV head)
 //     on one XCD when B*Hkv is a multiple of 8 (dispatch is round-robin over
 //     the 8 XCDs), so that head's K/V stays in that XCD's L2; the row groups
@@ -58,7 +51,7 @@ namespace {
 
 constexpr int kKT = 64;        // keys per LDS tile
 constexpr int kRowBlocks = 4;  // row blocks (32 queries of one head) per workgroup
-constexpr int kFwdThreads = 256;
+constexpr int kFwdThreads = 512;
 
 // Key k (0..31) of a 32-key block -> LDS row = MFMA A-operand row that reads
 // it.  Row 8q + 4h + r holds key 16h + 4q + r, so that accumulator register
@@ -75,108 +68,6 @@ __device__ __forceinline__ int v_chunk(int row, int c) {
   return c ^ ((row & 3) << (CPR == 16 ? 2 : 1));
 }
 
-// One online-softmax chain of a wave: running max (log2 domain), the lane's
-// partial row sum and the O^T accumulators.
-template <int DB>
-struct Chain {
-  f32x16 o[DB];
-  float m, l;
-};
-
-// Scores S^T (64 keys x 32 queries) of one tile: accumulator register r of
-// lane l holds key kb*32 + 16(l/32) + r against query l%32.
-template <int D>
-__device__ __forceinline__ void tile_scores(const bf16_t* Kt, const bf16x8 (&qf)[D / 16], int col,
-                                            int hf, f32x16& s0, f32x16& s1) {
-  constexpr int CPR = D / 8;
-  s0 = zero16();
-  s1 = zero16();
-#pragma unroll
-  for (int st = 0; st < D / 16; ++st) {
-    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(Kt + col * D + 8 * k_chunk<CPR>(col, 2 * st + hf));
-    const bf16x8 a1 =
-        *reinterpret_cast<const bf16x8*>(Kt + (32 + col) * D + 8 * k_chunk<CPR>(32 + col, 2 * st + hf));
-    s0 = mfma32x32x16(a0, qf[st], s0);
-    s1 = mfma32x32x16(a1, qf[st], s1);
-  }
-}
-
-// Masks (validity bits of the tile, causal bound), online-softmax update of
-// the chain and conversion of the probabilities to the PV B operands.
-template <int DB>
-__device__ __forceinline__ void tile_softmax(f32x16& s0, f32x16& s1, Chain<DB>& ch, uint64_t vm,
-                                             bool causal, int lim_i, int hf, float c2,
-                                             bf16x8 (&pb)[4]) {
-  if (vm != ~0ull || causal) {
-    const uint32_t bits0 = static_cast<uint32_t>(vm >> (16 * hf)) & 0xffffu;
-    const uint32_t bits1 = static_cast<uint32_t>(vm >> (32 + 16 * hf)) & 0xffffu;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const bool ok0 = ((bits0 >> r) & 1u) && (r <= lim_i);
-      const bool ok1 = ((bits1 >> r) & 1u) && (32 + r <= lim_i);
-      s0[r] = ok0 ? s0[r] : kNegInf;
-      s1[r] = ok1 ? s1[r] : kNegInf;
-    }
-  }
-  float mx = kNegInf;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-  mx = fmaxf(mx, xor32(mx));
-  const float m_new = fmaxf(ch.m, mx * c2);
-  const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-  const float alpha = fast_exp2(ch.m - m_use);
-  float rs = 0.f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    s0[r] = fast_exp2(fmaf(s0[r], c2, -m_use));
-    s1[r] = fast_exp2(fmaf(s1[r], c2, -m_use));
-    rs += s0[r] + s1[r];
-  }
-  ch.l = fmaf(ch.l, alpha, rs);
-  ch.m = m_new;
-  if (__ballot(alpha != 1.f)) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ch.o[db][r] *= alpha;
-  }
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    f32x8 v0, v1;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      v0[e] = s0[8 * u + e];
-      v1[e] = s1[8 * u + e];
-    }
-    pb[u] = to_bf16x8(v0);
-    pb[2 + u] = to_bf16x8(v1);
-  }
-}
-
-// O^T += V^T P^T for one tile.  MFMA (kb,u) covers keys 32kb + 16(l/32) +
-// 8u + e; its A operand comes from two transpose reads in which lane
-// j = 4r + q of a 16-lane group addresses V[key0 + r][d0 + 4q .. +4).
-template <int D>
-__device__ __forceinline__ void tile_pv(const bf16_t* Vt, const bf16x8 (&pb)[4], f32x16 (&o)[D / 32],
-                                        int hf, int tr_r, int tr_q, int tr_dg) {
-  constexpr int CPR = D / 8;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int d = db * 32 + tr_dg * 16 + 4 * tr_q;
-        const int key0 = kb * 32 + 16 * hf + 8 * u + tr_r;
-        const bf16x4 h0 = lds_read_tr16(Vt + key0 * D + 8 * v_chunk<CPR>(key0, d >> 3) + (d & 7));
-        const bf16x4 h1 = lds_read_tr16(Vt + (key0 + 4) * D + 8 * v_chunk<CPR>(key0 + 4, d >> 3) + (d & 7));
-        const bf16x8 a = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = mfma32x32x16(a, pb[2 * kb + u], o[db]);
-      }
-    }
-  }
-}
-
 template <int D>
 __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc,
@@ -188,18 +79,20 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   constexpr int DB = D / 32;              // 32-row blocks of O^T
   constexpr int CPR = D / 8;              // 16-byte chunks per row
   constexpr int TILE = kKT * D;           // elements per K or V tile
-  // [stage][tile of the pair][K,V][TILE]
+  constexpr int NCH = 2 * 2 * kKT * CPR / kFwdThreads;   // chunks per thread per tile pair
+  // [stage][group][K,V][TILE]
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * 2 * 2 * TILE];
-  __shared__ uint64_t s_vbits[16384 / kKT];
+  __shared__ uint64_t s_valid[2][2];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, col = lane & 31;
+  const int grp = wave >> 2, rbw = wave & 3;
   const int bh = blockIdx.x % n_heads;
   const int wgi = wg_per_head - 1 - static_cast<int>(blockIdx.x) / n_heads;
   const int b = bh / Hkv, kvh = bh - b * Hkv;
   const int G = Hq / Hkv;
   const int n_rb = G * ((S + 31) >> 5);
-  const int rb = wgi * kRowBlocks + wave;
+  const int rb = wgi * kRowBlocks + rbw;
   const bool active = rb < n_rb;
   const int g = active ? rb % G : 0;
   const int qb = active ? rb / G : 0;
@@ -228,126 +121,211 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
       qf[st] = qok ? v : bf16x8{};
     }
   }
-  Chain<DB> ch0, ch1;
+  f32x16 o[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    ch0.o[db] = zero16();
-    ch1.o[db] = zero16();
-  }
-  ch0.m = ch1.m = kNegInf;
-  ch0.l = ch1.l = 0.f;
+  for (int db = 0; db < DB; ++db) o[db] = zero16();
+  float m_run = kNegInf, l_run = 0.f;
 
-  // ---- validity of the cache slots: one 64-bit mask per cache tile
-  for (int t = wave; t < n_ct; t += kRowBlocks) {
-    const int key = t * kKT + lane;
-    const int pv = pos_head[min(key, M - 1)];
-    const uint64_t m = __ballot(key < n_cache && pv >= 0);
-    if (lane == 0) s_vbits[t] = m;
-  }
-
-  // ---- staging: tile pair p = tiles (2p, 2p+1).  Wave w fills matrix
-  // (w & 1 ? V : K) of tile 2p + (w >> 1): its instruction j writes LDS rows
-  // RPI*j .. RPI*j + RPI-1 of that matrix (1 KB), lane i landing on row
-  // RPI*j + i/CPR, physical chunk i%CPR.  The lane loads the logical chunk and
-  // key that belong there.  Rows past the tile's end read its last row; a
-  // tile past the last one reads chunk row 0 (never used).
-  constexpr int RPI = 64 / CPR;                       // rows per 1 KB instruction
-  const int dma_mat = wave & 1, dma_tt = wave >> 1;
-  const int dma_row_in = lane / CPR, dma_pc = lane % CPR;
-  const bf16_t* dma_cache = dma_mat ? vc_head : kc_head;
-  const bf16_t* dma_new = dma_mat ? vn_head : kn_head;
-  auto load_pair = [&](int p) __attribute__((always_inline)) {
-    const int t = 2 * p + dma_tt;
+  // ---- staging: tile pair p = tiles (2p, 2p+1).  Chunk r of a thread is
+  // c = tid + 512 r; its tile (tt), matrix (K or V) and row follow from r at
+  // compile time, so every source pointer is a uniform per-tile value.
+  struct TileSrc {
+    const bf16_t* k;
+    const bf16_t* v;
+    int n;            // rows of the tile that exist (keys < lim)
+  };
+  auto tile_src = [&](int t) __attribute__((always_inline)) {
+    TileSrc r;
     const bool is_cache = t < n_ct;
     const bool exists = t < n_tiles;
     const int base = is_cache ? t * kKT : (t - n_ct) * kKT;
-    const int n = exists ? (is_cache ? n_cache : S) - base : 1;
-    const bf16_t* src = ((exists && is_cache) ? dma_cache : dma_new) + (exists ? static_cast<size_t>(base) * D : 0);
-    bf16_t* dst = lds + (((p & 1) * 2 + dma_tt) * 2 + dma_mat) * TILE;
+    const size_t off = exists ? static_cast<size_t>(base) * D : 0;
+    r.k = ((exists && is_cache) ? kc_head : kn_head) + off;
+    r.v = ((exists && is_cache) ? vc_head : vn_head) + off;
+    r.n = exists ? (is_cache ? n_cache : S) - base : 1;   // a tile past the end reads chunk row 0
+    return r;
+  };
+  constexpr int RPT = NCH / 2;                  // chunks per thread per tile
+  constexpr int RPM = RPT / 2;                  // chunks per thread per matrix of a tile
+  const int ch = tid % CPR;                     // 16-byte chunk within the row
+  const int row0 = tid / CPR;                   // first row; chunk r adds (r % RPM) * (512 / CPR)
+  u32x4 reg[NCH];
+  int preg = -1;
+  auto load_pair = [&](int p) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < CPR; ++j) {
-      const int row = RPI * j + dma_row_in;
-      int key, c;
-      if (dma_mat == 0) {
-        key = (row & ~31) | (16 * ((row >> 2) & 1) + 4 * ((row & 31) >> 3) + (row & 3));
-        c = k_chunk<CPR>(row, dma_pc);
-      } else {
-        key = row;
-        c = v_chunk<CPR>(row, dma_pc);
+    for (int tt = 0; tt < 2; ++tt) {
+      const TileSrc ts = tile_src(2 * p + tt);
+#pragma unroll
+      for (int mat = 0; mat < 2; ++mat) {
+#pragma unroll
+        for (int i = 0; i < RPM; ++i) {
+          const int row = row0 + i * (kFwdThreads / CPR);
+          // rows past the end of a tile read its last row (masked later): no branches
+          const bf16_t* src = (mat ? ts.v : ts.k) + min(row, ts.n - 1) * D + ch * 8;
+          reg[(tt * 2 + mat) * RPM + i] = load_u32x4(src);
+        }
       }
-      key = min(key, n - 1);
-      __builtin_amdgcn_global_load_lds(src + key * D + c * 8, dst + j * (RPI * D), 16, 0, 0);
+    }
+    if (wave < 2) {                       // wave tt fetches the positions of tile 2p+tt
+      const int t = 2 * p + wave;
+      const bool is_cache = t < n_ct;
+      const int base = is_cache ? t * kKT : (t - n_ct) * kKT;
+      const int lim = t < n_tiles ? (is_cache ? n_cache : S) : base;
+      const int key = base + lane;
+      const int pv = pos_head[is_cache ? min(key, M - 1) : 0];
+      preg = key < lim ? (is_cache ? pv : 0) : -1;
     }
   };
-  auto wait_pair = [&]() __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(0x0f70);               // vmcnt(0): this wave's copies landed
-    __syncthreads();                                  // ... and every other wave's
+  auto store_pair = [&](int stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int mat = 0; mat < 2; ++mat) {
+        bf16_t* dst = lds + ((stage * 2 + tt) * 2 + mat) * TILE;
+#pragma unroll
+        for (int i = 0; i < RPM; ++i) {
+          const int row = row0 + i * (kFwdThreads / CPR);
+          const u32x4 v = reg[(tt * 2 + mat) * RPM + i];
+          if (mat == 0) {
+            const int krow = (row & ~31) | krow_of_key(row & 31);
+            store_u32x4(dst + krow * D + 8 * k_chunk<CPR>(krow, ch), v);
+          } else {
+            store_u32x4(dst + row * D + 8 * v_chunk<CPR>(row, ch), v);
+          }
+        }
+      }
+    }
+    if (wave < 2) {
+      const uint64_t m = __ballot(preg >= 0);
+      if (lane == 0) s_valid[stage][wave] = m;
+    }
   };
 
+  // per-lane parts of the transpose-read addresses (see the V^T operand below)
   const int tr_j = lane & 15, tr_r = tr_j >> 2, tr_q = tr_j & 3, tr_dg = (lane >> 4) & 1;
 
-  struct TileInfo {
-    int base;
-    bool work, causal;
-    uint64_t vmask;
-  };
-  auto tile_info = [&](int t) __attribute__((always_inline)) {
-    TileInfo i;
-    const bool is_cache = t < n_ct;
-    i.base = is_cache ? t * kKT : (t - n_ct) * kKT;
-    i.work = active && t < n_tiles && (is_cache || i.base <= qb * 32 + 31);
-    i.causal = !is_cache && (i.base + kKT - 1 > qb * 32);
-    const int nk = S - i.base;
-    i.vmask = is_cache ? s_vbits[min(t, n_ct - 1)]
-                       : (nk >= 64 ? ~0ull : ((1ull << (nk > 0 ? nk : 0)) - 1ull));
-    return i;
-  };
-
-  if (n_pairs > 0) load_pair(0);
-  wait_pair();
+  if (n_pairs > 0) {
+    load_pair(0);
+    store_pair(0);
+    if (n_pairs > 1) load_pair(1);
+  }
+  __syncthreads();
   for (int p = 0; p < n_pairs; ++p) {
     const int stage = p & 1;
-    if (p + 1 < n_pairs) load_pair(p + 1);          // into the stage computed last iteration
-    // tiles 2p (chain 0) and 2p+1 (chain 1); skip tiles past the end or past
-    // this wave's causal extent
-    const TileInfo i0 = tile_info(2 * p), i1 = tile_info(2 * p + 1);
-    const bf16_t* K0 = lds + ((stage * 2 + 0) * 2 + 0) * TILE;
-    const bf16_t* V0 = lds + ((stage * 2 + 0) * 2 + 1) * TILE;
-    const bf16_t* K1 = lds + ((stage * 2 + 1) * 2 + 0) * TILE;
-    const bf16_t* V1 = lds + ((stage * 2 + 1) * 2 + 1) * TILE;
-    if (i0.work && i1.work) {
-      // both chains: interleavable MFMA / VALU streams
-      f32x16 a0, a1, b0, b1;
-      bf16x8 pa[4], pbb[4];
-      tile_scores<D>(K0, qf, col, hf, a0, a1);
-      tile_scores<D>(K1, qf, col, hf, b0, b1);
-      tile_softmax<DB>(a0, a1, ch0, i0.vmask, i0.causal, qi - i0.base - 16 * hf, hf, c2, pa);
-      tile_softmax<DB>(b0, b1, ch1, i1.vmask, i1.causal, qi - i1.base - 16 * hf, hf, c2, pbb);
-      tile_pv<D>(V0, pa, ch0.o, hf, tr_r, tr_q, tr_dg);
-      tile_pv<D>(V1, pbb, ch1.o, hf, tr_r, tr_q, tr_dg);
-    } else if (i0.work) {
-      f32x16 a0, a1;
-      bf16x8 pa[4];
-      tile_scores<D>(K0, qf, col, hf, a0, a1);
-      tile_softmax<DB>(a0, a1, ch0, i0.vmask, i0.causal, qi - i0.base - 16 * hf, hf, c2, pa);
-      tile_pv<D>(V0, pa, ch0.o, hf, tr_r, tr_q, tr_dg);
-    } else if (i1.work) {
-      f32x16 b0, b1;
-      bf16x8 pbb[4];
-      tile_scores<D>(K1, qf, col, hf, b0, b1);
-      tile_softmax<DB>(b0, b1, ch1, i1.vmask, i1.causal, qi - i1.base - 16 * hf, hf, c2, pbb);
-      tile_pv<D>(V1, pbb, ch1.o, hf, tr_r, tr_q, tr_dg);
+    const int t = 2 * p + grp;
+    const bool is_cache = t < n_ct;
+    const int base = is_cache ? t * kKT : (t - n_ct) * kKT;
+    const bool work = active && t < n_tiles && (is_cache || base <= qb * 32 + 31);
+    if (work) {
+      const bf16_t* Kt = lds + ((stage * 2 + grp) * 2 + 0) * TILE;
+      const bf16_t* Vt = lds + ((stage * 2 + grp) * 2 + 1) * TILE;
+      f32x16 s0 = zero16(), s1 = zero16();
+#pragma unroll
+      for (int st = 0; st < DS; ++st) {
+        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(Kt + col * D + 8 * k_chunk<CPR>(col, 2 * st + hf));
+        const bf16x8 a1 =
+            *reinterpret_cast<const bf16x8*>(Kt + (32 + col) * D + 8 * k_chunk<CPR>(32 + col, 2 * st + hf));
+        s0 = mfma32x32x16(a0, qf[st], s0);
+        s1 = mfma32x32x16(a1, qf[st], s1);
+      }
+      const uint64_t vm = s_valid[stage][grp];
+      const bool causal = !is_cache && (base + kKT - 1 > qb * 32);
+      if (vm != ~0ull || causal) {
+        const uint32_t bits0 = static_cast<uint32_t>(vm >> (16 * hf)) & 0xffffu;
+        const uint32_t bits1 = static_cast<uint32_t>(vm >> (32 + 16 * hf)) & 0xffffu;
+        const int lim_i = causal ? qi - base - 16 * hf : 1 << 30;   // key offset bound
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool ok0 = ((bits0 >> r) & 1u) && (r <= lim_i);
+          const bool ok1 = ((bits1 >> r) & 1u) && (32 + r <= lim_i);
+          s0[r] = ok0 ? s0[r] : kNegInf;
+          s1[r] = ok1 ? s1[r] : kNegInf;
+        }
+      }
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+      mx = fmaxf(mx, xor32(mx));
+      const float m_new = fmaxf(m_run, mx * c2);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      float rs = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s0[r] = fast_exp2(fmaf(s0[r], c2, -m_use));
+        s1[r] = fast_exp2(fmaf(s1[r], c2, -m_use));
+        rs += s0[r] + s1[r];
+      }
+      l_run = fmaf(l_run, alpha, rs);
+      m_run = m_new;
+      if (__ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      }
+      // O^T += V^T P^T; MFMA (kb,u) covers keys 32kb + 16(l/32) + 8u + e.  The
+      // A operand V^T comes from two transpose reads: lane j = 4r + q of a
+      // 16-lane group addresses V[key0 + r][d0 + 4q .. +4).
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const f32x16& sv = kb ? s1 : s0;
+          f32x8 pv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pv[e] = sv[8 * u + e];
+          const bf16x8 pb = to_bf16x8(pv);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const int d = db * 32 + tr_dg * 16 + 4 * tr_q;
+            bf16x4 h0, h1;
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2) {
+              const int key = kb * 32 + 16 * hf + 8 * u + 4 * t2 + tr_r;
+              const bf16x4 v = lds_read_tr16(Vt + key * D + 8 * v_chunk<CPR>(key, d >> 3) + (d & 7));
+              if (t2 == 0) h0 = v; else h1 = v;
+            }
+            const bf16x8 a = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+            o[db] = mfma32x32x16(a, pb, o[db]);
+          }
+        }
+      }
     }
-    wait_pair();
+    // stage the next pair into the other buffer, prefetch the one after
+    if (p + 1 < n_pairs) store_pair(stage ^ 1);
+    if (p + 2 < n_pairs) load_pair(p + 2);
+    __syncthreads();
   }
-  if (!active) return;
 
-  // ---- merge the two chains
-  const float m = fmaxf(ch0.m, ch1.m);
-  const float mu = (m == kNegInf) ? 0.f : m;
-  const float w0 = fast_exp2(ch0.m - mu), w1 = fast_exp2(ch1.m - mu);
-  const float l_lane = ch0.l * w0 + ch1.l * w1;
-  const float l_tot = l_lane + xor32(l_lane);
+  // ---- merge the two groups' softmax states (group 1 -> LDS -> group 0)
+  float* xch = reinterpret_cast<float*>(lds);            // [DB*16 + 2][kRowBlocks*64]
+  const int slot = rbw * 64 + lane;
+  constexpr int NX = kRowBlocks * 64;
+  if (grp == 1) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xch[(db * 16 + r) * NX + slot] = o[db][r];
+    xch[(DB * 16) * NX + slot] = m_run;
+    xch[(DB * 16 + 1) * NX + slot] = l_run;
+  }
+  __syncthreads();
+  if (grp == 1 || !active) return;
+  {
+    const float m1 = xch[(DB * 16) * NX + slot];
+    const float l1 = xch[(DB * 16 + 1) * NX + slot];
+    const float m = fmaxf(m_run, m1);
+    const float mu = (m == kNegInf) ? 0.f : m;
+    const float a0 = fast_exp2(m_run - mu), a1 = fast_exp2(m1 - mu);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + xch[(db * 16 + r) * NX + slot] * a1;
+    l_run = l_run * a0 + l1 * a1;
+    m_run = m;
+  }
+  const float l_tot = l_run + xor32(l_run);
   if (qi >= S) return;
   const float inv = 1.f / l_tot;
   bf16_t* orow = O + (static_cast<size_t>(b * Hq + hq) * S + qi) * D;
@@ -355,13 +333,12 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      f32x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (ch0.o[db][4 * a + e] * w0 + ch1.o[db][4 * a + e] * w1) * inv;
+      f32x4 v = {o[db][4 * a] * inv, o[db][4 * a + 1] * inv, o[db][4 * a + 2] * inv,
+                 o[db][4 * a + 3] * inv};
       *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * a + 4 * hf) = to_bf16x4(v);
     }
   }
-  if (hf == 0) lse[static_cast<size_t>(b * Hq + hq) * S + qi] = (m + log2f(l_tot)) * kLn2;
+  if (hf == 0) lse[static_cast<size_t>(b * Hq + hq) * S + qi] = (m_run + log2f(l_tot)) * kLn2;
 }
 
 // fp32: one thread per (query head in group, query) row; 64 rows per wave.

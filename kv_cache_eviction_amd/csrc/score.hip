@@ -101,13 +101,14 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int idx = c * 256 + tid, row = idx / CPR, dc = idx % CPR;
-      const int r = r0 + row;
-      s.q[c] = (r < n_rows) ? load_u32x4(qhead + static_cast<size_t>(r) * D + dc * 8)
-                            : u32x4{0, 0, 0, 0};
+      // rows past the end read the last row; their lse of +inf zeroes them
+      const int r = min(r0 + row, n_rows - 1);
+      s.q[c] = load_u32x4(qhead + static_cast<size_t>(r) * D + dc * 8);
     }
     if (tid < kRB) {
       const int r = r0 + tid;
-      s.l = (r < n_rows) ? lhead[r] * kLog2e : __builtin_huge_valf();
+      const float lv = lhead[min(r, n_rows - 1)];
+      s.l = (r < n_rows) ? lv * kLog2e : __builtin_huge_valf();
       s.i = (r < n_rows) ? r % S : -1;
     }
   };
