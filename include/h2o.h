@@ -154,16 +154,18 @@ H2O_API h2o_status h2o_get_scores(const h2o_cache* c, float* scores_out,
 
 /* Frozen-eviction backward of one chunk's attention (the per-cell autograd of
  * LHF Fig. 1(b) for one chunk): gradients of sum(out * d_out) with the
- * visible sets of the forward step and the scores held constant.
+ * visible sets of the forward step (every slot with position >= 0, and chunk
+ * keys j <= i) and the scores held constant.  Stateless: uses `cfg` only.
  * Inputs: q [B,Hq,s,d]; the PRE-step cache k_cache, v_cache [B,Hkv,M,d] and
- * positions [B,Hkv,M]; k_new, v_new [B,Hkv,s,d]; the forward's out and lse;
- * d_out [B,Hq,s,d].
- * Outputs (all written): dq [B,Hq,s,d]; dk_cache, dv_cache [B,Hkv,M,d]
- * (zero at free slots); dk_new, dv_new [B,Hkv,s,d]; gradients in the
- * config's dtype.  workspace >= h2o_backward_workspace_bytes(cfg, s).
- * Errors: H2O_ERR_NULL, H2O_ERR_CONFIG, H2O_ERR_SHAPE (s < 1 or s > M... see
- * h2o_backward_workspace_bytes), H2O_ERR_WORKSPACE, H2O_ERR_UNSUPPORTED
- * (fp32 dtype), H2O_ERR_HIP. */
+ * positions [B,Hkv,M]; k_new, v_new [B,Hkv,s,d]; the forward's out
+ * [B,Hq,s,d] and lse [B,Hq,s]; d_out [B,Hq,s,d].
+ * Outputs (every element written): dq [B,Hq,s,d]; dk_cache, dv_cache
+ * [B,Hkv,M,d] (zero at free slots); dk_new, dv_new [B,Hkv,s,d]; all bf16.
+ * dK/dV of a KV head sum over the G query heads of its group.
+ * workspace >= h2o_backward_workspace_bytes(cfg, s) (holds dO . O per row).
+ * Deterministic (no atomics).  Errors: H2O_ERR_NULL, H2O_ERR_CONFIG,
+ * H2O_ERR_UNSUPPORTED (fp32 configs), H2O_ERR_SHAPE (s < 1 or s larger than
+ * max(max_chunk, max_prefill)), H2O_ERR_WORKSPACE, H2O_ERR_HIP. */
 H2O_API h2o_status h2o_chunk_backward(const h2o_config* cfg, const void* q,
                               const void* k_cache, const void* v_cache,
                               const int32_t* positions, const void* k_new,
@@ -173,7 +175,8 @@ H2O_API h2o_status h2o_chunk_backward(const h2o_config* cfg, const void* q,
                               void* dv_new, void* workspace,
                               size_t workspace_bytes, void* stream);
 
-/* Host only: workspace bytes h2o_chunk_backward needs for chunk length s. */
+/* Host only: workspace bytes h2o_chunk_backward needs for chunk length s
+ * (0 if the config is invalid or s < 1). */
 H2O_API size_t h2o_backward_workspace_bytes(const h2o_config* cfg, int32_t s);
 
 /* Tokens seen so far (T). */

@@ -337,9 +337,8 @@ void h2o_cache_destroy(h2o_cache* c) {
 int32_t h2o_last_hip_error(const h2o_cache* c) { return c ? c->last_hip_error : 0; }
 
 size_t h2o_backward_workspace_bytes(const h2o_config* cfg, int32_t s) {
-  (void)cfg;
-  (void)s;
-  return 0;
+  if (h2o_validate_config(cfg) != H2O_OK || s < 1) return 0;
+  return h2o::backward_workspace_bytes(cfg->batch, cfg->n_q_heads, s);
 }
 
 h2o_status h2o_chunk_backward(const h2o_config* cfg, const void* q, const void* k_cache,
@@ -348,10 +347,29 @@ h2o_status h2o_chunk_backward(const h2o_config* cfg, const void* q, const void* 
                               const void* d_out, void* dq, void* dk_cache, void* dv_cache,
                               void* dk_new, void* dv_new, void* workspace, size_t workspace_bytes,
                               void* stream) {
-  (void)cfg; (void)q; (void)k_cache; (void)v_cache; (void)positions; (void)k_new; (void)v_new;
-  (void)s; (void)out; (void)lse; (void)d_out; (void)dq; (void)dk_cache; (void)dv_cache;
-  (void)dk_new; (void)dv_new; (void)workspace; (void)workspace_bytes; (void)stream;
-  return H2O_ERR_UNSUPPORTED;
+  if (!cfg || !q || !k_cache || !v_cache || !positions || !k_new || !v_new || !out || !lse ||
+      !d_out || !dq || !dk_cache || !dv_cache || !dk_new || !dv_new || !workspace)
+    return H2O_ERR_NULL;
+  h2o_status r = h2o_validate_config(cfg);
+  if (r != H2O_OK) return r;
+  if (cfg->dtype != H2O_BF16) return H2O_ERR_UNSUPPORTED;
+  if (s < 1 || s > max_len(cfg)) return H2O_ERR_SHAPE;
+  if (workspace_bytes < h2o::backward_workspace_bytes(cfg->batch, cfg->n_q_heads, s))
+    return H2O_ERR_WORKSPACE;
+  h2o::StepShape sh;
+  sh.B = cfg->batch;
+  sh.Hq = cfg->n_q_heads;
+  sh.Hkv = cfg->n_kv_heads;
+  sh.D = cfg->head_dim;
+  sh.S = s;
+  sh.M = cfg->cache_slots;
+  sh.W = cfg->recent_window;
+  sh.n_cache = cfg->cache_slots;
+  sh.scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / sqrtf(static_cast<float>(cfg->head_dim));
+  h2o::BackwardArgs a{q, k_cache, v_cache, positions, k_new, v_new, out, lse, d_out,
+                      dq, dk_cache, dv_cache, dk_new, dv_new, workspace};
+  const hipError_t e = h2o::launch_backward(sh, a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? H2O_OK : H2O_ERR_HIP;
 }
 
 }  // extern "C"

@@ -1,0 +1,379 @@
+// Frozen-eviction backward of one chunk's attention (h2o_chunk_backward).
+//
+// "Learning how to Forget: Fine-tuning for Long-Context Sparse Attention"
+// (arXiv 2608.19920) trains through the chunk lattice of its Fig. 1 by
+// running autograd per cell (Fig. 1(b)); the gradient of one chunk step's
+// attention with the eviction decisions held fixed is the building block.
+// The visible sets are those of the forward step: every filled slot of the
+// pre-step cache and the chunk's keys j <= i; the scores are not
+// differentiated.  With P = softmax(scale * q.key) over the visible keys:
+//   D_i = dO_i . O_i,  dP = dO V^T,  dS = P * (dP - D),
+//   dq = scale * dS K,  dK = scale * dS^T Q,  dV = P^T dO,
+// where dK and dV of a KV head sum over the G query heads of its group.
+//
+// Two kernels, both deterministic (no atomics):
+//   * bwd_dq_kernel: one wave per 32-query row block (the forward's layout:
+//     S^T = K Q^T, lane = query), loops over the key tiles; also writes D.
+//     K rows sit in LDS in MFMA-row order, which keeps every aligned group of
+//     4 keys in 4 consecutive rows, so the same tile serves the K rows of S^T
+//     (16-byte reads) and K^T of dQ^T = K^T dS^T (transpose reads).
+//   * bwd_dkdv_kernel: one wave per 32 keys held in registers, loops over all
+//     query rows of the KV group (S = Q K^T, lane = key), accumulating
+//     dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T from transpose
+//     reads of the staged row block.
+#include "h2o_device.h"
+#include "h2o_launch.h"
+
+namespace h2o {
+namespace {
+
+constexpr int kBKT = 64;     // keys per LDS tile (dq kernel)
+constexpr int kBWaves = 4;
+
+__device__ __forceinline__ int bkrow_of_key(int k) {
+  return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3);
+}
+template <int CPR>
+__device__ __forceinline__ int bchunk(int row, int c) { return c ^ (row & (CPR - 1)); }
+
+// ---------------------------------------------------------------- dQ and D
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
+    const int32_t* __restrict__ pos, const bf16_t* __restrict__ Kn, const bf16_t* __restrict__ Vn,
+    const bf16_t* __restrict__ Oo, const bf16_t* __restrict__ dO, const float* __restrict__ lse,
+    float* __restrict__ Dws, bf16_t* __restrict__ dQ, int Hq, int Hkv, int S, int M, float c2,
+    float scale, int n_heads, int wg_per_head) {
+  constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
+  constexpr int NCH = kBKT * CPR / 256;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[kBKT * D];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[kBKT * D];
+  __shared__ uint64_t s_valid;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, col = lane & 31;
+  const int bh = blockIdx.x % n_heads;
+  const int wgi = wg_per_head - 1 - static_cast<int>(blockIdx.x) / n_heads;
+  const int b = bh / Hkv, kvh = bh - b * Hkv;
+  const int G = Hq / Hkv;
+  const int n_rb = G * ((S + 31) >> 5);
+  const int rb = wgi * kBWaves + wave;
+  const bool active = rb < n_rb;
+  const int g = active ? rb % G : 0;
+  const int qb = active ? rb / G : 0;
+  const int qi = qb * 32 + col;
+  const int hq = kvh * G + g;
+  const bool qok = active && qi < S;
+  const int rb_last = min(wgi * kBWaves + kBWaves - 1, n_rb - 1);
+  const int n_chunk_keys = min(S, (rb_last / G + 1) * 32);
+  const int n_ct = (M + kBKT - 1) / kBKT;
+  const int n_tiles = n_ct + (n_chunk_keys + kBKT - 1) / kBKT;
+
+  // the wave's queries and output gradients (B operands, lane = query)
+  const size_t row_off = (static_cast<size_t>(b * Hq + hq) * S + (qok ? qi : 0)) * D;
+  bf16x8 qf[DS], dof[DS];
+  float dsum = 0.f;
+#pragma unroll
+  for (int st = 0; st < DS; ++st) {
+    const bf16x8 q = load_bf16x8(Q + row_off + 16 * st + 8 * hf);
+    const bf16x8 go = load_bf16x8(dO + row_off + 16 * st + 8 * hf);
+    const bf16x8 o = load_bf16x8(Oo + row_off + 16 * st + 8 * hf);
+    qf[st] = qok ? q : bf16x8{};
+    dof[st] = qok ? go : bf16x8{};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dsum = fmaf(static_cast<float>(go[e]), static_cast<float>(o[e]), dsum);
+  }
+  dsum += xor32(dsum);
+  const float Di = qok ? dsum : 0.f;
+  const float lse2 = qok ? lse[static_cast<size_t>(b * Hq + hq) * S + qi] * kLog2e : __builtin_huge_valf();
+  if (qok && hf == 0) Dws[static_cast<size_t>(b * Hq + hq) * S + qi] = Di;
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = zero16();
+
+  const bf16_t* kc_head = Kc + static_cast<size_t>(bh) * M * D;
+  const bf16_t* vc_head = Vc + static_cast<size_t>(bh) * M * D;
+  const bf16_t* kn_head = Kn + static_cast<size_t>(bh) * S * D;
+  const bf16_t* vn_head = Vn + static_cast<size_t>(bh) * S * D;
+  const int32_t* pos_head = pos + static_cast<size_t>(bh) * M;
+  const int tr_j = lane & 15, tr_r = tr_j >> 2, tr_q = tr_j & 3, tr_dg = (lane >> 4) & 1;
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const bool is_cache = t < n_ct;
+    const int base = is_cache ? t * kBKT : (t - n_ct) * kBKT;
+    const int lim = is_cache ? M : S;
+    const bf16_t* ks = is_cache ? kc_head : kn_head;
+    const bf16_t* vs = is_cache ? vc_head : vn_head;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < NCH; ++r) {
+      const int c = r * 256 + tid, key = c / CPR, ch = c % CPR;
+      const int src = min(base + key, lim - 1);
+      const u32x4 kv = load_u32x4(ks + static_cast<size_t>(src) * D + ch * 8);
+      const u32x4 vv = load_u32x4(vs + static_cast<size_t>(src) * D + ch * 8);
+      const int row = (key & ~31) | bkrow_of_key(key & 31);
+      store_u32x4(&Ks[row * D + 8 * bchunk<CPR>(row, ch)], kv);
+      store_u32x4(&Vs[row * D + 8 * bchunk<CPR>(row, ch)], vv);
+    }
+    if (wave == 0) {
+      const int key = base + lane;
+      const int pv = pos_head[is_cache ? min(key, M - 1) : 0];
+      const uint64_t m = __ballot(key < lim && (!is_cache || pv >= 0));
+      if (lane == 0) s_valid = m;
+    }
+    __syncthreads();
+    if (!active || (!is_cache && base > qb * 32 + 31)) continue;
+    // S^T and dP^T (keys x queries): register r of lane l <-> key 16(l/32) + r (+32 kb)
+    f32x16 s0 = zero16(), s1 = zero16(), p0 = zero16(), p1 = zero16();
+#pragma unroll
+    for (int st = 0; st < DS; ++st) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[col * D + 8 * bchunk<CPR>(col, 2 * st + hf)]);
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&Ks[(32 + col) * D + 8 * bchunk<CPR>(32 + col, 2 * st + hf)]);
+      const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vs[col * D + 8 * bchunk<CPR>(col, 2 * st + hf)]);
+      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&Vs[(32 + col) * D + 8 * bchunk<CPR>(32 + col, 2 * st + hf)]);
+      s0 = mfma32x32x16(ka, qf[st], s0);
+      s1 = mfma32x32x16(kb, qf[st], s1);
+      p0 = mfma32x32x16(va, dof[st], p0);
+      p1 = mfma32x32x16(vb, dof[st], p1);
+    }
+    const uint64_t vm = s_valid;
+    const bool causal = !is_cache && (base + kBKT - 1 > qb * 32);
+    const uint32_t bits0 = static_cast<uint32_t>(vm >> (16 * hf)) & 0xffffu;
+    const uint32_t bits1 = static_cast<uint32_t>(vm >> (32 + 16 * hf)) & 0xffffu;
+    const int lim_i = causal ? qi - base - 16 * hf : 1 << 30;
+    f32x8 d8[4];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const bool ok0 = ((bits0 >> r) & 1u) && (r <= lim_i);
+      const bool ok1 = ((bits1 >> r) & 1u) && (32 + r <= lim_i);
+      const float pa = ok0 ? fast_exp2(fmaf(s0[r], c2, -lse2)) : 0.f;
+      const float pb = ok1 ? fast_exp2(fmaf(s1[r], c2, -lse2)) : 0.f;
+      d8[r >> 3][r & 7] = pa * (p0[r] - Di);
+      d8[2 + (r >> 3)][r & 7] = pb * (p1[r] - Di);
+    }
+    // dQ^T += K^T dS^T: MFMA (kb,u) covers keys 32kb + 16(l/32) + 8u + e
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bf16x8 ds = to_bf16x8(d8[2 * kb + u]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int d = db * 32 + tr_dg * 16 + 4 * tr_q;
+          const int k0 = kb * 32 + 16 * hf + 8 * u;             // keys k0 .. k0+7
+          const int r0 = (k0 & ~31) | bkrow_of_key((k0 & 31) + tr_r);
+          const int r1 = (k0 & ~31) | bkrow_of_key((k0 & 31) + 4 + tr_r);
+          const bf16x4 h0 = lds_read_tr16(&Ks[r0 * D + 8 * bchunk<CPR>(r0, d >> 3) + (d & 7)]);
+          const bf16x4 h1 = lds_read_tr16(&Ks[r1 * D + 8 * bchunk<CPR>(r1, d >> 3) + (d & 7)]);
+          const bf16x8 a = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+          acc[db] = mfma32x32x16(a, ds, acc[db]);
+        }
+      }
+    }
+  }
+  if (!qok) return;
+  bf16_t* out = dQ + row_off;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      f32x4 v = {acc[db][4 * a] * scale, acc[db][4 * a + 1] * scale, acc[db][4 * a + 2] * scale,
+                 acc[db][4 * a + 3] * scale};
+      *reinterpret_cast<bf16x4*>(out + db * 32 + 8 * a + 4 * hf) = to_bf16x4(v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dK and dV
+constexpr int kKeysPerWG = 128;     // 4 waves x 32 keys
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
+    const int32_t* __restrict__ pos, const bf16_t* __restrict__ Kn, const bf16_t* __restrict__ Vn,
+    const bf16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dws,
+    bf16_t* __restrict__ dKc, bf16_t* __restrict__ dVc, bf16_t* __restrict__ dKn,
+    bf16_t* __restrict__ dVn, int Hq, int Hkv, int S, int M, float c2, float scale, int n_heads,
+    int n_ct, int n_tiles) {
+  constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
+  constexpr int NCH = 32 * CPR / 256;      // 16-byte chunks per thread per 32-row block
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[32 * D];
+  __shared__ __attribute__((aligned(16))) bf16_t Gs[32 * D];
+  __shared__ __attribute__((aligned(16))) float s_lse2[32];
+  __shared__ __attribute__((aligned(16))) float s_D[32];
+  __shared__ __attribute__((aligned(16))) int s_irow[32];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, col = lane & 31;
+  const int bh = blockIdx.x % n_heads;
+  const int tile = static_cast<int>(blockIdx.x) / n_heads;
+  const int b = bh / Hkv, kvh = bh - b * Hkv;
+  const int G = Hq / Hkv;
+  const bool is_cache = tile < n_ct;
+  const int base = (is_cache ? tile : tile - n_ct) * kKeysPerWG;
+  const int lim = is_cache ? M : S;
+  const int key = base + wave * 32 + col;                 // this lane's key column
+  const bf16_t* kh = is_cache ? Kc + static_cast<size_t>(bh) * M * D : Kn + static_cast<size_t>(bh) * S * D;
+  const bf16_t* vh = is_cache ? Vc + static_cast<size_t>(bh) * M * D : Vn + static_cast<size_t>(bh) * S * D;
+  const int pv = pos[static_cast<size_t>(bh) * M + (is_cache ? min(key, M - 1) : 0)];
+  const bool key_ok = key < lim && (!is_cache || pv >= 0);
+  const int wave_key0 = base + wave * 32;
+
+  // the wave's keys and values: B operands of S = Q K^T and dP = dO V^T (lane = key)
+  bf16x8 kf[DS], vf[DS];
+  {
+    const size_t off = static_cast<size_t>(min(key, lim - 1)) * D;
+#pragma unroll
+    for (int st = 0; st < DS; ++st) {
+      const bf16x8 k = load_bf16x8(kh + off + 16 * st + 8 * hf);
+      const bf16x8 v = load_bf16x8(vh + off + 16 * st + 8 * hf);
+      kf[st] = key_ok ? k : bf16x8{};
+      vf[st] = key_ok ? v : bf16x8{};
+    }
+  }
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dk[db] = zero16();
+    dv[db] = zero16();
+  }
+
+  const int n_rows = G * S;
+  const bf16_t* qhead = Q + static_cast<size_t>(b * Hq + kvh * G) * S * D;   // rows g*S + i
+  const bf16_t* ghead = dO + static_cast<size_t>(b * Hq + kvh * G) * S * D;
+  const float* lhead = lse + static_cast<size_t>(b * Hq + kvh * G) * S;
+  const float* dhead = Dws + static_cast<size_t>(b * Hq + kvh * G) * S;
+  const int tr_j = lane & 15, tr_r = tr_j >> 2, tr_q = tr_j & 3, tr_dg = (lane >> 4) & 1;
+  const int wave_lim = min(lim, wave_key0 + 32);          // keys of this wave that exist
+
+  for (int r0 = 0; r0 < n_rows; r0 += 32) {
+    // chunk keys only see queries i >= key: skip blocks whose queries all precede the tile
+    if (!is_cache) {
+      const int r1 = min(r0 + 31, n_rows - 1);
+      if (r0 / S == r1 / S && (r1 % S) < base) continue;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int idx = c * 256 + tid, row = idx / CPR, ch = idx % CPR;
+      const int r = min(r0 + row, n_rows - 1);
+      const u32x4 q = load_u32x4(qhead + static_cast<size_t>(r) * D + ch * 8);
+      const u32x4 go = load_u32x4(ghead + static_cast<size_t>(r) * D + ch * 8);
+      store_u32x4(&Qs[row * D + 8 * bchunk<CPR>(row, ch)], q);
+      store_u32x4(&Gs[row * D + 8 * bchunk<CPR>(row, ch)], go);
+    }
+    if (tid < 32) {
+      const int r = r0 + tid;
+      const int rc = min(r, n_rows - 1);
+      const float lv = lhead[rc], dv_ = dhead[rc];
+      s_lse2[tid] = r < n_rows ? lv * kLog2e : __builtin_huge_valf();
+      s_D[tid] = r < n_rows ? dv_ : 0.f;
+      s_irow[tid] = r < n_rows ? r % S : -1;
+    }
+    __syncthreads();
+    if (wave_key0 >= wave_lim) continue;
+    // S and dP (queries x keys): register r of lane l <-> row 8(r/4) + 4(l/32) + r%4
+    f32x16 s = zero16(), p = zero16();
+#pragma unroll
+    for (int st = 0; st < DS; ++st) {
+      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qs[col * D + 8 * bchunk<CPR>(col, 2 * st + hf)]);
+      const bf16x8 ga = *reinterpret_cast<const bf16x8*>(&Gs[col * D + 8 * bchunk<CPR>(col, 2 * st + hf)]);
+      s = mfma32x32x16(qa, kf[st], s);
+      p = mfma32x32x16(ga, vf[st], p);
+    }
+    f32x8 pp[2], dd[2];
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int row0 = 8 * a4 + 4 * hf;
+      const f32x4 l2 = *reinterpret_cast<const f32x4*>(&s_lse2[row0]);
+      const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&s_D[row0]);
+      const int4 iv = *reinterpret_cast<const int4*>(&s_irow[row0]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * a4 + e;
+        const int qi = e == 0 ? iv.x : e == 1 ? iv.y : e == 2 ? iv.z : iv.w;
+        const bool ok = key_ok && (is_cache || key <= qi);
+        const float pr = ok ? fast_exp2(fmaf(s[r], c2, -l2[e])) : 0.f;
+        pp[r >> 3][r & 7] = pr;
+        dd[r >> 3][r & 7] = pr * (p[r] - dv4[e]);
+      }
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS: MFMA u contracts over the rows held
+    // in registers 8u..8u+7, i.e. rows 16u + 4(l/32) + {0..3, 8..11}
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const bf16x8 pb = to_bf16x8(pp[u]);
+      const bf16x8 db8 = to_bf16x8(dd[u]);
+      const int ra = 16 * u + 4 * hf + tr_r, rbx = ra + 8;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int d = db * 32 + tr_dg * 16 + 4 * tr_q;
+        const bf16x4 g0 = lds_read_tr16(&Gs[ra * D + 8 * bchunk<CPR>(ra, d >> 3) + (d & 7)]);
+        const bf16x4 g1 = lds_read_tr16(&Gs[rbx * D + 8 * bchunk<CPR>(rbx, d >> 3) + (d & 7)]);
+        const bf16x4 q0 = lds_read_tr16(&Qs[ra * D + 8 * bchunk<CPR>(ra, d >> 3) + (d & 7)]);
+        const bf16x4 q1 = lds_read_tr16(&Qs[rbx * D + 8 * bchunk<CPR>(rbx, d >> 3) + (d & 7)]);
+        dv[db] = mfma32x32x16(__builtin_shufflevector(g0, g1, 0, 1, 2, 3, 4, 5, 6, 7), pb, dv[db]);
+        dk[db] = mfma32x32x16(__builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7), db8, dk[db]);
+      }
+    }
+  }
+  if (key >= lim) return;
+  bf16_t* ko = (is_cache ? dKc + static_cast<size_t>(bh) * M * D : dKn + static_cast<size_t>(bh) * S * D) +
+               static_cast<size_t>(key) * D;
+  bf16_t* vo = (is_cache ? dVc + static_cast<size_t>(bh) * M * D : dVn + static_cast<size_t>(bh) * S * D) +
+               static_cast<size_t>(key) * D;
+  // accumulator register r of lane l: d = 32 db + 8(r/4) + 4(l/32) + r%4, key column l%32
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      f32x4 kv = {dk[db][4 * a] * scale, dk[db][4 * a + 1] * scale, dk[db][4 * a + 2] * scale,
+                  dk[db][4 * a + 3] * scale};
+      f32x4 vv = {dv[db][4 * a], dv[db][4 * a + 1], dv[db][4 * a + 2], dv[db][4 * a + 3]};
+      *reinterpret_cast<bf16x4*>(ko + db * 32 + 8 * a + 4 * hf) = to_bf16x4(kv);
+      *reinterpret_cast<bf16x4*>(vo + db * 32 + 8 * a + 4 * hf) = to_bf16x4(vv);
+    }
+  }
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(int B, int Hq, int S) {
+  return static_cast<size_t>(B) * Hq * S * sizeof(float);
+}
+
+hipError_t launch_backward(const StepShape& sh, const BackwardArgs& a, hipStream_t st) {
+  const int n_heads = sh.B * sh.Hkv;
+  const int G = sh.Hq / sh.Hkv;
+  const float c2 = sh.scale * kLog2e;
+  const int n_rb = G * ((sh.S + 31) / 32);
+  const int wgp = (n_rb + kBWaves - 1) / kBWaves;
+  float* Dws = static_cast<float*>(a.workspace);
+#define H2O_LAUNCH_DQ(DD)                                                                              \
+  hipLaunchKernelGGL(bwd_dq_kernel<DD>, dim3(n_heads * wgp), dim3(256), 0, st,                         \
+                     static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k_cache),          \
+                     static_cast<const bf16_t*>(a.v_cache), a.pos, static_cast<const bf16_t*>(a.k_new), \
+                     static_cast<const bf16_t*>(a.v_new), static_cast<const bf16_t*>(a.out),          \
+                     static_cast<const bf16_t*>(a.d_out), a.lse, Dws, static_cast<bf16_t*>(a.dq),     \
+                     sh.Hq, sh.Hkv, sh.S, sh.M, c2, sh.scale, n_heads, wgp)
+  if (sh.D == 128) H2O_LAUNCH_DQ(128);
+  else H2O_LAUNCH_DQ(64);
+#undef H2O_LAUNCH_DQ
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_ct = (sh.M + kKeysPerWG - 1) / kKeysPerWG;
+  const int n_tiles = n_ct + (sh.S + kKeysPerWG - 1) / kKeysPerWG;
+#define H2O_LAUNCH_DKDV(DD)                                                                            \
+  hipLaunchKernelGGL(bwd_dkdv_kernel<DD>, dim3(n_heads * n_tiles), dim3(256), 0, st,                   \
+                     static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k_cache),          \
+                     static_cast<const bf16_t*>(a.v_cache), a.pos, static_cast<const bf16_t*>(a.k_new), \
+                     static_cast<const bf16_t*>(a.v_new), static_cast<const bf16_t*>(a.d_out), a.lse, \
+                     Dws, static_cast<bf16_t*>(a.dk_cache), static_cast<bf16_t*>(a.dv_cache),         \
+                     static_cast<bf16_t*>(a.dk_new), static_cast<bf16_t*>(a.dv_new), sh.Hq, sh.Hkv,   \
+                     sh.S, sh.M, c2, sh.scale, n_heads, n_ct, n_tiles)
+  if (sh.D == 128) H2O_LAUNCH_DKDV(128);
+  else H2O_LAUNCH_DKDV(64);
+#undef H2O_LAUNCH_DKDV
+  return hipGetLastError();
+}
+
+}  // namespace h2o

@@ -52,12 +52,32 @@ struct SelectArgs {
   int32_t T;            // tokens seen before the chunk
 };
 
+struct BackwardArgs {
+  const void* q;
+  const void* k_cache;     // pre-step cache
+  const void* v_cache;
+  const int32_t* pos;      // pre-step positions
+  const void* k_new;
+  const void* v_new;
+  const void* out;
+  const float* lse;
+  const void* d_out;
+  void* dq;
+  void* dk_cache;
+  void* dv_cache;
+  void* dk_new;
+  void* dv_new;
+  void* workspace;         // >= backward_workspace_bytes: D_i = dO_i . O_i
+};
+
 enum Dtype { kBF16 = 0, kFP32 = 1 };
 
 hipError_t launch_attn_fwd(const StepShape& sh, const AttnArgs& a, int dtype, hipStream_t st);
 hipError_t launch_score(const StepShape& sh, const ScoreArgs& a, int dtype, hipStream_t st);
 hipError_t launch_select(const StepShape& sh, const SelectArgs& a, hipStream_t st);
 hipError_t launch_scatter(const StepShape& sh, const SelectArgs& a, int dtype, hipStream_t st);
+hipError_t launch_backward(const StepShape& sh, const BackwardArgs& a, hipStream_t st);
+size_t backward_workspace_bytes(int B, int Hq, int S);
 hipError_t launch_reset(float* scores, int32_t* pos, int64_t n_slots, int32_t* counters,
                         int64_t n_counters, hipStream_t st);
 
