@@ -124,9 +124,10 @@ def run_and_check_step(cache, cfg, q_np, k_np, v_np, heads, W, scale=None, prefi
     after = snapshot(cache)
     assert after.T == before.T + S
     out_g, lse_g = to_f64(out), to_f64(lse)
-    slots_g = slots.cpu().numpy()
-    mass_g = to_f64(mass)
-    kold_g, vold_g = to_f64(k_old), to_f64(v_old)
+    if not prefill:      # the prefill call does not take these outputs
+        slots_g = slots.cpu().numpy()
+        mass_g = to_f64(mass)
+        kold_g, vold_g = to_f64(k_old), to_f64(v_old)
     qf, kf, vf = wl.stored_to_f64(q_np), wl.stored_to_f64(k_np), wl.stored_to_f64(v_np)
     errs = dict(o_max_abs=0.0, o_rel_rms=0.0, lse_max_abs=0.0, score_rel=0.0, mass_rel=0.0,
                 tie_exempt=0, min_gap=math.inf)

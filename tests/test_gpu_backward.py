@@ -35,16 +35,17 @@ def _grads_vs_oracle(w, cfg, state, q, k, v, out, lse, dO, heads):
     h2o.h2o_chunk_backward(cfg, q, Kc, Vc, pos, k, v, out, lse, dO, dq, dkc, dvc, dkn, dvn, ws)
     torch.cuda.synchronize()
     f = lambda t: t.double().cpu().numpy()
+    Kn, Vn, Pn = f(Kc), f(Vc), pos.cpu().numpy().astype(np.int64)
+    qn, kn, vn, gn = f(q), f(k), f(v), f(dO)
+    gpu = [f(dq), f(dkc), f(dvc), f(dkn), f(dvn)]
     G = w.group
     worst = 0.0
     for b, h in heads:
         hs = slice(h * G, (h + 1) * G)
-        ref = orc.chunk_backward(f(Kc)[b:b + 1, h:h + 1], f(Vc)[b:b + 1, h:h + 1],
-                                 pos.cpu().numpy()[b:b + 1, h:h + 1].astype(np.int64),
-                                 f(q)[b:b + 1, hs], f(k)[b:b + 1, h:h + 1], f(v)[b:b + 1, h:h + 1],
-                                 f(dO)[b:b + 1, hs], 1.0 / math.sqrt(w.head_dim))
-        got = [f(dq)[b:b + 1, hs], f(dkc)[b:b + 1, h:h + 1], f(dvc)[b:b + 1, h:h + 1],
-               f(dkn)[b:b + 1, h:h + 1], f(dvn)[b:b + 1, h:h + 1]]
+        hk = slice(h, h + 1)
+        ref = orc.chunk_backward(Kn[b:b + 1, hk], Vn[b:b + 1, hk], Pn[b:b + 1, hk], qn[b:b + 1, hs],
+                                 kn[b:b + 1, hk], vn[b:b + 1, hk], gn[b:b + 1, hs], 1.0 / math.sqrt(w.head_dim))
+        got = [gpu[0][b:b + 1, hs]] + [t[b:b + 1, hk] for t in gpu[1:]]
         for name, g, r in zip(["dq", "dk_cache", "dv_cache", "dk_new", "dv_new"], got, ref):
             scale = np.abs(r).max()
             if scale == 0:
@@ -54,8 +55,8 @@ def _grads_vs_oracle(w, cfg, state, q, k, v, out, lse, dO, heads):
             max_rel = np.abs(g - r).max() / scale
             worst = max(worst, rel_rms)
             assert rel_rms <= REL_RMS and max_rel <= MAX_REL, (name, b, h, rel_rms, max_rel)
-        free = pos.cpu().numpy()[b, h] < 0
-        assert (f(dkc)[b, h][free] == 0).all() and (f(dvc)[b, h][free] == 0).all()
+        free = Pn[b, h] < 0
+        assert (gpu[1][b, h][free] == 0).all() and (gpu[2][b, h][free] == 0).all()
     return worst
 
 
