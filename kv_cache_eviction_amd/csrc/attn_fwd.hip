@@ -43,15 +43,19 @@
 //     with the longest causal extent are dispatched first.
 // fp32 path: one thread per query row, scalar online softmax over K/V rows
 // broadcast from LDS (used for fp32 workloads, which are tiny).
+#include <type_traits>
+
 #include "h2o_device.h"
 #include "h2o_launch.h"
 
 namespace h2o {
 namespace {
 
-constexpr int kKT = 64;        // keys per LDS tile
+constexpr int kKT = 64;        // keys per tile
 constexpr int kRowBlocks = 4;  // row blocks (32 queries of one head) per workgroup
 constexpr int kFwdThreads = 512;
+constexpr float kRescaleSlack = 8.f;   // log2 headroom before the running maximum must move
+constexpr float kNoMax = -1e30f;       // running maximum of a query that has seen no key yet
 
 // Key k (0..31) of a 32-key block -> LDS row = MFMA A-operand row that reads
 // it.  Row 8q + 4h + r holds key 16h + 4q + r, so that accumulator register
@@ -59,8 +63,12 @@ constexpr int kFwdThreads = 512;
 __device__ __forceinline__ int krow_of_key(int k) {
   return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3);
 }
+__device__ __forceinline__ int key_of_krow(int r) {
+  return ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3);
+}
 
-// Swizzled 16-byte chunk of a K row / V row (CPR chunks per row).
+// Swizzled 16-byte chunk of a K row / V row (CPR chunks per row); both maps
+// are involutions in the chunk index.
 template <int CPR>
 __device__ __forceinline__ int k_chunk(int row, int c) { return c ^ (row & (CPR - 1)); }
 template <int CPR>
@@ -78,14 +86,15 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   constexpr int DS = D / 16;              // MFMA k-steps over d
   constexpr int DB = D / 32;              // 32-row blocks of O^T
   constexpr int CPR = D / 8;              // 16-byte chunks per row
-  constexpr int TILE = kKT * D;           // elements per K or V tile
-  constexpr int NCH = 2 * 2 * kKT * CPR / kFwdThreads;   // chunks per thread per tile pair
-  // [stage][group][K,V][TILE]
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * 2 * 2 * TILE];
-  __shared__ uint64_t s_valid[2][2];
+  constexpr int RB = 2 * D;               // bytes per K or V row
+  constexpr int TB = kKT * RB;            // bytes per K or V tile
+  constexpr int NDMA = TB / 4096;         // 1 KB copies per wave per tile (4 waves per group)
+  // K slots [group][2] at 0, V slots [group][2] at 4 TB
+  __shared__ __attribute__((aligned(1024))) char lds[8 * TB];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, hf = lane >> 5, col = lane & 31;
   const int grp = wave >> 2, rbw = wave & 3;
   const int bh = blockIdx.x % n_heads;
   const int wgi = wg_per_head - 1 - static_cast<int>(blockIdx.x) / n_heads;
@@ -102,13 +111,20 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   const int n_chunk_keys = min(S, (rb_last / G + 1) * 32);
   const int n_ct = (n_cache + kKT - 1) / kKT;
   const int n_tiles = n_ct + (n_chunk_keys + kKT - 1) / kKT;
-  const int n_pairs = (n_tiles + 1) >> 1;
+  // group g takes tiles 2t + g, t < n_iter (even: the loop body is unrolled
+  // by two so that LDS slot parities are compile-time); tiles past the end
+  // are fully masked
+  const int n_iter = ((n_tiles + 3) >> 2) << 1;
 
   const bf16_t* kc_head = Kc + static_cast<size_t>(bh) * M * D;
   const bf16_t* vc_head = Vc + static_cast<size_t>(bh) * M * D;
   const bf16_t* kn_head = Kn + static_cast<size_t>(bh) * S * D;
   const bf16_t* vn_head = Vn + static_cast<size_t>(bh) * S * D;
   const int32_t* pos_head = pos + static_cast<size_t>(bh) * M;
+  const __amdgpu_buffer_rsrc_t rk_c = make_rsrc(kc_head, static_cast<uint32_t>(M) * RB);
+  const __amdgpu_buffer_rsrc_t rv_c = make_rsrc(vc_head, static_cast<uint32_t>(M) * RB);
+  const __amdgpu_buffer_rsrc_t rk_n = make_rsrc(kn_head, static_cast<uint32_t>(S) * RB);
+  const __amdgpu_buffer_rsrc_t rv_n = make_rsrc(vn_head, static_cast<uint32_t>(S) * RB);
 
   // The wave's queries: B operand of S^T = K Q^T (lane: query col, d 8hf..+8).
   bf16x8 qf[DS];
@@ -124,181 +140,252 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = zero16();
-  float m_run = kNegInf, l_run = 0.f;
+  float m_run = kNoMax, l_run = 0.f;
 
-  // ---- staging: tile pair p = tiles (2p, 2p+1).  Chunk r of a thread is
-  // c = tid + 512 r; its tile (tt), matrix (K or V) and row follow from r at
-  // compile time, so every source pointer is a uniform per-tile value.
-  struct TileSrc {
-    const bf16_t* k;
-    const bf16_t* v;
-    int n;            // rows of the tile that exist (keys < lim)
+  // ---- tile copies (global -> LDS, no registers).  LDS byte 1024 j' + 16 i
+  // of a tile (j' = rbw NDMA + j, lane i) is row r, physical chunk c'; the
+  // lane fetches the source row and logical chunk that belong there.  Worked
+  // out for the two row sizes, the source offset splits into a per-lane part
+  // (one register; for K rows of 256 bytes the copy index flips two bits of
+  // it) and a wave-uniform part passed as the scalar offset.
+  // lane_src(l, &k, &v): per-lane parts for lane l
+  auto lane_src = [](int l, uint32_t& k, uint32_t& v) __attribute__((always_inline)) {
+    if constexpr (D == 128) {
+      const int q = l >> 4;
+      k = 256 * q + 16 * ((l & 15) ^ q);
+      v = 256 * q + 16 * ((l & 15) ^ (4 * q));
+    } else {
+      const int q8 = l >> 3, c = l & 7;
+      k = 128 * (16 * ((q8 >> 2) & 1) + (q8 & 3)) + 16 * (c ^ q8);
+      v = 128 * q8 + 16 * (c ^ ((q8 & 3) << 1));
+    }
   };
-  auto tile_src = [&](int t) __attribute__((always_inline)) {
-    TileSrc r;
-    const bool is_cache = t < n_ct;
-    const bool exists = t < n_tiles;
-    const int base = is_cache ? t * kKT : (t - n_ct) * kKT;
-    const size_t off = exists ? static_cast<size_t>(base) * D : 0;
-    r.k = ((exists && is_cache) ? kc_head : kn_head) + off;
-    r.v = ((exists && is_cache) ? vc_head : vn_head) + off;
-    r.n = exists ? (is_cache ? n_cache : S) - base : 1;   // a tile past the end reads chunk row 0
-    return r;
+  uint32_t dk_lane, dv_lane;
+  lane_src(lane, dk_lane, dv_lane);
+  auto dk_voff = [&](int j) __attribute__((always_inline)) {
+    return D == 128 ? (dk_lane ^ (64u * j)) : dk_lane;
   };
-  constexpr int RPT = NCH / 2;                  // chunks per thread per tile
-  constexpr int RPM = RPT / 2;                  // chunks per thread per matrix of a tile
-  const int ch = tid % CPR;                     // 16-byte chunk within the row
-  const int row0 = tid / CPR;                   // first row; chunk r adds (r % RPM) * (512 / CPR)
-  u32x4 reg[NCH];
-  int preg = -1;
-  auto load_pair = [&](int p) __attribute__((always_inline)) {
+  auto dk_soff = [&](int j) __attribute__((always_inline)) {
+    return static_cast<uint32_t>(D == 128 ? 256 * (32 * (rbw >> 1) + 8 * (rbw & 1) + 16 * (j & 1) + 4 * (j >> 1))
+                                          : 128 * (32 * (rbw >> 1) + 4 * (2 * (rbw & 1) + j)));
+  };
+  auto dv_soff = [&](int j) __attribute__((always_inline)) {
+    return static_cast<uint32_t>(D == 128 ? 256 * (16 * rbw + 4 * j) : 128 * 8 * (2 * rbw + j));
+  };
+  const char* lds_k = lds + grp * 2 * TB;
+  const char* lds_v = lds + 4 * TB + grp * 2 * TB;
+  // rows past the end of a partial tile re-read its last row (masked later)
+  auto clamp_row = [](uint32_t off, int n) __attribute__((always_inline)) {
+    const int key = static_cast<int>(off / RB);
+    return key < n ? off : off - static_cast<uint32_t>(key - n + 1) * RB;
+  };
+  auto issue_k = [&](int T, int slot) __attribute__((always_inline)) {
+    if (T >= n_tiles) return;
+    const bool is_cache = T < n_ct;
+    const int base = is_cache ? T * kKT : (T - n_ct) * kKT;
+    const int n = (is_cache ? n_cache : S) - base;
+    const __amdgpu_buffer_rsrc_t r = is_cache ? rk_c : rk_n;
+    const char* dst = lds_k + slot * TB + rbw * NDMA * 1024;
+    const uint32_t soff = static_cast<uint32_t>(base) * RB;
+    if (n >= kKT) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const TileSrc ts = tile_src(2 * p + tt);
+      for (int j = 0; j < NDMA; ++j) dma16(r, dst + j * 1024, dk_voff(j), soff + dk_soff(j));
+    } else {      // rare: recomputed here so that the clamped offsets hold no registers
+      int l = lane;
+      asm volatile("" : "+v"(l));
+      uint32_t kl, vl;
+      lane_src(l, kl, vl);
 #pragma unroll
-      for (int mat = 0; mat < 2; ++mat) {
-#pragma unroll
-        for (int i = 0; i < RPM; ++i) {
-          const int row = row0 + i * (kFwdThreads / CPR);
-          // rows past the end of a tile read its last row (masked later): no branches
-          const bf16_t* src = (mat ? ts.v : ts.k) + min(row, ts.n - 1) * D + ch * 8;
-          reg[(tt * 2 + mat) * RPM + i] = load_u32x4(src);
-        }
+      for (int j = 0; j < NDMA; ++j) {
+        const uint32_t ko = D == 128 ? (kl ^ (64u * j)) : kl;
+        dma16(r, dst + j * 1024, clamp_row(ko + dk_soff(j), n), soff);
       }
     }
-    if (wave < 2) {                       // wave tt fetches the positions of tile 2p+tt
-      const int t = 2 * p + wave;
-      const bool is_cache = t < n_ct;
-      const int base = is_cache ? t * kKT : (t - n_ct) * kKT;
-      const int lim = t < n_tiles ? (is_cache ? n_cache : S) : base;
-      const int key = base + lane;
-      const int pv = pos_head[is_cache ? min(key, M - 1) : 0];
-      preg = key < lim ? (is_cache ? pv : 0) : -1;
+  };
+  auto issue_v = [&](int T, int slot) __attribute__((always_inline)) {
+    if (T >= n_tiles) return;
+    const bool is_cache = T < n_ct;
+    const int base = is_cache ? T * kKT : (T - n_ct) * kKT;
+    const int n = (is_cache ? n_cache : S) - base;
+    const __amdgpu_buffer_rsrc_t r = is_cache ? rv_c : rv_n;
+    const char* dst = lds_v + slot * TB + rbw * NDMA * 1024;
+    const uint32_t soff = static_cast<uint32_t>(base) * RB;
+    if (n >= kKT) {
+#pragma unroll
+      for (int j = 0; j < NDMA; ++j) dma16(r, dst + j * 1024, dv_lane, soff + dv_soff(j));
+    } else {      // rare: as for K
+      int l = lane;
+      asm volatile("" : "+v"(l));
+      uint32_t kl, vl;
+      lane_src(l, kl, vl);
+#pragma unroll
+      for (int j = 0; j < NDMA; ++j) dma16(r, dst + j * 1024, clamp_row(vl + dv_soff(j), n), soff);
     }
   };
-  auto store_pair = [&](int stage) __attribute__((always_inline)) {
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-      for (int mat = 0; mat < 2; ++mat) {
-        bf16_t* dst = lds + ((stage * 2 + tt) * 2 + mat) * TILE;
-#pragma unroll
-        for (int i = 0; i < RPM; ++i) {
-          const int row = row0 + i * (kFwdThreads / CPR);
-          const u32x4 v = reg[(tt * 2 + mat) * RPM + i];
-          if (mat == 0) {
-            const int krow = (row & ~31) | krow_of_key(row & 31);
-            store_u32x4(dst + krow * D + 8 * k_chunk<CPR>(krow, ch), v);
-          } else {
-            store_u32x4(dst + row * D + 8 * v_chunk<CPR>(row, ch), v);
-          }
-        }
-      }
-    }
-    if (wave < 2) {
-      const uint64_t m = __ballot(preg >= 0);
-      if (lane == 0) s_valid[stage][wave] = m;
-    }
+  // position of this lane's key in global tile T (cache tiles; -1 = free or past the end)
+  auto load_pos = [&](int T) __attribute__((always_inline)) {
+    const int key = T * kKT + lane;
+    const int p = pos_head[min(key, M - 1)];
+    return key < n_cache ? p : -1;
   };
 
-  // per-lane parts of the transpose-read addresses (see the V^T operand below)
-  const int tr_j = lane & 15, tr_r = tr_j >> 2, tr_q = tr_j & 3, tr_dg = (lane >> 4) & 1;
-
-  if (n_pairs > 0) {
-    load_pair(0);
-    store_pair(0);
-    if (n_pairs > 1) load_pair(1);
+  // ---- LDS fragment addresses (bytes from the group's slot 0)
+  uint32_t k_rd[DS], v_rd[DB];
+  {
+#pragma unroll
+    for (int st = 0; st < DS; ++st) k_rd[st] = col * RB + 16 * k_chunk<CPR>(col, 2 * st + hf);
+    const int tr_j = lane & 15, tr_r = tr_j >> 2, tr_q = tr_j & 3, tr_dg = (lane >> 4) & 1;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d = db * 32 + tr_dg * 16 + 4 * tr_q;
+      v_rd[db] = (16 * hf + tr_r) * RB + 16 * v_chunk<CPR>(tr_r, d >> 3) + 2 * (d & 7);
+    }
   }
-  __syncthreads();
-  for (int p = 0; p < n_pairs; ++p) {
-    const int stage = p & 1;
-    const int t = 2 * p + grp;
-    const bool is_cache = t < n_ct;
-    const int base = is_cache ? t * kKT : (t - n_ct) * kKT;
-    const bool work = active && t < n_tiles && (is_cache || base <= qb * 32 + 31);
-    if (work) {
-      const bf16_t* Kt = lds + ((stage * 2 + grp) * 2 + 0) * TILE;
-      const bf16_t* Vt = lds + ((stage * 2 + grp) * 2 + 1) * TILE;
-      f32x16 s0 = zero16(), s1 = zero16();
+
+  // S^T of one tile: register r of a0 (a1) <-> key 16(l/32) + r (+32)
+  auto qk = [&](int slot, f32x16& a0, f32x16& a1) __attribute__((always_inline)) {
+    const char* kt = lds_k + slot * TB;
+    a0 = zero16();
+    a1 = zero16();
 #pragma unroll
-      for (int st = 0; st < DS; ++st) {
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(Kt + col * D + 8 * k_chunk<CPR>(col, 2 * st + hf));
-        const bf16x8 a1 =
-            *reinterpret_cast<const bf16x8*>(Kt + (32 + col) * D + 8 * k_chunk<CPR>(32 + col, 2 * st + hf));
-        s0 = mfma32x32x16(a0, qf[st], s0);
-        s1 = mfma32x32x16(a1, qf[st], s1);
-      }
-      const uint64_t vm = s_valid[stage][grp];
-      const bool causal = !is_cache && (base + kKT - 1 > qb * 32);
-      if (vm != ~0ull || causal) {
-        const uint32_t bits0 = static_cast<uint32_t>(vm >> (16 * hf)) & 0xffffu;
-        const uint32_t bits1 = static_cast<uint32_t>(vm >> (32 + 16 * hf)) & 0xffffu;
-        const int lim_i = causal ? qi - base - 16 * hf : 1 << 30;   // key offset bound
+    for (int st = 0; st < DS; ++st) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + k_rd[st]);
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(kt + 32 * RB + k_rd[st]);
+      a0 = mfma32x32x16(ka, qf[st], a0);
+      a1 = mfma32x32x16(kb, qf[st], a1);
+    }
+  };
+  // O^T += V^T P^T; MFMA (kb,u) covers keys 32kb + 16(l/32) + 8u + e.  The A
+  // operand V^T comes from two transpose reads: lane j = 4r + q of a 16-lane
+  // group addresses V[key0 + r][d0 + 4q .. +4).
+  auto pv = [&](int slot, const bf16x8 (&pb)[4]) __attribute__((always_inline)) {
+    const char* vt = lds_v + slot * TB;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool ok0 = ((bits0 >> r) & 1u) && (r <= lim_i);
-          const bool ok1 = ((bits1 >> r) & 1u) && (32 + r <= lim_i);
-          s0[r] = ok0 ? s0[r] : kNegInf;
-          s1[r] = ok1 ? s1[r] : kNegInf;
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const char* p = vt + v_rd[db] + (32 * kb + 8 * u) * RB;
+          const bf16x4 h0 = lds_read_tr16(reinterpret_cast<const bf16_t*>(p));
+          const bf16x4 h1 = lds_read_tr16(reinterpret_cast<const bf16_t*>(p + 4 * RB));
+          const bf16x8 a = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[db] = mfma32x32x16(a, pb[2 * kb + u], o[db]);
         }
-      }
-      float mx = kNegInf;
+  };
+  // probabilities of the current tile against the running maximum
+  auto softmax = [&](const f32x16& a0, const f32x16& a1, bf16x8 (&pb)[4]) __attribute__((always_inline)) {
+    f32x8 t[4];
+    float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-      mx = fmaxf(mx, xor32(mx));
-      const float m_new = fmaxf(m_run, mx * c2);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float rs = 0.f;
+    for (int r = 0; r < 16; ++r) {
+      const float p0 = fast_exp2(fmaf(a0[r], c2, -m_run));
+      const float p1 = fast_exp2(fmaf(a1[r], c2, -m_run));
+      t[r >> 3][r & 7] = p0;
+      t[2 + (r >> 3)][r & 7] = p1;
+      rs0 += p0;
+      rs1 += p1;
+    }
+    l_run += rs0 + rs1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pb[i] = to_bf16x8(t[i]);
+  };
+  // masks global tile T's scores, then moves the running maximum (and
+  // rescales O and l) only if some score exceeds it by the slack
+  auto mask_and_check = [&](f32x16& a0, f32x16& a1, int T, int posv) __attribute__((always_inline)) {
+    const bool exists = T < n_tiles;
+    const bool is_cache = T < n_ct;
+    const int base = is_cache ? T * kKT : (T - n_ct) * kKT;
+    uint64_t vm;
+    if (!exists) {
+      vm = 0;
+    } else if (is_cache) {
+      vm = __ballot(posv >= 0);
+    } else {
+      const int n = S - base;
+      vm = n >= 64 ? ~0ull : ((1ull << n) - 1);
+    }
+    const bool causal = exists && !is_cache && (base + kKT - 1 > qb * 32);
+    if (vm != ~0ull || causal) {
+      const uint32_t bits0 = static_cast<uint32_t>(vm >> (16 * hf)) & 0xffffu;
+      const uint32_t bits1 = static_cast<uint32_t>(vm >> (32 + 16 * hf)) & 0xffffu;
+      const int lim_i = causal ? qi - base - 16 * hf : (1 << 30);   // key offset bound
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        s0[r] = fast_exp2(fmaf(s0[r], c2, -m_use));
-        s1[r] = fast_exp2(fmaf(s1[r], c2, -m_use));
-        rs += s0[r] + s1[r];
-      }
-      l_run = fmaf(l_run, alpha, rs);
-      m_run = m_new;
-      if (__ballot(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      }
-      // O^T += V^T P^T; MFMA (kb,u) covers keys 32kb + 16(l/32) + 8u + e.  The
-      // A operand V^T comes from two transpose reads: lane j = 4r + q of a
-      // 16-lane group addresses V[key0 + r][d0 + 4q .. +4).
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const f32x16& sv = kb ? s1 : s0;
-          f32x8 pv;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pv[e] = sv[8 * u + e];
-          const bf16x8 pb = to_bf16x8(pv);
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const int d = db * 32 + tr_dg * 16 + 4 * tr_q;
-            bf16x4 h0, h1;
-#pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2) {
-              const int key = kb * 32 + 16 * hf + 8 * u + 4 * t2 + tr_r;
-              const bf16x4 v = lds_read_tr16(Vt + key * D + 8 * v_chunk<CPR>(key, d >> 3) + (d & 7));
-              if (t2 == 0) h0 = v; else h1 = v;
-            }
-            const bf16x8 a = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
-            o[db] = mfma32x32x16(a, pb, o[db]);
-          }
-        }
+        const bool ok0 = ((bits0 >> r) & 1u) && (r <= lim_i);
+        const bool ok1 = ((bits1 >> r) & 1u) && (32 + r <= lim_i);
+        a0[r] = ok0 ? a0[r] : kNegInf;
+        a1[r] = ok1 ? a1[r] : kNegInf;
       }
     }
-    // stage the next pair into the other buffer, prefetch the one after
-    if (p + 1 < n_pairs) store_pair(stage ^ 1);
-    if (p + 2 < n_pairs) load_pair(p + 2);
+    // v_maximum3_f32 (NaN-propagating; masked entries are -inf, never NaN)
+    float mx = __builtin_elementwise_maximum(a0[0], a1[0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(a0[r], a1[r]));
+    if (__ballot(mx * c2 > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, fmaxf(mx, xor32(mx)) * c2);
+      const float alpha = fast_exp2(m_run - m_new);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+  };
+
+  // ---- prologue: V slots zeroed (a masked tile multiplies P = 0 with
+  // whatever its slot holds, which must be finite), K and V of the group's
+  // tiles 0 and 1, scores of tile 0
+  {
+    u32x4* vz = reinterpret_cast<u32x4*>(lds + 4 * TB);
+#pragma unroll
+    for (int i = 0; i < 4 * TB / 16 / kFwdThreads; ++i) vz[i * kFwdThreads + tid] = u32x4{0, 0, 0, 0};
     __syncthreads();
+  }
+  f32x16 sc0, sc1;
+  int pos_n;
+  {
+    const int pos0 = load_pos(grp);
+    pos_n = load_pos(2 + grp);
+    issue_k(grp, 0);
+    issue_k(2 + grp, 1);
+    issue_v(grp, 0);
+    issue_v(2 + grp, 1);
+    wait_vmem_all();
+    __syncthreads();
+    qk(0, sc0, sc1);
+    mask_and_check(sc0, sc1, grp, pos0);
+    __syncthreads();
+    issue_k(4 + grp, 0);
+  }
+  // Iteration t: softmax(t), S^T of tile t+1 (K slot (t+1)&1), O += PV of
+  // tile t (V slot t&1), mask and check tile t+1.  Then, behind one barrier,
+  // K of tile t+3 and V of tile t+2 are fetched into the slots just read.
+  auto iteration = [&](int t, auto par) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
+    bf16x8 pb[4];
+    softmax(sc0, sc1, pb);
+    f32x16 sn0, sn1;
+    qk(P ^ 1, sn0, sn1);
+    pv(P, pb);
+    mask_and_check(sn0, sn1, 2 * (t + 1) + grp, pos_n);
+    sc0 = sn0;
+    sc1 = sn1;
+    wait_vmem_all();
+    __syncthreads();
+    pos_n = load_pos(2 * (t + 2) + grp);
+    issue_k(2 * (t + 3) + grp, P ^ 1);
+    issue_v(2 * (t + 2) + grp, P);
+  };
+  for (int t = 0; t < n_iter; t += 2) {
+    iteration(t, std::integral_constant<int, 0>{});
+    iteration(t + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- merge the two groups' softmax states (group 1 -> LDS -> group 0)
+  wait_vmem_all();
+  __syncthreads();
   float* xch = reinterpret_cast<float*>(lds);            // [DB*16 + 2][kRowBlocks*64]
   const int slot = rbw * 64 + lane;
   constexpr int NX = kRowBlocks * 64;
@@ -316,8 +403,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
     const float m1 = xch[(DB * 16) * NX + slot];
     const float l1 = xch[(DB * 16 + 1) * NX + slot];
     const float m = fmaxf(m_run, m1);
-    const float mu = (m == kNegInf) ? 0.f : m;
-    const float a0 = fast_exp2(m_run - mu), a1 = fast_exp2(m1 - mu);
+    const float a0 = fast_exp2(m_run - m), a1 = fast_exp2(m1 - m);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll

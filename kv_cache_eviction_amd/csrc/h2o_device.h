@@ -39,6 +39,25 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const bf16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
 }
 
+// Raw buffer resource over [base, base + bytes) (gfx9 word 3): a load whose
+// offset falls past `bytes` returns zeros instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+// buffer_load_dwordx4 ... lds: lane i copies the 16 bytes at voff + soff of
+// the resource to LDS address lds_base + 16 i (lds_base wave-uniform).  The
+// compiler does not track these writes: wait with vmcnt(0) and a barrier
+// before any wave reads the destination.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds_base, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)(const_cast<void*>(lds_base)), 16, voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
 __device__ __forceinline__ bf16x8 load_bf16x8(const bf16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
