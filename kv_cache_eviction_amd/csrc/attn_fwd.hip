@@ -180,7 +180,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
     return key < n ? off : off - static_cast<uint32_t>(key - n + 1) * RB;
   };
   auto issue_k = [&](int T, int slot) __attribute__((always_inline)) {
-    if (T >= n_tiles) return;
+    T = min(T, n_tiles - 1);          // past the end: reload the last tile (masked)
     const bool is_cache = T < n_ct;
     const int base = is_cache ? T * kKT : (T - n_ct) * kKT;
     const int n = (is_cache ? n_cache : S) - base;
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
     }
   };
   auto issue_v = [&](int T, int slot) __attribute__((always_inline)) {
-    if (T >= n_tiles) return;
+    T = min(T, n_tiles - 1);          // past the end: reload the last tile (masked)
     const bool is_cache = T < n_ct;
     const int base = is_cache ? T * kKT : (T - n_ct) * kKT;
     const int n = (is_cache ? n_cache : S) - base;
@@ -290,9 +290,17 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) pb[i] = to_bf16x8(t[i]);
   };
-  // masks global tile T's scores, then moves the running maximum (and
-  // rescales O and l) only if some score exceeds it by the slack
-  auto mask_and_check = [&](f32x16& a0, f32x16& a1, int T, int posv) __attribute__((always_inline)) {
+  // largest raw score of the lane's 32 entries (v_maximum3_f32; NaN-propagating)
+  auto tile_max = [&](const f32x16& a0, const f32x16& a1) __attribute__((always_inline)) {
+    float mx = __builtin_elementwise_maximum(a0[0], a1[0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(a0[r], a1[r]));
+    return mx;
+  };
+  // masks global tile T's scores (then the maximum mx of the raw scores is
+  // recomputed over the visible ones), and moves the running maximum (with
+  // O and l rescaled) only if some score exceeds it by the slack
+  auto mask_and_check = [&](f32x16& a0, f32x16& a1, float mx, int T, int posv) __attribute__((always_inline)) {
     const bool exists = T < n_tiles;
     const bool is_cache = T < n_ct;
     const int base = is_cache ? T * kKT : (T - n_ct) * kKT;
@@ -317,11 +325,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
         a0[r] = ok0 ? a0[r] : kNegInf;
         a1[r] = ok1 ? a1[r] : kNegInf;
       }
+      mx = tile_max(a0, a1);
     }
-    // v_maximum3_f32 (NaN-propagating; masked entries are -inf, never NaN)
-    float mx = __builtin_elementwise_maximum(a0[0], a1[0]);
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(a0[r], a1[r]));
     if (__ballot(mx * c2 > m_run + kRescaleSlack)) {
       const float m_new = fmaxf(m_run, fmaxf(mx, xor32(mx)) * c2);
       const float alpha = fast_exp2(m_run - m_new);
@@ -334,53 +339,86 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
     }
   };
 
-  // ---- prologue: V slots zeroed (a masked tile multiplies P = 0 with
-  // whatever its slot holds, which must be finite), K and V of the group's
-  // tiles 0 and 1, scores of tile 0
-  {
-    u32x4* vz = reinterpret_cast<u32x4*>(lds + 4 * TB);
-#pragma unroll
-    for (int i = 0; i < 4 * TB / 16 / kFwdThreads; ++i) vz[i * kFwdThreads + tid] = u32x4{0, 0, 0, 0};
-    __syncthreads();
-  }
+  // ---- prologue: K and V of the group's tiles 0 and 1, scores of tile 0.
+  // Every slot receives a real tile before its first use (tile indices past
+  // the end reload the last tile, masked), so masked P = 0 always meets
+  // finite V.
   f32x16 sc0, sc1;
-  int pos_n;
-  {
-    const int pos0 = load_pos(grp);
-    pos_n = load_pos(2 + grp);
-    issue_k(grp, 0);
-    issue_k(2 + grp, 1);
-    issue_v(grp, 0);
-    issue_v(2 + grp, 1);
-    wait_vmem_all();
-    __syncthreads();
-    qk(0, sc0, sc1);
-    mask_and_check(sc0, sc1, grp, pos0);
-    __syncthreads();
-    issue_k(4 + grp, 0);
-  }
-  // Iteration t: softmax(t), S^T of tile t+1 (K slot (t+1)&1), O += PV of
-  // tile t (V slot t&1), mask and check tile t+1.  Then, behind one barrier,
-  // K of tile t+3 and V of tile t+2 are fetched into the slots just read.
-  auto iteration = [&](int t, auto par) __attribute__((always_inline)) {
-    constexpr int P = decltype(par)::value;
-    bf16x8 pb[4];
-    softmax(sc0, sc1, pb);
+  bf16x8 pb[4];
+  const int pos0 = load_pos(grp);
+  int pos1 = load_pos(2 + grp);
+  issue_k(grp, 0);
+  issue_k(2 + grp, 1);
+  issue_v(grp, 0);
+  issue_v(2 + grp, 1);
+  wait_vmem_all();
+  __syncthreads();
+  qk(0, sc0, sc1);
+  __syncthreads();
+  issue_k(4 + grp, 0);
+
+  // Ping-pong: iteration t has an MFMA phase M(t) = {S^T of tile t+1 from K
+  // slot (t+1)&1, O += PV of tile t from V slot t&1} and a VALU phase
+  // V(t') = {mask, check and softmax of tile t'} producing P(t').  Group 0
+  // runs M(t) then V(t+1); group 1 runs V(t) then M(t), one phase behind, so
+  // that of the two waves sharing a SIMD one issues MFMAs while the other
+  // does the softmax.  A barrier separates the phases.  Each wave issues the
+  // same number of loads per iteration (position + K and V tile copies), so
+  // a fixed vmcnt waits for exactly the previous iteration's copies: after
+  // its MFMA phase a group fetches K of tile t+3 and V of tile t+2 into the
+  // slots it just read, three phases before their use.
+  constexpr int kLoadsPerIter = 1 + 2 * NDMA;
+  constexpr int kWaitPrev = 0x0f70 | (kLoadsPerIter & 15) | ((kLoadsPerIter >> 4) << 14);
+  auto m_phase = [&](int P) __attribute__((always_inline)) {
     f32x16 sn0, sn1;
     qk(P ^ 1, sn0, sn1);
     pv(P, pb);
-    mask_and_check(sn0, sn1, 2 * (t + 1) + grp, pos_n);
     sc0 = sn0;
     sc1 = sn1;
-    wait_vmem_all();
-    __syncthreads();
-    pos_n = load_pos(2 * (t + 2) + grp);
-    issue_k(2 * (t + 3) + grp, P ^ 1);
-    issue_v(2 * (t + 2) + grp, P);
   };
-  for (int t = 0; t < n_iter; t += 2) {
-    iteration(t, std::integral_constant<int, 0>{});
-    iteration(t + 1, std::integral_constant<int, 1>{});
+  auto v_phase = [&](int T, int posv) __attribute__((always_inline)) {
+    mask_and_check(sc0, sc1, tile_max(sc0, sc1), T, posv);
+    softmax(sc0, sc1, pb);
+  };
+  // Two loops (one per group, same barrier count) so that each carries only
+  // its own state across iterations: group 0 P, group 1 S.
+  if (grp == 0) {
+    v_phase(0, pos0);                 // P(0)
+    int pos_n = pos1;                 // position of tile t+1
+    auto iteration = [&](int t, auto par) __attribute__((always_inline)) {
+      constexpr int P = decltype(par)::value;
+      m_phase(P);
+      __syncthreads();
+      const int pn = load_pos(2 * (t + 2));
+      issue_k(2 * (t + 3), P ^ 1);
+      issue_v(2 * (t + 2), P);
+      v_phase(2 * (t + 1), pos_n);
+      pos_n = pn;
+      __builtin_amdgcn_s_waitcnt(kWaitPrev);
+      __syncthreads();
+    };
+    for (int t = 0; t < n_iter; t += 2) {
+      iteration(t, std::integral_constant<int, 0>{});
+      iteration(t + 1, std::integral_constant<int, 1>{});
+    }
+  } else {
+    int pos_c = pos0, pos_n = pos1;   // positions of tiles t and t+1
+    auto iteration = [&](int t, auto par) __attribute__((always_inline)) {
+      constexpr int P = decltype(par)::value;
+      v_phase(2 * t + 1, pos_c);
+      __builtin_amdgcn_s_waitcnt(kWaitPrev);
+      __syncthreads();
+      m_phase(P);
+      __syncthreads();
+      pos_c = pos_n;
+      pos_n = load_pos(2 * (t + 2) + 1);
+      issue_k(2 * (t + 3) + 1, P ^ 1);
+      issue_v(2 * (t + 2) + 1, P);
+    };
+    for (int t = 0; t < n_iter; t += 2) {
+      iteration(t, std::integral_constant<int, 0>{});
+      iteration(t + 1, std::integral_constant<int, 1>{});
+    }
   }
 
   // ---- merge the two groups' softmax states (group 1 -> LDS -> group 0)
