@@ -187,11 +187,14 @@ H2O_API int64_t h2o_tokens_seen(const h2o_cache* c);
 H2O_API h2o_status h2o_device_status(h2o_cache* c, void* stream, int32_t* flags);
 
 /* Per-kernel timing with HIP events recorded on the launch stream around
- * every kernel launch while enabled.  Kernel ids: 0 attention forward,
- * 1 score accumulation, 2 eviction select, 3 state reset, 4 K/V scatter.
- * h2o_get_timing synchronises on the last recorded event and returns the
- * summed milliseconds and launch count since timing was enabled. */
-H2O_API h2o_status h2o_set_timing(h2o_cache* c, int32_t enable);
+ * the launches of the kernels selected by `kernel_mask` (bit k = kernel id
+ * k; -1 = all, 0 = off).  Kernel ids: 0 attention forward, 1 score
+ * accumulation, 2 eviction select, 3 state reset, 4 K/V scatter.  Each
+ * bracketed launch adds two event records to the stream, so select only
+ * the kernels of interest when the step time matters.  h2o_get_timing
+ * synchronises on the last recorded event and returns the summed
+ * milliseconds and launch count since timing was enabled. */
+H2O_API h2o_status h2o_set_timing(h2o_cache* c, int32_t kernel_mask);
 H2O_API h2o_status h2o_get_timing(h2o_cache* c, int32_t kernel_id, double* total_ms,
                           int64_t* launches);
 

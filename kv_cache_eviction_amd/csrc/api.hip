@@ -64,7 +64,7 @@ struct h2o_cache {
   int64_t T;
   int filled;          // slots [0, filled) hold tokens, the rest are free; -1: unknown (adopted)
   int32_t last_hip_error;
-  bool timing;
+  uint32_t timing_mask;      // bit k: bracket kernel id k with events
   std::vector<TimedLaunch> pending;
   std::vector<hipEvent_t> event_pool;
   double total_ms[kTimedKernels];
@@ -88,7 +88,7 @@ hipEvent_t take_event(h2o_cache* c) {
 template <class F>
 h2o_status timed(h2o_cache* c, int kid, hipStream_t st, F&& launch) {
   hipEvent_t a = nullptr, b = nullptr;
-  if (c && c->timing) {
+  if (c && ((c->timing_mask >> kid) & 1u)) {
     a = take_event(c);
     b = take_event(c);
     if (a && b && hipEventRecord(a, st) != hipSuccess) {
@@ -218,7 +218,7 @@ h2o_status h2o_cache_init(const h2o_config* cfg, void* k_cache, void* v_cache, f
   c->T = tokens_seen;
   c->filled = adopt ? -1 : 0;
   c->last_hip_error = 0;
-  c->timing = false;
+  c->timing_mask = 0;
   for (int i = 0; i < kTimedKernels; ++i) {
     c->total_ms[i] = 0.0;
     c->launches[i] = 0;
@@ -295,9 +295,9 @@ h2o_status h2o_device_status(h2o_cache* c, void* stream, int32_t* flags) {
   return H2O_OK;
 }
 
-h2o_status h2o_set_timing(h2o_cache* c, int32_t enable) {
+h2o_status h2o_set_timing(h2o_cache* c, int32_t kernel_mask) {
   if (!c) return H2O_ERR_NULL;
-  c->timing = enable != 0;
+  c->timing_mask = static_cast<uint32_t>(kernel_mask);
   return H2O_OK;
 }
 

@@ -14,11 +14,25 @@
 // partials of a column in split order, so the result is deterministic.
 //
 // bf16 path: S = Q K^T on v_mfma_f32_32x32x16_bf16 with the wave's 64 keys
-// as the B operand held in registers for the whole kernel and 64-row query
-// blocks as the A operand, staged in a double-buffered LDS ring shared by
-// the 4 waves and prefetched two blocks ahead through registers.  Each
-// accumulator column belongs to one key, so the column sum is one fp32 add
-// per element inside the lane plus one exchange with lane l^32 at the end.
+// as the B operand held in registers for the whole kernel; 64-row query
+// blocks are the A operand, each 16-byte fragment read from LDS feeding two
+// MFMAs (the wave's two 32-key halves).  Each accumulator column belongs to
+// one key, so the column sum is one fp32 add per element inside the lane
+// plus one exchange with lane l^32 at the end.
+//   * Rows: a cache-key tile takes every (query head, query) row of the KV
+//     group; a chunk-key tile only the rows whose query index reaches its
+//     first key, so no staged block is wasted.  Rows are numbered g * L + i
+//     over the needed queries and split into R contiguous ranges.
+//   * Query blocks reach LDS through direct copies (buffer_load ... lds)
+//     into a 3-stage ring, the row swizzle applied on the source side; the
+//     rows' lse values are staged one block ahead through registers.
+//   * Each 64-row block is computed in two 32-row halves, software
+//     pipelined: the MFMAs of the next half are issued beside the exp and
+//     column adds of the current one, with one barrier per block.
+//   * Blocks where some query of the block precedes some key of the wave
+//     take a masked variant; all others no per-element test.
+#include <type_traits>
+
 #include "h2o_device.h"
 #include "h2o_launch.h"
 
@@ -27,7 +41,11 @@ namespace {
 
 constexpr int kCT = 256;        // key columns per workgroup (4 waves x 64)
 constexpr int kRB = 64;         // query rows per staged block (2 MFMA row blocks)
+constexpr int kStages = 3;
 constexpr int kRowSplitsMax = 16;
+
+template <int CPR>
+__device__ __forceinline__ int q_chunk(int row, int c) { return c ^ (row & (CPR - 1)); }
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
@@ -36,15 +54,18 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
     float* __restrict__ partial, int Hq, int Hkv, int S, int M, int n_cache, float c2,
     int n_heads, int n_ct, int n_tiles, int R) {
   constexpr int DS = D / 16;
-  constexpr int QLD = D + 8;
   constexpr int CPR = D / 8;
-  constexpr int NCH = kRB * CPR / 256;  // 16-byte chunks per thread per row block
-  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][kRB * QLD];
-  __shared__ __attribute__((aligned(16))) float s_lse2[2][kRB];
-  __shared__ __attribute__((aligned(16))) int s_irow[2][kRB];
+  constexpr int RBY = 2 * D;                  // bytes per query row
+  constexpr int BLK = kRB * RBY;              // bytes per staged block
+  constexpr int NDMA = BLK / 1024 / 4;        // 1 KB copies per wave per block
+  __shared__ __attribute__((aligned(1024))) char qs[kStages * BLK];
+  __shared__ __attribute__((aligned(16))) float s_l2[kStages][kRB];
+  __shared__ __attribute__((aligned(16))) int s_qi[kStages][kRB];
+  __shared__ int s_min_qi[kStages];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int hf = lane >> 5, col = lane & 31;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, hf = lane >> 5, col = lane & 31;
   const int bh = blockIdx.x % n_heads;
   const int rest = static_cast<int>(blockIdx.x) / n_heads;
   const int tile = rest % n_tiles, split = rest / n_tiles;
@@ -71,125 +92,178 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
     }
   }
 
-  const int n_rows = G * S;
-  const int n_blk = (n_rows + kRB - 1) / kRB;
+  // needed rows: u = g * L + (i - i_off), i_off = 0 (cache tile) or base
+  const int i_off = is_cache ? 0 : base;
+  const int L = S - i_off;
+  const int n_need = G * L;
+  const int n_blk = (n_need + kRB - 1) / kRB;
   const int blk_lo = static_cast<int>(static_cast<int64_t>(split) * n_blk / R);
   const int blk_hi = static_cast<int>(static_cast<int64_t>(split + 1) * n_blk / R);
-  const bf16_t* qhead = Q + static_cast<size_t>(b * Hq + kvh * G) * S * D;  // rows g*S + i
+  const float invL = 1.f / static_cast<float>(L);
+  // row u (< n_need) -> row g * S + i of the group's Q / lse
+  auto row_of = [&](int u, int& i) __attribute__((always_inline)) {
+    int g = static_cast<int>(static_cast<float>(u) * invL);
+    g = g * L > u ? g - 1 : g;
+    g = (g + 1) * L <= u ? g + 1 : g;
+    i = i_off + (u - g * L);
+    return g * S + i;
+  };
+  const bf16_t* qhead = Q + static_cast<size_t>(b * Hq + kvh * G) * S * D;
   const float* lhead = lse + static_cast<size_t>(b * Hq + kvh * G) * S;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qhead, static_cast<uint32_t>(G) * S * RBY);
 
-  // A row block contributes to chunk keys only if one of its queries i >= base.
-  auto block_needed = [&](int blk) __attribute__((always_inline)) {
-    if (is_cache) return true;
-    const int r0 = blk * kRB, r1 = min(r0 + kRB - 1, n_rows - 1);
-    if (r0 / S != r1 / S) return true;
-    return (r1 % S) >= base;
-  };
-  auto next_needed = [&](int blk) __attribute__((always_inline)) {
-    ++blk;
-    while (blk < blk_hi && !block_needed(blk)) ++blk;
-    return blk;
-  };
-
-  struct Stage {
-    u32x4 q[NCH];
-    float l;
-    int i;
-  };
-  auto load_blk = [&](int blk, Stage& s) __attribute__((always_inline)) {
-    const int r0 = blk * kRB;
+  // copies of block bk into stage stg: LDS byte 1024 j' + 16 i (j' = wave NDMA
+  // + j) is row r, physical chunk c' of the block; the lane fetches that row's
+  // logical chunk c' ^ (r mod CPR)
+  auto issue_blk = [&](int bk, int stg) __attribute__((always_inline)) {
+    constexpr int RK = 1024 / RBY;            // rows per 1 KB copy
+    const char* dst = qs + stg * BLK + wave * NDMA * 1024;
+    const int r0 = wave * NDMA * RK + lane / CPR, cp = lane % CPR;
+    const int u0 = bk * kRB + r0;
+    int i0;
+    const int row0 = row_of(min(u0, n_need - 1), i0);
+    const int row_last = (n_need - 1) / L * S + i_off + (n_need - 1) % L;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int idx = c * 256 + tid, row = idx / CPR, dc = idx % CPR;
-      // rows past the end read the last row; their lse of +inf zeroes them
-      const int r = min(r0 + row, n_rows - 1);
-      s.q[c] = load_u32x4(qhead + static_cast<size_t>(r) * D + dc * 8);
-    }
-    if (tid < kRB) {
-      const int r = r0 + tid;
-      const float lv = lhead[min(r, n_rows - 1)];
-      s.l = (r < n_rows) ? lv * kLog2e : __builtin_huge_valf();
-      s.i = (r < n_rows) ? r % S : -1;
+    for (int j = 0; j < NDMA; ++j) {
+      const int r = r0 + j * RK, u = u0 + j * RK;
+      int row;
+      if (L >= kRB) {               // rows of a block cross at most one head boundary
+        const int i = i0 + j * RK;
+        row = row0 + j * RK + (i >= S ? S - L : 0);
+      } else {
+        int i;
+        row = row_of(min(u, n_need - 1), i);
+      }
+      row = u < n_need ? row : row_last;
+      dma16(rq, dst + j * 1024, static_cast<uint32_t>(row) * RBY + 16 * q_chunk<CPR>(r, cp), 0);
     }
   };
-  auto store_blk = [&](const Stage& s, int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int idx = c * 256 + tid, row = idx / CPR, dc = idx % CPR;
-      store_u32x4(&Qs[buf][row * QLD + dc * 8], s.q[c]);
-    }
+  // lse (log2 domain) and query index of row tid of block bk; rows past the
+  // end get +inf (P = 0)
+  struct RowInfo {
+    float l2;
+    int qi;
+  };
+  auto load_rows = [&](int bk) __attribute__((always_inline)) {
+    RowInfo ri{__builtin_huge_valf(), 1 << 30};
     if (tid < kRB) {
-      s_lse2[buf][tid] = s.l;
-      s_irow[buf][tid] = s.i;
+      const int u = bk * kRB + tid;
+      int i;
+      const int row = row_of(min(u, n_need - 1), i);
+      const float lv = lhead[row];
+      ri.l2 = u < n_need ? lv * kLog2e : __builtin_huge_valf();
+      ri.qi = u < n_need ? i : (1 << 30);
+    }
+    return ri;
+  };
+  auto store_rows = [&](const RowInfo& ri, int stg) __attribute__((always_inline)) {
+    if (tid < kRB) {
+      s_l2[stg][tid] = ri.l2;
+      s_qi[stg][tid] = ri.qi;
+      int mn = ri.qi;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) mn = min(mn, __shfl_xor(mn, o));
+      if (tid == 0) s_min_qi[stg] = mn;
     }
   };
 
+  // per-lane LDS offsets of the A-operand fragments (row 32h + col, logical chunk 2st + hf)
+  uint32_t q_rd[DS];
+#pragma unroll
+  for (int st = 0; st < DS; ++st) q_rd[st] = col * RBY + 16 * q_chunk<CPR>(col, 2 * st + hf);
+
+  auto mfma_half = [&](int stg, int h, f32x16& a0, f32x16& a1) __attribute__((always_inline)) {
+    const char* qb = qs + stg * BLK + h * 32 * RBY;
+    a0 = zero16();
+    a1 = zero16();
+#pragma unroll
+    for (int st = 0; st < DS; ++st) {
+      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qb + q_rd[st]);
+      a0 = mfma32x32x16(qa, kf[0][st], a0);
+      a1 = mfma32x32x16(qa, kf[1][st], a1);
+    }
+  };
   float cs0 = 0.f, cs1 = 0.f;     // column sums of this lane's two key columns
-  // Ping-pong register stages: while block `cur` is computed from LDS buffer
-  // `buf`, one stage holds block n1 (stored to the other buffer after the
-  // MFMAs) and the other block n2; each stage's loads get two blocks of
-  // compute to land.
-  Stage st0, st1;
-  int cur = next_needed(blk_lo - 1);
-  int n1 = cur < blk_hi ? next_needed(cur) : blk_hi;
-  int n2 = n1 < blk_hi ? next_needed(n1) : blk_hi;
-  if (cur < blk_hi) {
-    load_blk(cur, st0);
-    store_blk(st0, 0);
-  }
-  if (n1 < blk_hi) load_blk(n1, st0);
-  if (n2 < blk_hi) load_blk(n2, st1);
-  __syncthreads();
-  int buf = 0;
-  auto iter = [&](Stage& st) __attribute__((always_inline)) {
-    if (key0 < lim) {
+  // accumulator register r of lane l: row 32h + 8(r/4) + 4hf + r%4 of the
+  // block; the 4 rows of each group of 4 registers are consecutive
+  auto valu_half = [&](const f32x16& a0, const f32x16& a1, int stg, int h, auto masked) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        f32x16 a0 = zero16(), a1 = zero16();
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int row0 = h * 32 + 8 * a4 + 4 * hf;
+      const f32x4 l2v = *reinterpret_cast<const f32x4*>(&s_l2[stg][row0]);
+      int4 qiv = {0, 0, 0, 0};
+      if (MASKED) qiv = *reinterpret_cast<const int4*>(&s_qi[stg][row0]);
 #pragma unroll
-        for (int q = 0; q < DS; ++q) {
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(
-              &Qs[buf][(half * 32 + col) * QLD + 16 * q + 8 * hf]);
-          a0 = mfma32x32x16(qa, kf[0][q], a0);
-          a1 = mfma32x32x16(qa, kf[1][q], a1);
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * a4 + e;
+        float p0 = fast_exp2(fmaf(a0[r], c2, -l2v[e]));
+        float p1 = fast_exp2(fmaf(a1[r], c2, -l2v[e]));
+        if (MASKED) {
+          const int qi = e == 0 ? qiv.x : e == 1 ? qiv.y : e == 2 ? qiv.z : qiv.w;
+          p0 = (key0 + col <= qi) ? p0 : 0.f;
+          p1 = (key0 + 32 + col <= qi) ? p1 : 0.f;
         }
-        // accumulator register r of lane l: query row 8(r/4) + 4hf + r%4 of this half block;
-        // the 4 rows of each group of 4 registers are consecutive (one 16-byte LDS read)
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const int row0 = half * 32 + 8 * a4 + 4 * hf;
-          const f32x4 l2v = *reinterpret_cast<const f32x4*>(&s_lse2[buf][row0]);
-          int4 qiv = {0, 0, 0, 0};
-          if (!is_cache) qiv = *reinterpret_cast<const int4*>(&s_irow[buf][row0]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * a4 + e;
-            float p0 = fast_exp2(fmaf(a0[r], c2, -l2v[e]));
-            float p1 = fast_exp2(fmaf(a1[r], c2, -l2v[e]));
-            if (!is_cache) {
-              const int qi = e == 0 ? qiv.x : e == 1 ? qiv.y : e == 2 ? qiv.z : qiv.w;
-              p0 = (key0 + col <= qi) ? p0 : 0.f;
-              p1 = (key0 + 32 + col <= qi) ? p1 : 0.f;
-            }
-            cs0 += p0;
-            cs1 += p1;
-          }
-        }
+        cs0 += p0;
+        cs1 += p1;
       }
     }
-    if (n1 < blk_hi) store_blk(st, buf ^ 1);      // st holds block n1
-    const int n3 = n2 < blk_hi ? next_needed(n2) : blk_hi;
-    if (n3 < blk_hi) load_blk(n3, st);             // st now carries block n3
-    __syncthreads();
-    cur = n1;
-    n1 = n2;
-    n2 = n3;
-    buf ^= 1;
   };
-  while (cur < blk_hi) {
-    iter(st0);
-    if (cur >= blk_hi) break;
-    iter(st1);
+  auto block_masked = [&](int stg) __attribute__((always_inline)) {
+    return !is_cache && __builtin_amdgcn_readfirstlane(s_min_qi[stg]) < key0 + 63;
+  };
+
+  if (blk_lo < blk_hi) {
+    // prologue: blocks lo (stage 0) and lo + 1 (stage 1) in flight, rows of
+    // lo staged, MFMAs of lo's first half
+    issue_blk(blk_lo, 0);
+    if (blk_lo + 1 < blk_hi) issue_blk(blk_lo + 1, 1);
+    const RowInfo r0 = load_rows(blk_lo);
+    RowInfo rn = load_rows(blk_lo + 1);
+    wait_vmem_all();
+    store_rows(r0, 0);
+    __syncthreads();
+    f32x16 A0, A1, B0, B1;
+    mfma_half(0, 0, A0, A1);
+    int stg = 0;
+    bool masked = block_masked(0);
+    for (int bk = blk_lo; bk < blk_hi; ++bk) {
+      const int stg1 = stg == kStages - 1 ? 0 : stg + 1;
+      const int stg2 = stg1 == kStages - 1 ? 0 : stg1 + 1;
+      // second half's MFMAs beside the first half's exp and column sums
+      if (masked) {
+        mfma_half(stg, 1, B0, B1);
+        valu_half(A0, A1, stg, 0, std::true_type{});
+      } else {
+        mfma_half(stg, 1, B0, B1);
+        valu_half(A0, A1, stg, 0, std::false_type{});
+      }
+      // block bk+1 landed (copies and rows issued one block ago); then
+      // fetch block bk+2 into the stage block bk-1 used
+      wait_vmem_all();
+      if (bk + 1 < blk_hi) store_rows(rn, stg1);
+      __syncthreads();
+      if (bk + 2 < blk_hi) {
+        issue_blk(bk + 2, stg2);
+        rn = load_rows(bk + 2);
+      }
+      const bool masked_next = bk + 1 < blk_hi && block_masked(stg1);
+      // next block's first-half MFMAs beside this block's second half
+      if (bk + 1 < blk_hi) {
+        if (masked) {
+          mfma_half(stg1, 0, A0, A1);
+          valu_half(B0, B1, stg, 1, std::true_type{});
+        } else {
+          mfma_half(stg1, 0, A0, A1);
+          valu_half(B0, B1, stg, 1, std::false_type{});
+        }
+      } else {
+        if (masked) valu_half(B0, B1, stg, 1, std::true_type{});
+        else valu_half(B0, B1, stg, 1, std::false_type{});
+      }
+      masked = masked_next;
+      stg = stg1;
+    }
   }
   cs0 += xor32(cs0);
   cs1 += xor32(cs1);

@@ -243,8 +243,18 @@ def h2o_device_status(handle, stream=None) -> int:
     return flags.value
 
 
-def h2o_set_timing(handle, enable: bool):
-    _check(_lib.h2o_set_timing(handle, int(enable)), "h2o_set_timing")
+def h2o_set_timing(handle, kernels=True):
+    """Brackets the selected kernels' launches with HIP events: True (all),
+    False (none), or an iterable of kernel names / ids."""
+    if kernels is True:
+        mask = -1
+    elif kernels is False or kernels is None:
+        mask = 0
+    else:
+        mask = 0
+        for k in kernels:
+            mask |= 1 << (KERNEL_IDS[k] if isinstance(k, str) else int(k))
+    _check(_lib.h2o_set_timing(handle, mask), "h2o_set_timing")
 
 
 def h2o_get_timing(handle, kernel: str | int):
