@@ -95,7 +95,9 @@ typedef struct h2o_cache h2o_cache;   /* opaque host-side handle */
 /* Host only (no HIP call): H2O_OK if the config is usable.  Checks B, Hq, Hkv
  * >= 1, Hq % Hkv == 0, d in {64, 128}, dtype known, 1 <= max_chunk,
  * 1 <= max_prefill <= M, 0 <= W and M - W >= max_chunk (a reading of the pages:
- * with it every eviction finds enough candidates). */
+ * with it every eviction finds enough candidates), M, max_chunk and
+ * max_prefill <= 16384, (Hq / Hkv) * max(max_chunk, max_prefill) <= 2^20
+ * query rows per KV group, and every chunk tensor below 2^31 elements. */
 H2O_API h2o_status h2o_validate_config(const h2o_config* cfg);
 
 /* Host only: bytes of device workspace h2o_cache_init needs for `cfg`

@@ -186,6 +186,9 @@ h2o_status h2o_validate_config(const h2o_config* c) {
   if (static_cast<int64_t>(c->cache_slots) - c->recent_window < c->max_chunk) return H2O_ERR_CONFIG;
   if (c->max_chunk > 16384 || c->max_prefill > 16384) return H2O_ERR_CONFIG;
   if (!(c->softmax_scale == c->softmax_scale)) return H2O_ERR_CONFIG;   // NaN
+  // query rows of one KV group (G queries per chunk position) index with 24-bit arithmetic
+  if (static_cast<int64_t>(c->n_q_heads / c->n_kv_heads) * max_len(c) > (int64_t{1} << 20))
+    return H2O_ERR_CONFIG;
   // every tensor offset must fit in int64 and every chunk tensor below 2^31 elements
   const int64_t big = static_cast<int64_t>(c->batch) * c->n_q_heads * max_len(c) * c->head_dim;
   if (big >= (int64_t{1} << 31)) return H2O_ERR_CONFIG;

@@ -58,10 +58,13 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
   constexpr int RBY = 2 * D;                  // bytes per query row
   constexpr int BLK = kRB * RBY;              // bytes per staged block
   constexpr int NDMA = BLK / 1024 / 4;        // 1 KB copies per wave per block
-  __shared__ __attribute__((aligned(1024))) char qs[kStages * BLK];
+  // one array per stage: the compiler can then tell that a copy in flight
+  // into one stage does not alias the reads of another (and inserts no wait)
+  __shared__ __attribute__((aligned(1024))) char qs0[BLK];
+  __shared__ __attribute__((aligned(1024))) char qs1[BLK];
+  __shared__ __attribute__((aligned(1024))) char qs2[BLK];
   __shared__ __attribute__((aligned(16))) float s_l2[kStages][kRB];
   __shared__ __attribute__((aligned(16))) int s_qi[kStages][kRB];
-  __shared__ int s_min_qi[kStages];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -101,12 +104,16 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
   const int blk_hi = static_cast<int>(static_cast<int64_t>(split + 1) * n_blk / R);
   const float invL = 1.f / static_cast<float>(L);
   // row u (< n_need) -> row g * S + i of the group's Q / lse
+  // (u < G L <= 2^20 and every product stays below 2^24: 24-bit multiplies)
   auto row_of = [&](int u, int& i) __attribute__((always_inline)) {
     int g = static_cast<int>(static_cast<float>(u) * invL);
-    g = g * L > u ? g - 1 : g;
-    g = (g + 1) * L <= u ? g + 1 : g;
-    i = i_off + (u - g * L);
-    return g * S + i;
+    int rel = u - __mul24(g, L);
+    g = rel < 0 ? g - 1 : g;
+    rel = rel < 0 ? rel + L : rel;
+    g = rel >= L ? g + 1 : g;
+    rel = rel >= L ? rel - L : rel;
+    i = i_off + rel;
+    return __mul24(g, S) + i;
   };
   const bf16_t* qhead = Q + static_cast<size_t>(b * Hq + kvh * G) * S * D;
   const float* lhead = lse + static_cast<size_t>(b * Hq + kvh * G) * S;
@@ -115,55 +122,63 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
   // copies of block bk into stage stg: LDS byte 1024 j' + 16 i (j' = wave NDMA
   // + j) is row r, physical chunk c' of the block; the lane fetches that row's
   // logical chunk c' ^ (r mod CPR)
-  auto issue_blk = [&](int bk, int stg) __attribute__((always_inline)) {
-    constexpr int RK = 1024 / RBY;            // rows per 1 KB copy
-    const char* dst = qs + stg * BLK + wave * NDMA * 1024;
-    const int r0 = wave * NDMA * RK + lane / CPR, cp = lane % CPR;
+  // Per lane: its rows r0 + RK j, j < NDMA, of every block; the swizzled
+  // chunk of row r0 + RK j is c ^ (r mod CPR) = (its value for j = 0) with
+  // two bits flipped by j (CPR = 16) or unchanged (CPR = 8).
+  constexpr int RK = 1024 / RBY;              // rows per 1 KB copy
+  const int r0 = wave * NDMA * RK + lane / CPR;
+  const uint32_t chunk0 = 16 * q_chunk<CPR>(r0, lane % CPR);
+  const int row_last = (n_need - 1) / L * S + i_off + (n_need - 1) % L;
+  auto stage_buf = [&](auto stg) __attribute__((always_inline)) {
+    constexpr int SG = decltype(stg)::value;
+    return SG == 0 ? qs0 : SG == 1 ? qs1 : qs2;
+  };
+  auto issue_blk = [&](int bk, auto stg) __attribute__((always_inline)) {
+    const char* dst = stage_buf(stg) + wave * NDMA * 1024;
     const int u0 = bk * kRB + r0;
     int i0;
     const int row0 = row_of(min(u0, n_need - 1), i0);
-    const int row_last = (n_need - 1) / L * S + i_off + (n_need - 1) % L;
+    int rows[NDMA];
+    if (L >= kRB) {                 // a block's rows cross at most one head boundary
+#pragma unroll
+      for (int j = 0; j < NDMA; ++j) rows[j] = row0 + j * RK + (i0 + j * RK >= S ? S - L : 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NDMA; ++j) {
+        int i;
+        rows[j] = row_of(min(u0 + j * RK, n_need - 1), i);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
-      const int r = r0 + j * RK, u = u0 + j * RK;
-      int row;
-      if (L >= kRB) {               // rows of a block cross at most one head boundary
-        const int i = i0 + j * RK;
-        row = row0 + j * RK + (i >= S ? S - L : 0);
-      } else {
-        int i;
-        row = row_of(min(u, n_need - 1), i);
-      }
-      row = u < n_need ? row : row_last;
-      dma16(rq, dst + j * 1024, static_cast<uint32_t>(row) * RBY + 16 * q_chunk<CPR>(r, cp), 0);
+      const int row = u0 + j * RK < n_need ? rows[j] : row_last;
+      const uint32_t chunk = CPR == 16 ? (chunk0 ^ (64u * j)) : chunk0;
+      dma16(rq, dst + j * 1024, static_cast<uint32_t>(row) * RBY + chunk, 0);
     }
   };
   // lse (log2 domain) and query index of row tid of block bk; rows past the
   // end get +inf (P = 0)
+  // (the loaded lse is first used at the next barrier, so the load does not
+  // hold up the copies issued just before it)
   struct RowInfo {
-    float l2;
-    int qi;
+    float lv;
+    int qi;     // query index, or 1 << 30 for rows past the end
   };
   auto load_rows = [&](int bk) __attribute__((always_inline)) {
-    RowInfo ri{__builtin_huge_valf(), 1 << 30};
+    RowInfo ri{0.f, 1 << 30};
     if (tid < kRB) {
       const int u = bk * kRB + tid;
       int i;
       const int row = row_of(min(u, n_need - 1), i);
-      const float lv = lhead[row];
-      ri.l2 = u < n_need ? lv * kLog2e : __builtin_huge_valf();
+      ri.lv = lhead[row];
       ri.qi = u < n_need ? i : (1 << 30);
     }
     return ri;
   };
   auto store_rows = [&](const RowInfo& ri, int stg) __attribute__((always_inline)) {
     if (tid < kRB) {
-      s_l2[stg][tid] = ri.l2;
+      s_l2[stg][tid] = ri.qi < (1 << 30) ? ri.lv * kLog2e : __builtin_huge_valf();
       s_qi[stg][tid] = ri.qi;
-      int mn = ri.qi;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) mn = min(mn, __shfl_xor(mn, o));
-      if (tid == 0) s_min_qi[stg] = mn;
     }
   };
 
@@ -172,8 +187,8 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
 #pragma unroll
   for (int st = 0; st < DS; ++st) q_rd[st] = col * RBY + 16 * q_chunk<CPR>(col, 2 * st + hf);
 
-  auto mfma_half = [&](int stg, int h, f32x16& a0, f32x16& a1) __attribute__((always_inline)) {
-    const char* qb = qs + stg * BLK + h * 32 * RBY;
+  auto mfma_half = [&](auto stg, int h, f32x16& a0, f32x16& a1) __attribute__((always_inline)) {
+    const char* qb = stage_buf(stg) + h * 32 * RBY;
     a0 = zero16();
     a1 = zero16();
 #pragma unroll
@@ -183,7 +198,9 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
       a1 = mfma32x32x16(qa, kf[1][st], a1);
     }
   };
-  float cs0 = 0.f, cs1 = 0.f;     // column sums of this lane's two key columns
+  // column sums of this lane's two key columns, four partial sums each
+  // (short dependency chains)
+  float cs0[4] = {0.f, 0.f, 0.f, 0.f}, cs1[4] = {0.f, 0.f, 0.f, 0.f};
   // accumulator register r of lane l: row 32h + 8(r/4) + 4hf + r%4 of the
   // block; the 4 rows of each group of 4 registers are consecutive
   auto valu_half = [&](const f32x16& a0, const f32x16& a1, int stg, int h, auto masked) __attribute__((always_inline)) {
@@ -204,75 +221,96 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
           p0 = (key0 + col <= qi) ? p0 : 0.f;
           p1 = (key0 + 32 + col <= qi) ? p1 : 0.f;
         }
-        cs0 += p0;
-        cs1 += p1;
+        cs0[e] += p0;
+        cs1[e] += p1;
       }
     }
   };
-  auto block_masked = [&](int stg) __attribute__((always_inline)) {
-    return !is_cache && __builtin_amdgcn_readfirstlane(s_min_qi[stg]) < key0 + 63;
+  // smallest query index among block bk's rows (scalar): the first row's
+  // index, or i_off when the block reaches the start of another head
+  auto block_masked = [&](int bk) __attribute__((always_inline)) {
+    const int u0 = bk * kRB;
+    const int r = u0 % L;
+    const int min_qi = (r + kRB - 1 >= L && u0 + L - r < n_need) ? i_off : i_off + r;
+    return !is_cache && min_qi < key0 + 63;
   };
 
   if (blk_lo < blk_hi) {
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
     // prologue: blocks lo (stage 0) and lo + 1 (stage 1) in flight, rows of
     // lo staged, MFMAs of lo's first half
-    issue_blk(blk_lo, 0);
-    if (blk_lo + 1 < blk_hi) issue_blk(blk_lo + 1, 1);
+    issue_blk(blk_lo, S0{});
+    if (blk_lo + 1 < blk_hi) issue_blk(blk_lo + 1, S1{});
     const RowInfo r0 = load_rows(blk_lo);
     RowInfo rn = load_rows(blk_lo + 1);
     wait_vmem_all();
     store_rows(r0, 0);
     __syncthreads();
     f32x16 A0, A1, B0, B1;
-    mfma_half(0, 0, A0, A1);
-    int stg = 0;
-    bool masked = block_masked(0);
-    for (int bk = blk_lo; bk < blk_hi; ++bk) {
-      const int stg1 = stg == kStages - 1 ? 0 : stg + 1;
-      const int stg2 = stg1 == kStages - 1 ? 0 : stg1 + 1;
+    mfma_half(S0{}, 0, A0, A1);
+    bool masked = block_masked(blk_lo);
+    // block bk in stage STG (= (bk - lo) mod 3, compile-time after unrolling)
+    auto block = [&](int bk, auto stg) __attribute__((always_inline)) {
+      constexpr int STG = decltype(stg)::value;
+      using N1 = std::integral_constant<int, (STG + 1) % kStages>;
+      using N2 = std::integral_constant<int, (STG + 2) % kStages>;
       // second half's MFMAs beside the first half's exp and column sums
       if (masked) {
         mfma_half(stg, 1, B0, B1);
-        valu_half(A0, A1, stg, 0, std::true_type{});
+        valu_half(A0, A1, STG, 0, std::true_type{});
       } else {
         mfma_half(stg, 1, B0, B1);
-        valu_half(A0, A1, stg, 0, std::false_type{});
+        valu_half(A0, A1, STG, 0, std::false_type{});
       }
       // block bk+1 landed (copies and rows issued one block ago); then
       // fetch block bk+2 into the stage block bk-1 used
       wait_vmem_all();
-      if (bk + 1 < blk_hi) store_rows(rn, stg1);
+      if (bk + 1 < blk_hi) store_rows(rn, N1::value);
       __syncthreads();
       if (bk + 2 < blk_hi) {
-        issue_blk(bk + 2, stg2);
+        issue_blk(bk + 2, N2{});
         rn = load_rows(bk + 2);
       }
-      const bool masked_next = bk + 1 < blk_hi && block_masked(stg1);
+      const bool masked_next = bk + 1 < blk_hi && block_masked(bk + 1);
       // next block's first-half MFMAs beside this block's second half
       if (bk + 1 < blk_hi) {
         if (masked) {
-          mfma_half(stg1, 0, A0, A1);
-          valu_half(B0, B1, stg, 1, std::true_type{});
+          mfma_half(N1{}, 0, A0, A1);
+          valu_half(B0, B1, STG, 1, std::true_type{});
         } else {
-          mfma_half(stg1, 0, A0, A1);
-          valu_half(B0, B1, stg, 1, std::false_type{});
+          mfma_half(N1{}, 0, A0, A1);
+          valu_half(B0, B1, STG, 1, std::false_type{});
         }
       } else {
-        if (masked) valu_half(B0, B1, stg, 1, std::true_type{});
-        else valu_half(B0, B1, stg, 1, std::false_type{});
+        if (masked) valu_half(B0, B1, STG, 1, std::true_type{});
+        else valu_half(B0, B1, STG, 1, std::false_type{});
       }
       masked = masked_next;
-      stg = stg1;
+    };
+    // whole triples without conditions between the blocks (so the wait
+    // analysis sees every copy into a stage waited before that stage is
+    // read), then the remaining one or two blocks
+    int bk = blk_lo;
+    for (; bk + kStages <= blk_hi; bk += kStages) {
+      block(bk, S0{});
+      block(bk + 1, S1{});
+      block(bk + 2, S2{});
     }
+    if (bk < blk_hi) block(bk, S0{});
+    if (bk + 1 < blk_hi) block(bk + 1, S1{});
   }
-  cs0 += xor32(cs0);
-  cs1 += xor32(cs1);
+  float t0 = (cs0[0] + cs0[1]) + (cs0[2] + cs0[3]);
+  float t1 = (cs1[0] + cs1[1]) + (cs1[2] + cs1[3]);
+  t0 += xor32(t0);
+  t1 += xor32(t1);
   const size_t PS = static_cast<size_t>(M) + S;
   if (hf == 0) {
     float* out = partial + (static_cast<size_t>(bh) * R + split) * PS + (is_cache ? 0 : M);
     const int k0 = key0 + col, k1 = key0 + 32 + col;
-    if (k0 < lim) out[k0] = cs0;
-    if (k1 < lim) out[k1] = cs1;
+    if (k0 < lim) out[k0] = t0;
+    if (k1 < lim) out[k1] = t1;
   }
 }
 

@@ -60,6 +60,7 @@ def test_named_workload_configs_validate():
     dict(max_chunk=0),
     dict(recent_window=-1),
     dict(softmax_scale=math.nan),
+    dict(n_q_heads=1024, n_kv_heads=1),  # G * max_len above 2^20 query rows per KV group
 ])
 def test_invalid_configs_are_rejected(kw):
     h2o = _lib_module()
