@@ -89,8 +89,28 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   constexpr int RB = 2 * D;               // bytes per K or V row
   constexpr int TB = kKT * RB;            // bytes per K or V tile
   constexpr int NDMA = TB / 4096;         // 1 KB copies per wave per tile (4 waves per group)
-  // K slots [group][2] at 0, V slots [group][2] at 4 TB
-  __shared__ __attribute__((aligned(1024))) char lds[8 * TB];
+  // K and V slots, one array per (group, slot): the compiler can then tell
+  // that a copy in flight into one slot does not alias reads of another, and
+  // inserts no wait for it
+  __shared__ __attribute__((aligned(1024))) char k00[TB];
+  __shared__ __attribute__((aligned(1024))) char k01[TB];
+  __shared__ __attribute__((aligned(1024))) char k10[TB];
+  __shared__ __attribute__((aligned(1024))) char k11[TB];
+  __shared__ __attribute__((aligned(1024))) char v00[TB];
+  __shared__ __attribute__((aligned(1024))) char v01[TB];
+  __shared__ __attribute__((aligned(1024))) char v10[TB];
+  __shared__ __attribute__((aligned(1024))) char v11[TB];
+  // compile-time (group, slot) -> buffer
+  auto kbuf = [&](auto g, auto sl) __attribute__((always_inline)) {
+    constexpr int GG = decltype(g)::value, SL = decltype(sl)::value;
+    return GG == 0 ? (SL == 0 ? k00 : k01) : (SL == 0 ? k10 : k11);
+  };
+  auto vbuf = [&](auto g, auto sl) __attribute__((always_inline)) {
+    constexpr int GG = decltype(g)::value, SL = decltype(sl)::value;
+    return GG == 0 ? (SL == 0 ? v00 : v01) : (SL == 0 ? v10 : v11);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -172,20 +192,18 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   auto dv_soff = [&](int j) __attribute__((always_inline)) {
     return static_cast<uint32_t>(D == 128 ? 256 * (16 * rbw + 4 * j) : 128 * 8 * (2 * rbw + j));
   };
-  const char* lds_k = lds + grp * 2 * TB;
-  const char* lds_v = lds + 4 * TB + grp * 2 * TB;
   // rows past the end of a partial tile re-read its last row (masked later)
   auto clamp_row = [](uint32_t off, int n) __attribute__((always_inline)) {
     const int key = static_cast<int>(off / RB);
     return key < n ? off : off - static_cast<uint32_t>(key - n + 1) * RB;
   };
-  auto issue_k = [&](int T, int slot) __attribute__((always_inline)) {
+  auto issue_k = [&](int T, auto g, auto slot) __attribute__((always_inline)) {
     T = min(T, n_tiles - 1);          // past the end: reload the last tile (masked)
     const bool is_cache = T < n_ct;
     const int base = is_cache ? T * kKT : (T - n_ct) * kKT;
     const int n = (is_cache ? n_cache : S) - base;
     const __amdgpu_buffer_rsrc_t r = is_cache ? rk_c : rk_n;
-    const char* dst = lds_k + slot * TB + rbw * NDMA * 1024;
+    const char* dst = kbuf(g, slot) + rbw * NDMA * 1024;
     const uint32_t soff = static_cast<uint32_t>(base) * RB;
     if (n >= kKT) {
 #pragma unroll
@@ -202,13 +220,13 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
       }
     }
   };
-  auto issue_v = [&](int T, int slot) __attribute__((always_inline)) {
+  auto issue_v = [&](int T, auto g, auto slot) __attribute__((always_inline)) {
     T = min(T, n_tiles - 1);          // past the end: reload the last tile (masked)
     const bool is_cache = T < n_ct;
     const int base = is_cache ? T * kKT : (T - n_ct) * kKT;
     const int n = (is_cache ? n_cache : S) - base;
     const __amdgpu_buffer_rsrc_t r = is_cache ? rv_c : rv_n;
-    const char* dst = lds_v + slot * TB + rbw * NDMA * 1024;
+    const char* dst = vbuf(g, slot) + rbw * NDMA * 1024;
     const uint32_t soff = static_cast<uint32_t>(base) * RB;
     if (n >= kKT) {
 #pragma unroll
@@ -243,8 +261,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   }
 
   // S^T of one tile: register r of a0 (a1) <-> key 16(l/32) + r (+32)
-  auto qk = [&](int slot, f32x16& a0, f32x16& a1) __attribute__((always_inline)) {
-    const char* kt = lds_k + slot * TB;
+  auto qk = [&](auto g, auto slot, f32x16& a0, f32x16& a1) __attribute__((always_inline)) {
+    const char* kt = kbuf(g, slot);
     a0 = zero16();
     a1 = zero16();
 #pragma unroll
@@ -258,8 +276,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   // O^T += V^T P^T; MFMA (kb,u) covers keys 32kb + 16(l/32) + 8u + e.  The A
   // operand V^T comes from two transpose reads: lane j = 4r + q of a 16-lane
   // group addresses V[key0 + r][d0 + 4q .. +4).
-  auto pv = [&](int slot, const bf16x8 (&pb)[4]) __attribute__((always_inline)) {
-    const char* vt = lds_v + slot * TB;
+  auto pv = [&](auto g, auto slot, const bf16x8 (&pb)[4]) __attribute__((always_inline)) {
+    const char* vt = vbuf(g, slot);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -345,17 +363,6 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   // finite V.
   f32x16 sc0, sc1;
   bf16x8 pb[4];
-  const int pos0 = load_pos(grp);
-  int pos1 = load_pos(2 + grp);
-  issue_k(grp, 0);
-  issue_k(2 + grp, 1);
-  issue_v(grp, 0);
-  issue_v(2 + grp, 1);
-  wait_vmem_all();
-  __syncthreads();
-  qk(0, sc0, sc1);
-  __syncthreads();
-  issue_k(4 + grp, 0);
 
   // Ping-pong: iteration t has an MFMA phase M(t) = {S^T of tile t+1 from K
   // slot (t+1)&1, O += PV of tile t from V slot t&1} and a VALU phase
@@ -366,89 +373,115 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   // same number of loads per iteration (position + K and V tile copies), so
   // a fixed vmcnt waits for exactly the previous iteration's copies: after
   // its MFMA phase a group fetches K of tile t+3 and V of tile t+2 into the
-  // slots it just read, three phases before their use.
+  // slots it just read, three phases before their use.  Each group runs its
+  // own loop (same barrier count), so that each carries only its own state
+  // across iterations (group 0 P, group 1 S) and its buffers are fixed.
   constexpr int kLoadsPerIter = 1 + 2 * NDMA;
   constexpr int kWaitPrev = 0x0f70 | (kLoadsPerIter & 15) | ((kLoadsPerIter >> 4) << 14);
-  auto m_phase = [&](int P) __attribute__((always_inline)) {
-    f32x16 sn0, sn1;
-    qk(P ^ 1, sn0, sn1);
-    pv(P, pb);
-    sc0 = sn0;
-    sc1 = sn1;
-  };
-  auto v_phase = [&](int T, int posv) __attribute__((always_inline)) {
-    mask_and_check(sc0, sc1, tile_max(sc0, sc1), T, posv);
-    softmax(sc0, sc1, pb);
-  };
-  // Two loops (one per group, same barrier count) so that each carries only
-  // its own state across iterations: group 0 P, group 1 S.
-  if (grp == 0) {
-    v_phase(0, pos0);                 // P(0)
-    int pos_n = pos1;                 // position of tile t+1
-    auto iteration = [&](int t, auto par) __attribute__((always_inline)) {
-      constexpr int P = decltype(par)::value;
-      m_phase(P);
-      __syncthreads();
-      const int pn = load_pos(2 * (t + 2));
-      issue_k(2 * (t + 3), P ^ 1);
-      issue_v(2 * (t + 2), P);
-      v_phase(2 * (t + 1), pos_n);
-      pos_n = pn;
-      __builtin_amdgcn_s_waitcnt(kWaitPrev);
-      __syncthreads();
+  auto run_group = [&](auto g) __attribute__((always_inline)) {
+    constexpr int GG = decltype(g)::value;
+    const int pos0 = load_pos(GG);
+    const int pos1 = load_pos(2 + GG);
+    issue_k(GG, g, I0{});
+    issue_k(2 + GG, g, I1{});
+    issue_v(GG, g, I0{});
+    issue_v(2 + GG, g, I1{});
+    wait_vmem_all();
+    barrier_lds();
+    qk(g, I0{}, sc0, sc1);
+    barrier_lds();
+    issue_k(4 + GG, g, I0{});
+    auto m_phase = [&](auto par) __attribute__((always_inline)) {
+      using PN = std::integral_constant<int, decltype(par)::value ^ 1>;
+      f32x16 sn0, sn1;
+      qk(g, PN{}, sn0, sn1);
+      pv(g, par, pb);
+      sc0 = sn0;
+      sc1 = sn1;
     };
-    for (int t = 0; t < n_iter; t += 2) {
-      iteration(t, std::integral_constant<int, 0>{});
-      iteration(t + 1, std::integral_constant<int, 1>{});
-    }
-  } else {
-    int pos_c = pos0, pos_n = pos1;   // positions of tiles t and t+1
-    auto iteration = [&](int t, auto par) __attribute__((always_inline)) {
-      constexpr int P = decltype(par)::value;
-      v_phase(2 * t + 1, pos_c);
-      __builtin_amdgcn_s_waitcnt(kWaitPrev);
-      __syncthreads();
-      m_phase(P);
-      __syncthreads();
-      pos_c = pos_n;
-      pos_n = load_pos(2 * (t + 2) + 1);
-      issue_k(2 * (t + 3) + 1, P ^ 1);
-      issue_v(2 * (t + 2) + 1, P);
+    auto v_phase = [&](int T, int posv) __attribute__((always_inline)) {
+      mask_and_check(sc0, sc1, tile_max(sc0, sc1), T, posv);
+      softmax(sc0, sc1, pb);
     };
-    for (int t = 0; t < n_iter; t += 2) {
-      iteration(t, std::integral_constant<int, 0>{});
-      iteration(t + 1, std::integral_constant<int, 1>{});
+    if constexpr (GG == 0) {
+      v_phase(0, pos0);                 // P(0)
+      int pos_n = pos1;                 // position of tile t+1
+      auto iteration = [&](int t, auto par) __attribute__((always_inline)) {
+        using PN = std::integral_constant<int, decltype(par)::value ^ 1>;
+        m_phase(par);
+        barrier_lds();
+        const int pn = load_pos(2 * (t + 2));
+        issue_k(2 * (t + 3), g, PN{});
+        issue_v(2 * (t + 2), g, par);
+        v_phase(2 * (t + 1), pos_n);
+        pos_n = pn;
+        __builtin_amdgcn_s_waitcnt(kWaitPrev);
+        barrier_lds();
+      };
+      for (int t = 0; t < n_iter; t += 2) {
+        iteration(t, I0{});
+        iteration(t + 1, I1{});
+      }
+    } else {
+      int pos_c = pos0, pos_n = pos1;   // positions of tiles t and t+1
+      auto iteration = [&](int t, auto par) __attribute__((always_inline)) {
+        using PN = std::integral_constant<int, decltype(par)::value ^ 1>;
+        v_phase(2 * t + 1, pos_c);
+        __builtin_amdgcn_s_waitcnt(kWaitPrev);
+        barrier_lds();
+        m_phase(par);
+        barrier_lds();
+        pos_c = pos_n;
+        pos_n = load_pos(2 * (t + 2) + 1);
+        issue_k(2 * (t + 3) + 1, g, PN{});
+        issue_v(2 * (t + 2) + 1, g, par);
+      };
+      for (int t = 0; t < n_iter; t += 2) {
+        iteration(t, I0{});
+        iteration(t + 1, I1{});
+      }
     }
-  }
+  };
+  if (grp == 0) run_group(I0{});
+  else run_group(I1{});
 
-  // ---- merge the two groups' softmax states (group 1 -> LDS -> group 0)
+  // ---- merge the two groups' softmax states (group 1 -> LDS -> group 0),
+  // one 32-row block of O^T per round through a K slot
   wait_vmem_all();
-  __syncthreads();
-  float* xch = reinterpret_cast<float*>(lds);            // [DB*16 + 2][kRowBlocks*64]
+  barrier_lds();
+  constexpr int NX = kRowBlocks * 64;                     // lanes of a group
+  float* xo = reinterpret_cast<float*>(k00);              // 16 x NX floats
+  float* xm = reinterpret_cast<float*>(k01);              // m, l of group 1
   const int slot = rbw * 64 + lane;
-  constexpr int NX = kRowBlocks * 64;
   if (grp == 1) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) xch[(db * 16 + r) * NX + slot] = o[db][r];
-    xch[(DB * 16) * NX + slot] = m_run;
-    xch[(DB * 16 + 1) * NX + slot] = l_run;
+    xm[slot] = m_run;
+    xm[NX + slot] = l_run;
   }
-  __syncthreads();
-  if (grp == 1 || !active) return;
-  {
-    const float m1 = xch[(DB * 16) * NX + slot];
-    const float l1 = xch[(DB * 16 + 1) * NX + slot];
+  barrier_lds();
+  float a0 = 1.f, a1 = 0.f;
+  if (grp == 0) {
+    const float m1 = xm[slot];
+    const float l1 = xm[NX + slot];
     const float m = fmaxf(m_run, m1);
-    const float a0 = fast_exp2(m_run - m), a1 = fast_exp2(m1 - m);
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + xch[(db * 16 + r) * NX + slot] * a1;
+    a0 = fast_exp2(m_run - m);
+    a1 = fast_exp2(m1 - m);
     l_run = l_run * a0 + l1 * a1;
     m_run = m;
   }
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    if (grp == 1) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xo[r * NX + slot] = o[db][r];
+    }
+    barrier_lds();
+    if (grp == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + xo[r * NX + slot] * a1;
+    }
+    barrier_lds();
+  }
+  if (grp == 1 || !active) return;
   const float l_tot = l_run + xor32(l_run);
   if (qi >= S) return;
   const float inv = 1.f / l_tot;

@@ -58,6 +58,16 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds_
 
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
+// Workgroup barrier for LDS traffic: waits for this wave's LDS accesses
+// (lgkmcnt(0)) and meets the other waves.  Unlike __syncthreads, whose
+// release fence waits for every outstanding global load -- copies into LDS
+// still in flight included -- it leaves those copies running; their
+// completion is waited for explicitly (vmcnt) where a stage is consumed.
+// The memory clobber keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ bf16x8 load_bf16x8(const bf16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }

@@ -247,7 +247,7 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
     RowInfo rn = load_rows(blk_lo + 1);
     wait_vmem_all();
     store_rows(r0, 0);
-    __syncthreads();
+    barrier_lds();
     f32x16 A0, A1, B0, B1;
     mfma_half(S0{}, 0, A0, A1);
     bool masked = block_masked(blk_lo);
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
       // fetch block bk+2 into the stage block bk-1 used
       wait_vmem_all();
       if (bk + 1 < blk_hi) store_rows(rn, N1::value);
-      __syncthreads();
+      barrier_lds();
       if (bk + 2 < blk_hi) {
         issue_blk(bk + 2, N2{});
         rn = load_rows(bk + 2);
