@@ -2,24 +2,29 @@
 
 One step = one whole synthetic sequence of the named workload through the C
 ABI: cache reset, the prefill chunk (N_C tokens), then every chunk step of
-length S up to the total length.  Inputs are generated on the host from the
-seeded generators and uploaded before timing, so they are resident in HBM
-when the timed region starts.
+length S up to the total length (with the frozen-eviction backward after
+each chunk step for the workload that trains through the lattice).  Inputs
+are generated on the host from the seeded generators and uploaded before
+timing, so they are resident in HBM when the timed region starts.
 
 Reported (one JSON line): algorithmic TFLOP/s of the attention (4 d flops per
-visible (query, key) pair per query head; the score pass's recompute is not
-counted), tokens/s, the roofline of the dominant kernel (attention forward,
-bf16 MFMA) from HIP events recorded by the library on the launch stream, and
-the fp64 CPU oracle timed on a bounded sample of the same workload.
+visible (query, key) pair per query head forward, 10 d backward; the score
+pass's recompute is not counted), tokens/s, the roofline of the dominant
+kernel (attention forward: bf16 MFMA, or HBM for the decode workload) from
+HIP events recorded by the library on the launch stream, and the fp64 CPU
+oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       python bench.py --copy-probe MB    (plain copy of known size, for
+                                           scaling the HBM byte counters)
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
-import math
 import os
+import re
 import sys
 import time
 
@@ -33,25 +38,67 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0
 
+# workloads whose metric is bytes (HBM-bound); their prefill only fills the
+# cache and is not timed
+HBM_BOUND = {"decode_b32"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+ATTN_SOURCE = os.path.join(ROOT, "kv_cache_eviction_amd", "csrc", "attn_fwd.hip")
 
-def algorithmic_flops(w, with_prefill=True):
-    """Per-launch attention flops of a whole sequence: list of (kind, flops)."""
-    d, B, Hq, M = w.head_dim, w.batch, w.n_q_heads, w.cache_slots
+
+def visible_pairs(w, c, T):
+    """Visible (query, key) pairs per query head of chunk c after T tokens."""
+    _, n = w.chunk_bounds(c)
+    mv = min(T, w.cache_slots)
+    return n * mv + n * (n + 1) // 2
+
+
+def algorithmic_flops(w, backward=False):
+    """Attention flops of a whole sequence, per launch: list of (kind, flops)."""
+    d, B, Hq = w.head_dim, w.batch, w.n_q_heads
     out = []
     T = 0
     for c in range(w.n_chunks):
-        _, n = w.chunk_bounds(c)
-        mv = min(T, M)
-        visible = n * mv + n * (n + 1) // 2
-        if c > 0 or with_prefill:
-            out.append(("prefill" if c == 0 else "chunk", 4.0 * B * Hq * d * visible))
-        T += n
+        v = visible_pairs(w, c, T)
+        out.append(("prefill" if c == 0 else "chunk", 4.0 * B * Hq * d * v))
+        if backward and c > 0:
+            out.append(("backward", 10.0 * B * Hq * d * v))
+        T += w.chunk_bounds(c)[1]
     return out
+
+
+def attn_bytes(w, c, T):
+    """Algorithmic HBM bytes of one attention launch: Q in, O out, the valid
+    cache rows of K and V once, the chunk's K and V, and lse."""
+    _, n = w.chunk_bounds(c)
+    e, B, Hq, Hkv, d = w.elem_bytes, w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
+    mv = min(T, w.cache_slots)
+    return e * (2 * B * Hq * n * d + 2 * B * Hkv * mv * d + 2 * B * Hkv * n * d) + 4 * B * Hq * n
+
+
+def source_digest(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch from the counter runs recorded in
+    profiles/hbm_traffic.md, or None if absent or taken on another version of
+    the kernel source."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    pat = re.compile(r"^\|\s*%s\s*\|\s*%s\s*\|\s*([0-9]+)\s*\|\s*([0-9a-f]+)\s*\|" % (
+        re.escape(kernel), re.escape(workload)), re.M)
+    m = pat.search(text)
+    if not m or m.group(2) != source_digest(ATTN_SOURCE):
+        return None
+    return int(m.group(1))
 
 
 def oracle_sample(w, seed, budget_s=20.0):
     """Times the fp64 oracle on the first chunks of the workload (prefill plus
-    as many chunk steps as fit in about `budget_s`), all heads."""
+    as many chunk steps as fit in about `budget_s`), all heads, forward."""
     from oracle import h2o_oracle as orc
     from kv_cache_eviction_amd import workloads as wl
     try:
@@ -60,7 +107,7 @@ def oracle_sample(w, seed, budget_s=20.0):
     except Exception:
         threads = os.cpu_count() or 1
     hh = wl.heavy_hitters(w, seed)
-    flops = algorithmic_flops(w)
+    flops = [f for k, f in algorithmic_flops(w)]
     K, V, sig, pos = orc.empty_state(w.batch, w.n_kv_heads, w.cache_slots, w.head_dim)
     done_flops = 0.0
     tokens = 0
@@ -73,12 +120,27 @@ def oracle_sample(w, seed, budget_s=20.0):
         st = orc.chunk_step(K, V, sig, pos, T, q, k, v, w.recent_window)
         elapsed += time.perf_counter() - t0
         K, V, sig, pos, T = st["K"], st["V"], st["sigma"], st["pos"], st["T"]
-        done_flops += flops[c][1]
+        done_flops += flops[c]
         tokens += w.batch * q.shape[2]
         c += 1
     return dict(value=done_flops / elapsed / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
-                sample=f"prefill + {c - 1} chunk steps of {w.name} (all heads), {elapsed:.1f} s",
+                sample=f"prefill + {c - 1} chunk steps of {w.name} (all heads, forward), {elapsed:.1f} s",
                 tokens_per_s=tokens / elapsed)
+
+
+def copy_probe(mb):
+    """A plain elementwise copy of a known size (reads mb MiB, writes mb MiB,
+    three launches), so that HBM byte counters can be scaled to bytes."""
+    import torch
+    n = mb * 1024 * 1024 // 4
+    a = torch.rand(n, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": 3}),
+          flush=True)
 
 
 def main():
@@ -90,17 +152,23 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MB")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the H2O step shards by batch or KV head with no "
               f"exchange); --gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
 
     import torch
     from kv_cache_eviction_amd import workloads as wl
     from kv_cache_eviction_amd import h2o
 
     w = wl.workload(args.workload)
+    hbm = w.name in HBM_BOUND
+    backward = w.backward
     cfg = h2o.H2OConfig(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.cache_slots,
                         w.recent_window, w.chunk, w.prefill, w.dtype)
     dev = torch.device("cuda:0")
@@ -125,39 +193,60 @@ def main():
     positions = torch.empty((B, Hkv, M), dtype=torch.int32, device=dev)
     workspace = torch.empty(h2o.h2o_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    if backward:
+        # the backward needs the pre-step cache: copied before each step (part of the job)
+        k_pre, v_pre, pos_pre = torch.empty_like(k_cache), torch.empty_like(v_cache), torch.empty_like(positions)
+        d_outs = [up(wl.chunk_grad_out(w, args.seed, c)) if c > 0 else None for c in range(w.n_chunks)]
+        grads = [torch.empty_like(chunks[1][0]), torch.empty_like(k_cache), torch.empty_like(v_cache),
+                 torch.empty_like(chunks[1][1]), torch.empty_like(chunks[1][2])]
+        bws = torch.empty(h2o.h2o_backward_workspace_bytes(cfg, w.chunk), dtype=torch.uint8, device=dev)
+    bwd_marks = []
 
-    timing_handles = []
-
-    def one_pass(timing):
+    def one_pass(timing, marks=None, bwd_timing=False):
         handle = h2o.h2o_cache_init(cfg, k_cache, v_cache, scores, positions, workspace, stream=stream)
         if timing:
             h2o.h2o_set_timing(handle, timing)
         q, k, v = chunks[0]
         h2o.h2o_prefill(handle, cfg, q, k, v, outs[0], lses[0], stream)
+        if marks is not None:
+            marks[0].record(stream)
         for c in range(1, w.n_chunks):
             q, k, v = chunks[c]
+            if backward:
+                k_pre.copy_(k_cache)
+                v_pre.copy_(v_cache)
+                pos_pre.copy_(positions)
             h2o.h2o_chunk_step(handle, cfg, q, k, v, outs[c], lses[c], stream=stream)
+            if backward:
+                if bwd_timing:
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                h2o.h2o_chunk_backward(cfg, q, k_pre, v_pre, pos_pre, k, v, outs[c], lses[c], d_outs[c],
+                                       *grads, bws, stream)
+                if bwd_timing:
+                    e1.record(stream)
+                    bwd_marks.append((e0, e1))
+        if marks is not None:
+            marks[1].record(stream)
         return handle
 
     for _ in range(args.warmup):
         h2o.h2o_cache_destroy(one_pass(None))
     torch.cuda.synchronize()
     # timed region: only the attention kernel is bracketed with library events
-    # (two extra stream records per step); each pass is bracketed too, for the
-    # per-step median
+    # (two extra stream records per step); the chunk steps of each pass are
+    # bracketed too
     marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(args.steps)]
+    handles = []
     t0 = time.perf_counter()
     for i in range(args.steps):
-        marks[i][0].record(stream)
-        timing_handles.append(one_pass(["attn_fwd"]))
-        marks[i][1].record(stream)
+        handles.append(one_pass(["attn_fwd"], marks[i]))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    pass_ms = sorted(a.elapsed_time(b) for a, b in marks)
+    chunk_ms = sorted(a.elapsed_time(b) for a, b in marks)     # chunk steps of each pass
     attn_ms, attn_n = 0.0, 0
-    for hd in timing_handles:
+    for hd in handles:
         ms, cnt = h2o.h2o_get_timing(hd, "attn_fwd")
         attn_ms += ms
         attn_n += cnt
@@ -165,36 +254,68 @@ def main():
 
     # per-kernel breakdown: one more pass with every kernel bracketed (outside
     # the timed region; its event records slow that pass slightly)
-    hd = one_pass(True)
+    hd = one_pass(True, bwd_timing=backward)
     torch.cuda.synchronize()
     step_ms = {}
     for name in ("attn_fwd", "score", "select", "scatter", "reset"):
-        ms, cnt = h2o.h2o_get_timing(hd, name)
+        ms, _ = h2o.h2o_get_timing(hd, name)
         step_ms[name] = ms
     h2o.h2o_cache_destroy(hd)
+    if backward:
+        step_ms["backward"] = sum(a.elapsed_time(b) for a, b in bwd_marks)
 
-    fl = algorithmic_flops(w)
-    flops_per_step = sum(f for _, f in fl)
-    tflops = flops_per_step / (ms_per_step * 1e-3) / 1e12
-    tokens_per_s = w.batch * w.total_len / (ms_per_step * 1e-3)
+    fl = algorithmic_flops(w, backward)
+    attn_fl = [f for kind, f in fl if kind != "backward"]
     attn_avg_ms = attn_ms / max(attn_n, 1)
-    achieved = flops_per_step * args.steps / (attn_ms * 1e-3) / 1e12 if attn_ms > 0 else None
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
-    chunk_flops = [f for k, f in fl if k == "chunk"]
+    if hbm:
+        # the prefill only fills the cache: time and count the chunk steps
+        ms_per_step = sum(chunk_ms) / args.steps
+        ms_median = chunk_ms[len(chunk_ms) // 2]
+        tflops = sum(f for kind, f in fl if kind != "prefill") / (ms_per_step * 1e-3) / 1e12
+        tokens = w.batch * (w.total_len - w.prefill)
+        T, abytes = 0, []
+        for c in range(w.n_chunks):
+            abytes.append(attn_bytes(w, c, T))
+            T += w.chunk_bounds(c)[1]
+        per_launch = sum(abytes) / len(abytes)        # the timed launches include the prefill's
+        achieved = per_launch / (attn_avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "attn_fwd_bf16_kernel", "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": recorded_traffic("attn_fwd_bf16_kernel", w.name),
+                "avg_launch_us": round(attn_avg_ms * 1e3, 3), "algorithmic_bytes_per_launch": round(per_launch)}
+        metric = "H2O decode-step algorithmic HBM GB/s of the chunk steps (B32, S16, M2048)"
+        unit = "GB/s"
+        value = round(sum(abytes[1:]) / (ms_per_step * 1e-3) / 1e9, 1)
+    else:
+        ms_per_step = wall * 1e3 / args.steps
+        ms_median = None
+        tflops = sum(f for _, f in fl) / (ms_per_step * 1e-3) / 1e12
+        tokens = w.batch * w.total_len
+        per_launch = sum(attn_fl) / len(attn_fl)
+        achieved = per_launch / (attn_avg_ms * 1e-3) / 1e12
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+        roof = {"bound": "mfma", "kernel": "attn_fwd_bf16_kernel" if w.dtype == "bf16" else "attn_fwd_f32_kernel",
+                "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": recorded_traffic("attn_fwd_bf16_kernel", w.name),
+                "avg_launch_us": round(attn_avg_ms * 1e3, 3), "algorithmic_flops_per_launch": round(per_launch)}
+        metric = "H2O chunk-step TFLOP/s + tokens/s at 64k ctx, 8B-GQA shape; % of roofline"
+        unit = "TFLOP/s"
+        value = round(tflops, 3)
+    tokens_per_s = tokens / (ms_per_step * 1e-3)
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = oracle_sample(w, args.seed, args.cpu_budget)
 
     rec = {
-        "metric": "H2O chunk-step TFLOP/s + tokens/s at 64k ctx, 8B-GQA shape; % of roofline",
-        "value": round(tflops, 3),
-        "unit": "TFLOP/s",
+        "metric": metric,
+        "value": value,
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
-        "ms_per_step_median": round(pass_ms[len(pass_ms) // 2], 4),
+        "ms_chunk_steps_median": round(ms_median if ms_median is not None else chunk_ms[len(chunk_ms) // 2], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -204,16 +325,13 @@ def main():
             "workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
             "head_dim": w.head_dim, "prefill": w.prefill, "chunk": w.chunk, "total_len": w.total_len,
             "cache_slots": w.cache_slots, "recent_window": w.recent_window,
-            "step": "cache reset + prefill + %d chunk steps" % w.n_steps,
+            "step": "%s + %d chunk steps%s" % (
+                "untimed cache reset + prefill" if hbm else "cache reset + prefill", w.n_steps,
+                ", each followed by the frozen-eviction backward" if backward else ""),
         },
+        "tflops": round(tflops, 3),
         "tokens_per_s": round(tokens_per_s, 1),
-        "roofline": {
-            "bound": "mfma", "kernel": "attn_fwd_bf16_kernel" if w.dtype == "bf16" else "attn_fwd_f32_kernel",
-            "achieved": None if achieved is None else round(achieved, 2), "peak": peak,
-            "unit": "TFLOP/s", "frac": None if achieved is None else round(achieved / peak, 4),
-            "traffic": None, "avg_launch_us": round(attn_avg_ms * 1e3, 3),
-            "chunk_step_flops": chunk_flops[0] if chunk_flops else None,
-        },
+        "roofline": roof,
         "kernel_ms_per_step": {k: round(v, 4) for k, v in step_ms.items()},
         "cpu_baseline": cpu,
     }
