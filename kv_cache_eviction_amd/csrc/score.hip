@@ -42,7 +42,7 @@ namespace {
 constexpr int kCT = 256;        // key columns per workgroup (4 waves x 64)
 constexpr int kRB = 64;         // query rows per staged block (2 MFMA row blocks)
 constexpr int kStages = 3;
-constexpr int kRowSplitsMax = 16;
+constexpr int kRowSplitsMax = 8;     // the select kernel sums up to this many splits
 
 template <int CPR>
 __device__ __forceinline__ int q_chunk(int row, int c) { return c ^ (row & (CPR - 1)); }

@@ -11,16 +11,16 @@
 // smallest (score, slot index); chunk token j goes to the j-th smallest
 // target slot.
 //
-// Two kernels.  The select kernel runs one 1024-thread workgroup per
+// Two kernels.  The select kernel runs one 512-thread workgroup per
 // (b, KV head): no other workgroup reads or writes that head's scores,
 // positions or slots, so it needs no inter-workgroup synchronisation.  It
 //   1. adds the score kernel's R per-split masses to the filled slots'
 //      scores (fixed split order: deterministic);
 //   2. selects the targets: scores map to order-preserving 32-bit keys, the
 //      bits every candidate shares are found with an AND/OR reduction and
-//      skipped, and 8-bit LDS radix passes over the remaining bits find the
-//      n_e-th smallest key; equal keys resolve to the lowest slot through an
-//      exclusive scan in slot order;
+//      skipped, and 8-bit LDS radix passes over the remaining bits (one
+//      barrier each) find the n_e-th smallest key; equal keys resolve to the
+//      lowest slot through one exclusive scan in slot order;
 //   3. writes scores, positions and the target list R (with a flag for
 //      targets that were free).
 // The scatter kernel then copies the chunk's K/V rows into their slots with
@@ -31,10 +31,10 @@
 namespace h2o {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 512;
 constexpr int kWavesSel = kThreads / 64;
-constexpr int kPre = 4;        // 16-byte chunks of K and of V each thread prefetches
-constexpr int kMaxSplits = 16; // upper bound of the score kernel's row splits
+constexpr int kMaxSplits = 8;  // upper bound of the score kernel's row splits
+constexpr int kMuRegs = 2;     // chunk keys per thread whose masses are prefetched
 
 enum : uint8_t { kFree = 0, kCand = 1, kKeep = 2, kTarget = 4 };
 constexpr int32_t kWasFree = 0x40000000;   // flag bit of a target-list entry
@@ -50,56 +50,57 @@ __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
-  return v;
+// wave64 inclusive prefix on DPP: shifts within 16-lane rows (lanes without
+// a source add the identity), then row broadcasts across rows
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31 -> rows 2, 3
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_and(uint32_t v) {
+  int x = static_cast<int>(v);
+  x &= __builtin_amdgcn_update_dpp(-1, x, 0x111, 0xf, 0xf, false);
+  x &= __builtin_amdgcn_update_dpp(-1, x, 0x112, 0xf, 0xf, false);
+  x &= __builtin_amdgcn_update_dpp(-1, x, 0x114, 0xf, 0xf, false);
+  x &= __builtin_amdgcn_update_dpp(-1, x, 0x118, 0xf, 0xf, false);
+  x &= __builtin_amdgcn_update_dpp(-1, x, 0x142, 0xa, 0xf, false);
+  x &= __builtin_amdgcn_update_dpp(-1, x, 0x143, 0xc, 0xf, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 63));
+}
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  int x = static_cast<int>(v);
+  x |= __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);
+  x |= __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);
+  x |= __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);
+  x |= __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);
+  x |= __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);
+  x |= __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 63));
 }
 
-// Exclusive prefix of v over the threads of the block (thread order); also
-// returns the block total.  `tmp` holds kWavesSel ints of LDS.
-__device__ int block_excl_scan(int v, int* tmp, int& total) {
+// Exclusive prefix over the threads of the block (thread order) of two ints
+// at once, one barrier; `tmp` (2 * kWavesSel ints) must not be in use by
+// another call until the next barrier.
+__device__ void block_excl_scan2(int a, int b, int* tmp, int& pa, int& pb) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int incl = wave_incl_scan(v, lane);
+  const int ia = wave_incl_scan(a), ib = wave_incl_scan(b);
+  if (lane == 63) {
+    tmp[wave] = ia;
+    tmp[kWavesSel + wave] = ib;
+  }
   __syncthreads();
-  if (lane == 63) tmp[wave] = incl;
-  __syncthreads();
-  int before = 0, tot = 0;
+  int ba = 0, bb = 0;
 #pragma unroll
   for (int w = 0; w < kWavesSel; ++w) {
-    const int x = tmp[w];
-    before += (w < wave) ? x : 0;
-    tot += x;
+    ba += (w < wave) ? tmp[w] : 0;
+    bb += (w < wave) ? tmp[kWavesSel + w] : 0;
   }
-  total = tot;
-  return before + incl - v;
-}
-
-// Block-wide AND and OR (utmp holds 2*kWavesSel words of LDS).
-__device__ void block_and_or(uint32_t v_and, uint32_t v_or, uint32_t* utmp, uint32_t& r_and,
-                             uint32_t& r_or) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    v_and &= static_cast<uint32_t>(__shfl_xor(static_cast<int>(v_and), o));
-    v_or |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(v_or), o));
-  }
-  __syncthreads();
-  if (lane == 0) {
-    utmp[wave] = v_and;
-    utmp[kWavesSel + wave] = v_or;
-  }
-  __syncthreads();
-  r_and = 0xffffffffu;
-  r_or = 0u;
-#pragma unroll
-  for (int w = 0; w < kWavesSel; ++w) {
-    r_and &= utmp[w];
-    r_or |= utmp[kWavesSel + w];
-  }
+  pa = ba + ia - a;
+  pb = bb + ib - b;
 }
 
 __global__ __launch_bounds__(kThreads) void select_kernel(
@@ -111,26 +112,34 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   uint32_t* s_key = reinterpret_cast<uint32_t*>(smem);                        // [M]
   int* s_R = reinterpret_cast<int*>(smem + 4 * static_cast<size_t>(M));      // [S]
   uint8_t* s_fl = reinterpret_cast<uint8_t*>(smem + 4 * static_cast<size_t>(M) + 4 * static_cast<size_t>(S));
-  __shared__ uint32_t hist[256];
-  __shared__ int s_tmp[kWavesSel];
-  __shared__ uint32_t s_utmp[2 * kWavesSel];
-  __shared__ int s_sel[2];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[3][kWavesSel / 2][256];   // per wave pair, 3 rotating
+  __shared__ int s_red[3][kWavesSel];
+  __shared__ int s_scan[2 * kWavesSel];
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bh = blockIdx.x;
   const size_t PS = static_cast<size_t>(M) + S;
   const float* ph = partial + static_cast<size_t>(bh) * R * PS;
   float* sc_h = scores + static_cast<size_t>(bh) * M;
   int32_t* pos_h = pos + static_cast<size_t>(bh) * M;
 
+  // 0. the chunk keys' masses (first kMuRegs keys per thread) are fetched now
+  // and summed at the end: unconditional loads from valid rows
+  float mup[kMuRegs][kMaxSplits];
+#pragma unroll
+  for (int k = 0; k < kMuRegs; ++k) {
+    const int jj = min(tid + k * kThreads, S - 1);
+#pragma unroll
+    for (int r = 0; r < kMaxSplits; ++r) mup[k][r] = ph[static_cast<size_t>(min(r, R - 1)) * PS + M + jj];
+  }
+
   // 1. scores after this step's mass; slot classes; AND/OR of candidate keys
-  int my_free = 0, my_cand = 0;
+  int my_free = 0, my_cand = 0;     // wave-uniform counts (ballots)
   uint32_t k_and = 0xffffffffu, k_or = 0u;
 #pragma unroll 2
   for (int m = tid; m < M; m += kThreads) {
     const int p = pos_h[m];
     float s = sc_h[m];
-    // all R partials in flight at once: unconditional loads from valid rows
     float part[kMaxSplits];
 #pragma unroll
     for (int r = 0; r < kMaxSplits; ++r) part[r] = ph[static_cast<size_t>(min(r, R - 1)) * PS + m];
@@ -149,16 +158,35 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     const uint32_t key = order_key(s);
     s_key[m] = key;
     s_fl[m] = fl;
-    my_free += fl == kFree;
-    my_cand += fl == kCand;
+    my_free += __builtin_popcountll(__ballot(fl == kFree));
+    my_cand += __builtin_popcountll(__ballot(fl == kCand));
     if (fl == kCand) {
       k_and &= key;
       k_or |= key;
     }
   }
-  int n_free, n_cand;
-  block_excl_scan(my_free, s_tmp, n_free);
-  block_excl_scan(my_cand, s_tmp, n_cand);
+  for (int i = tid; i < 2 * (kWavesSel / 2) * 256; i += kThreads) (&hist[0][0][0])[i] = 0;
+  // 2. counts (free | candidates << 16: each at most M <= 16384) and the
+  // candidates' common bits, one barrier
+  {
+    const int packed = my_free | (my_cand << 16);
+    const uint32_t wa = wave_and(k_and), wo = wave_or(k_or);
+    if (lane == 0) {
+      s_red[0][wave] = packed;
+      s_red[1][wave] = static_cast<int>(wa);
+      s_red[2][wave] = static_cast<int>(wo);
+    }
+  }
+  __syncthreads();
+  int tot = 0;
+  uint32_t all_and = 0xffffffffu, all_or = 0u;
+#pragma unroll
+  for (int w = 0; w < kWavesSel; ++w) {
+    tot += s_red[0][w];
+    all_and &= static_cast<uint32_t>(s_red[1][w]);
+    all_or |= static_cast<uint32_t>(s_red[2][w]);
+  }
+  const int n_free = tot & 0xffff, n_cand = tot >> 16;
   const int n_f = min(S, n_free);
   const int n_e = S - n_f;
   if (n_cand < n_e) {                      // infeasible adopted state: no slot is written
@@ -169,62 +197,88 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     return;
   }
 
-  // 2. radix select of the n_e-th smallest candidate key
+  // 3. radix select of the n_e-th smallest candidate key over the bits the
+  // candidates do not all share, 8 bits per pass, one barrier per pass:
+  // histograms rotate through three buffers (a buffer is cleared two passes
+  // before its use, after every wave has read it) and every wave finds the
+  // digit itself
   uint32_t thr = 0;
   int k_eq = 0;
   if (n_e > 0) {
-    uint32_t all_and, all_or;
-    block_and_or(k_and, k_or, s_utmp, all_and, all_or);
-    const uint32_t differ = all_and ^ all_or;           // bits not shared by every candidate
+    const uint32_t differ = all_and ^ all_or;
     uint32_t prefix = all_and & ~differ, pmask = ~differ;
     int kk = n_e;
     int top = differ ? 31 - __builtin_clz(differ) : -1;  // highest differing bit
+    int pass = 0;
     while (top >= 0) {
       const int shift = top >= 7 ? top - 7 : 0;
       const uint32_t dmask = (top >= 7 ? 0xffu : ((1u << (top + 1)) - 1u)) << shift;
-      __syncthreads();
-      if (tid < 256) hist[tid] = 0;
-      __syncthreads();
+      uint32_t (*h)[256] = hist[pass % 3];
+      uint32_t* hw = h[wave >> 1];
       for (int m = tid; m < M; m += kThreads) {
         if (s_fl[m] != kCand) continue;
         const uint32_t u = s_key[m];
-        if ((u & pmask) == prefix) atomicAdd(&hist[(u & dmask) >> shift], 1u);
+        if ((u & pmask) == prefix) atomicAdd(&hw[(u & dmask) >> shift], 1u);
       }
       __syncthreads();
-      if (tid < 64) {
-        int c[4], tot = 0;
+      for (int i = tid; i < (kWavesSel / 2) * 256; i += kThreads) (&hist[(pass + 2) % 3][0][0])[i] = 0;
+      int c[4] = {0, 0, 0, 0}, sum = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) { c[q] = static_cast<int>(hist[4 * tid + q]); tot += c[q]; }
-        int cb = wave_incl_scan(tot, lane) - tot;
+      for (int wp = 0; wp < kWavesSel / 2; ++wp) {
+        const uint4 v = *reinterpret_cast<const uint4*>(&h[wp][4 * lane]);
+        c[0] += static_cast<int>(v.x);
+        c[1] += static_cast<int>(v.y);
+        c[2] += static_cast<int>(v.z);
+        c[3] += static_cast<int>(v.w);
+      }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (cb < kk && kk <= cb + c[q]) { s_sel[0] = 4 * tid + q; s_sel[1] = cb; }
-          cb += c[q];
+      for (int q = 0; q < 4; ++q) sum += c[q];
+      int cb = wave_incl_scan(sum) - sum;
+      int digit = 0, before = 0;
+      bool found = false;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (!found && cb < kk && kk <= cb + c[q]) {
+          found = true;
+          digit = 4 * lane + q;
+          before = cb;
         }
+        cb += c[q];
       }
-      __syncthreads();
-      prefix |= static_cast<uint32_t>(s_sel[0]) << shift;
+      const uint64_t bal = __ballot(found);
+      const int src = bal ? static_cast<int>(__builtin_ctzll(bal)) : 0;   // exactly one lane finds it
+      digit = __builtin_amdgcn_readlane(digit, src);
+      before = __builtin_amdgcn_readlane(before, src);
+      prefix |= static_cast<uint32_t>(digit) << shift;
       pmask |= dmask;
-      kk -= s_sel[1];
+      kk -= before;
       top = shift - 1;
+      ++pass;
     }
     thr = prefix;
     k_eq = kk;      // how many candidates with key == thr are taken (lowest slots)
   }
 
-  // 3. targets in ascending slot order: each thread owns a contiguous slot range
+  // 4. targets in ascending slot order: each thread owns a contiguous slot
+  // range.  One scan of (free | equal << 16, below) gives each range's first
+  // target index: the free targets are the first n_f free slots and the
+  // equal ones the first k_eq candidates with key == thr.
   const int per = (M + kThreads - 1) / kThreads;
   const int lo = min(M, tid * per), hi = min(M, lo + per);
-  int c_free = 0, c_eq = 0;
+  int c_free = 0, c_eq = 0, c_lt = 0;
   for (int m = lo; m < hi; ++m) {
     const uint8_t fl = s_fl[m];
     c_free += fl == kFree;
-    c_eq += (n_e > 0 && fl == kCand && s_key[m] == thr);
+    if (n_e > 0 && fl == kCand) {
+      const uint32_t u = s_key[m];
+      c_lt += u < thr;
+      c_eq += u == thr;
+    }
   }
-  int dummy;
-  int fr = block_excl_scan(c_free, s_tmp, dummy);
-  int eq = block_excl_scan(c_eq, s_tmp, dummy);
-  int c_t = 0;
+  int p_fe, p_lt;
+  block_excl_scan2(c_free | (c_eq << 16), c_lt, s_scan, p_fe, p_lt);
+  int fr = p_fe & 0xffff, eq = p_fe >> 16;
+  int j = min(fr, n_f) + p_lt + min(eq, k_eq);
   for (int m = lo; m < hi; ++m) {
     const uint8_t fl = s_fl[m];
     bool t = false;
@@ -236,30 +290,41 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       t = (u < thr) || (u == thr && eq < k_eq);
       eq += u == thr;
     }
-    if (t) s_fl[m] = fl | kTarget;
-    else if (fl != kFree) sc_h[m] = key_value(s_key[m]);    // kept filled slot: new score
-    c_t += t;
+    if (t) {
+      s_fl[m] = fl | kTarget;
+      s_R[j++] = m;
+    } else if (fl != kFree) {
+      sc_h[m] = key_value(s_key[m]);    // kept filled slot: new score
+    }
   }
-  int j = block_excl_scan(c_t, s_tmp, dummy);
-  for (int m = lo; m < hi; ++m)
-    if ((s_fl[m] & kTarget) && j < S) s_R[j++] = m;
   __syncthreads();
 
-  // 4. targets: score = mass from the chunk's own queries, position T + j
-  for (int jj = tid; jj < S; jj += kThreads) {
+  // 5. targets: score = mass from the chunk's own queries, position T + j
+  auto write_target = [&](int jj, float mu) __attribute__((always_inline)) {
     const int slot = s_R[jj];
-    float part[kMaxSplits];
-#pragma unroll
-    for (int r = 0; r < kMaxSplits; ++r) part[r] = ph[static_cast<size_t>(min(r, R - 1)) * PS + M + jj];
-    float mu = 0.f;
-#pragma unroll
-    for (int r = 0; r < kMaxSplits; ++r) mu += (r < R) ? part[r] : 0.f;
     sc_h[slot] = mu;
     pos_h[slot] = T + jj;
     const bool was_free = (s_fl[slot] & 3) == kFree;
     targets[static_cast<size_t>(bh) * S + jj] = was_free ? (slot | kWasFree) : slot;
     if (slots_out) slots_out[static_cast<size_t>(bh) * S + jj] = slot;
     if (step_mass) step_mass[static_cast<size_t>(bh) * PS + M + jj] = mu;
+  };
+#pragma unroll
+  for (int k = 0; k < kMuRegs; ++k) {
+    const int jj = tid + k * kThreads;
+    float mu = 0.f;
+#pragma unroll
+    for (int r = 0; r < kMaxSplits; ++r) mu += (r < R) ? mup[k][r] : 0.f;
+    if (jj < S) write_target(jj, mu);
+  }
+  for (int jj = tid + kMuRegs * kThreads; jj < S; jj += kThreads) {
+    float part[kMaxSplits];
+#pragma unroll
+    for (int r = 0; r < kMaxSplits; ++r) part[r] = ph[static_cast<size_t>(min(r, R - 1)) * PS + M + jj];
+    float mu = 0.f;
+#pragma unroll
+    for (int r = 0; r < kMaxSplits; ++r) mu += (r < R) ? part[r] : 0.f;
+    write_target(jj, mu);
   }
 }
 
