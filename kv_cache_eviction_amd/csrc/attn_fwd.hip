@@ -76,7 +76,7 @@ __device__ __forceinline__ int v_chunk(int row, int c) {
   return c ^ ((row & 3) << (CPR == 16 ? 2 : 1));
 }
 
-template <int D>
+template <int D, bool DEC>
 __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc,
     const bf16_t* __restrict__ Vc, const int32_t* __restrict__ pos,
@@ -120,15 +120,35 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   const int wgi = wg_per_head - 1 - static_cast<int>(blockIdx.x) / n_heads;
   const int b = bh / Hkv, kvh = bh - b * Hkv;
   const int G = Hq / Hkv;
-  const int n_rb = G * ((S + 31) >> 5);
-  const int rb = wgi * kRowBlocks + rbw;
+  const int n_rb = DEC ? (G * S + 31) >> 5 : G * ((S + 31) >> 5);
+  // Row blocks.  Chunk layout: row block = 32 consecutive queries of one
+  // head, numbered (query block, head); the workgroup's 4 waves of a group
+  // own 4 row blocks.  Short-chunk layout (DEC, S < 32): the G*S rows
+  // (head, query) of the KV group are packed 32 to a row block, and the
+  // group's waves are 2 row blocks x 2 key halves: wave kh takes keys
+  // 32 kh..32 kh+31 of every tile, so no MFMA works on padding rows.
+  constexpr int RBW = DEC ? 2 : kRowBlocks;     // row blocks per workgroup
+  const int rbp = DEC ? (rbw >> 1) : rbw;
+  const int kh = DEC ? (rbw & 1) : 0;
+  const int rb = wgi * RBW + rbp;
   const bool active = rb < n_rb;
-  const int g = active ? rb % G : 0;
-  const int qb = active ? rb / G : 0;
-  const int qi = qb * 32 + col;
+  int g, qb, qi;
+  bool row_ok;                                  // this lane's row exists
+  if constexpr (DEC) {
+    const int R = rb * 32 + col;
+    row_ok = active && R < G * S;
+    g = row_ok ? R / S : 0;
+    qi = row_ok ? R - g * S : 0;
+    qb = 0;
+  } else {
+    g = active ? rb % G : 0;
+    qb = active ? rb / G : 0;
+    qi = qb * 32 + col;
+    row_ok = active && qi < S;
+  }
   const int hq = kvh * G + g;
-  const int rb_last = min(wgi * kRowBlocks + kRowBlocks - 1, n_rb - 1);
-  const int n_chunk_keys = min(S, (rb_last / G + 1) * 32);
+  const int rb_last = min(wgi * RBW + RBW - 1, n_rb - 1);
+  const int n_chunk_keys = DEC ? S : min(S, (rb_last / G + 1) * 32);
   const int n_ct = (n_cache + kKT - 1) / kKT;
   const int n_tiles = n_ct + (n_chunk_keys + kKT - 1) / kKT;
   // group g takes tiles 2t + g, t < n_iter (even: the loop body is unrolled
@@ -149,7 +169,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   // The wave's queries: B operand of S^T = K Q^T (lane: query col, d 8hf..+8).
   bf16x8 qf[DS];
   {
-    const bool qok = active && qi < S;
+    const bool qok = row_ok;
     const bf16_t* qrow = Q + (static_cast<size_t>(b * Hq + hq) * S + (qok ? qi : 0)) * D;
 #pragma unroll
     for (int st = 0; st < DS; ++st) {
@@ -251,26 +271,29 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   uint32_t k_rd[DS], v_rd[DB];
   {
 #pragma unroll
-    for (int st = 0; st < DS; ++st) k_rd[st] = col * RB + 16 * k_chunk<CPR>(col, 2 * st + hf);
+    for (int st = 0; st < DS; ++st) k_rd[st] = (32 * kh + col) * RB + 16 * k_chunk<CPR>(col, 2 * st + hf);
     const int tr_j = lane & 15, tr_r = tr_j >> 2, tr_q = tr_j & 3, tr_dg = (lane >> 4) & 1;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int d = db * 32 + tr_dg * 16 + 4 * tr_q;
-      v_rd[db] = (16 * hf + tr_r) * RB + 16 * v_chunk<CPR>(tr_r, d >> 3) + 2 * (d & 7);
+      v_rd[db] = (32 * kh + 16 * hf + tr_r) * RB + 16 * v_chunk<CPR>(tr_r, d >> 3) + 2 * (d & 7);
     }
   }
 
-  // S^T of one tile: register r of a0 (a1) <-> key 16(l/32) + r (+32)
+  // S^T of one tile: register r of a0 (a1) <-> key 16(l/32) + r (+32); in
+  // the short-chunk layout only a0, for the wave's key half
   auto qk = [&](auto g, auto slot, f32x16& a0, f32x16& a1) __attribute__((always_inline)) {
     const char* kt = kbuf(g, slot);
     a0 = zero16();
-    a1 = zero16();
+    if constexpr (!DEC) a1 = zero16();
 #pragma unroll
     for (int st = 0; st < DS; ++st) {
       const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + k_rd[st]);
-      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(kt + 32 * RB + k_rd[st]);
       a0 = mfma32x32x16(ka, qf[st], a0);
-      a1 = mfma32x32x16(kb, qf[st], a1);
+      if constexpr (!DEC) {
+        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(kt + 32 * RB + k_rd[st]);
+        a1 = mfma32x32x16(kb, qf[st], a1);
+      }
     }
   };
   // O^T += V^T P^T; MFMA (kb,u) covers keys 32kb + 16(l/32) + 8u + e.  The A
@@ -279,7 +302,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   auto pv = [&](auto g, auto slot, const bf16x8 (&pb)[4]) __attribute__((always_inline)) {
     const char* vt = vbuf(g, slot);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < (DEC ? 1 : 2); ++kb)
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -298,22 +321,31 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float p0 = fast_exp2(fmaf(a0[r], c2, -m_run));
-      const float p1 = fast_exp2(fmaf(a1[r], c2, -m_run));
       t[r >> 3][r & 7] = p0;
-      t[2 + (r >> 3)][r & 7] = p1;
       rs0 += p0;
-      rs1 += p1;
+      if constexpr (!DEC) {
+        const float p1 = fast_exp2(fmaf(a1[r], c2, -m_run));
+        t[2 + (r >> 3)][r & 7] = p1;
+        rs1 += p1;
+      }
     }
     l_run += rs0 + rs1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pb[i] = to_bf16x8(t[i]);
+    for (int i = 0; i < (DEC ? 2 : 4); ++i) pb[i] = to_bf16x8(t[i]);
   };
   // largest raw score of the lane's 32 entries (v_maximum3_f32; NaN-propagating)
   auto tile_max = [&](const f32x16& a0, const f32x16& a1) __attribute__((always_inline)) {
-    float mx = __builtin_elementwise_maximum(a0[0], a1[0]);
+    if constexpr (DEC) {
+      float mx = __builtin_elementwise_maximum(a0[0], a0[1]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(a0[r], a1[r]));
-    return mx;
+      for (int r = 2; r < 16; r += 2) mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(a0[r], a0[r + 1]));
+      return mx;
+    } else {
+      float mx = __builtin_elementwise_maximum(a0[0], a1[0]);
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(a0[r], a1[r]));
+      return mx;
+    }
   };
   // masks global tile T's scores (then the maximum mx of the raw scores is
   // recomputed over the visible ones), and moves the running maximum (with
@@ -331,17 +363,20 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
       const int n = S - base;
       vm = n >= 64 ? ~0ull : ((1ull << n) - 1);
     }
-    const bool causal = exists && !is_cache && (base + kKT - 1 > qb * 32);
-    if (vm != ~0ull || causal) {
+    const bool causal = exists && !is_cache && (DEC || base + kKT - 1 > qb * 32);
+    if constexpr (DEC) vm = (vm >> (32 * kh)) & 0xffffffffull;   // the wave's key half
+    if (vm != (DEC ? 0xffffffffull : ~0ull) || causal) {
       const uint32_t bits0 = static_cast<uint32_t>(vm >> (16 * hf)) & 0xffffu;
       const uint32_t bits1 = static_cast<uint32_t>(vm >> (32 + 16 * hf)) & 0xffffu;
-      const int lim_i = causal ? qi - base - 16 * hf : (1 << 30);   // key offset bound
+      const int lim_i = causal ? qi - base - 16 * hf - 32 * kh : (1 << 30);   // key offset bound
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const bool ok0 = ((bits0 >> r) & 1u) && (r <= lim_i);
-        const bool ok1 = ((bits1 >> r) & 1u) && (32 + r <= lim_i);
         a0[r] = ok0 ? a0[r] : kNegInf;
-        a1[r] = ok1 ? a1[r] : kNegInf;
+        if constexpr (!DEC) {
+          const bool ok1 = ((bits1 >> r) & 1u) && (32 + r <= lim_i);
+          a1[r] = ok1 ? a1[r] : kNegInf;
+        }
       }
       mx = tile_max(a0, a1);
     }
@@ -445,45 +480,55 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   if (grp == 0) run_group(I0{});
   else run_group(I1{});
 
-  // ---- merge the two groups' softmax states (group 1 -> LDS -> group 0),
-  // one 32-row block of O^T per round through a K slot
+  // ---- merge the partial softmax states of a row block: writer waves pass
+  // (m, l, O^T) through LDS (one 32-row block of O^T per round, through a K
+  // slot) to the reader wave that holds the same rows.  Chunk layout: group
+  // 1 -> group 0.  Short-chunk layout: key half 1 -> key half 0 in each
+  // group, then group 1 -> group 0.
   wait_vmem_all();
   barrier_lds();
-  constexpr int NX = kRowBlocks * 64;                     // lanes of a group
+  constexpr int NX = kRowBlocks * 64;                     // exchange slots
   float* xo = reinterpret_cast<float*>(k00);              // 16 x NX floats
-  float* xm = reinterpret_cast<float*>(k01);              // m, l of group 1
-  const int slot = rbw * 64 + lane;
-  if (grp == 1) {
-    xm[slot] = m_run;
-    xm[NX + slot] = l_run;
-  }
-  barrier_lds();
-  float a0 = 1.f, a1 = 0.f;
-  if (grp == 0) {
-    const float m1 = xm[slot];
-    const float l1 = xm[NX + slot];
-    const float m = fmaxf(m_run, m1);
-    a0 = fast_exp2(m_run - m);
-    a1 = fast_exp2(m1 - m);
-    l_run = l_run * a0 + l1 * a1;
-    m_run = m;
-  }
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    if (grp == 1) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) xo[r * NX + slot] = o[db][r];
+  float* xm = reinterpret_cast<float*>(k01);              // m, l
+  auto fold = [&](bool writer, bool reader, int slot) __attribute__((always_inline)) {
+    if (writer) {
+      xm[slot] = m_run;
+      xm[NX + slot] = l_run;
     }
     barrier_lds();
-    if (grp == 0) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + xo[r * NX + slot] * a1;
+    float a0 = 1.f, a1 = 0.f;
+    if (reader) {
+      const float m1 = xm[slot];
+      const float l1 = xm[NX + slot];
+      const float m = fmaxf(m_run, m1);
+      a0 = fast_exp2(m_run - m);
+      a1 = fast_exp2(m1 - m);
+      l_run = l_run * a0 + l1 * a1;
+      m_run = m;
     }
-    barrier_lds();
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      if (writer) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[r * NX + slot] = o[db][r];
+      }
+      barrier_lds();
+      if (reader) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + xo[r * NX + slot] * a1;
+      }
+      barrier_lds();
+    }
+  };
+  if constexpr (DEC) {
+    fold(kh == 1, kh == 0, (grp * 2 + rbp) * 64 + lane);
+    fold(grp == 1 && kh == 0, grp == 0 && kh == 0, rbp * 64 + lane);
+  } else {
+    fold(grp == 1, grp == 0, rbw * 64 + lane);
   }
-  if (grp == 1 || !active) return;
+  if (grp == 1 || kh == 1 || !active) return;
   const float l_tot = l_run + xor32(l_run);
-  if (qi >= S) return;
+  if (!row_ok) return;
   const float inv = 1.f / l_tot;
   bf16_t* orow = O + (static_cast<size_t>(b * Hq + hq) * S + qi) * D;
 #pragma unroll
@@ -581,19 +626,28 @@ hipError_t launch_attn_fwd(const StepShape& sh, const AttnArgs& a, int dtype, hi
   const int G = sh.Hq / sh.Hkv;
   const float c2 = sh.scale * kLog2e;
   if (dtype == kBF16) {
-    const int n_rb = G * ((sh.S + 31) / 32);
-    const int wgp = (n_rb + kRowBlocks - 1) / kRowBlocks;
+    // short chunks pack the G*S rows of a KV group densely (see the kernel)
+    const bool dec = sh.S < 32;
+    const int n_rb = dec ? (G * sh.S + 31) / 32 : G * ((sh.S + 31) / 32);
+    const int rbw = dec ? 2 : kRowBlocks;
+    const int wgp = (n_rb + rbw - 1) / rbw;
     const dim3 grid(n_heads * wgp), block(kFwdThreads);
-#define H2O_LAUNCH_FWD(DD)                                                                          \
-  hipLaunchKernelGGL(attn_fwd_bf16_kernel<DD>, grid, block, 0, st,                                  \
+#define H2O_LAUNCH_FWD1(DD, DEC)                                                                    \
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(attn_fwd_bf16_kernel<DD, DEC>), grid, block, 0, st,            \
                      static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k_cache),        \
                      static_cast<const bf16_t*>(a.v_cache), a.pos,                                  \
                      static_cast<const bf16_t*>(a.k_new), static_cast<const bf16_t*>(a.v_new),      \
                      static_cast<bf16_t*>(a.out), a.lse, sh.Hq, sh.Hkv, sh.S, sh.M, sh.n_cache, c2, \
                      n_heads, wgp)
-    if (sh.D == 128) H2O_LAUNCH_FWD(128);
-    else H2O_LAUNCH_FWD(64);
+#define H2O_LAUNCH_FWD(DD) \
+  if (dec) H2O_LAUNCH_FWD1(DD, true); else H2O_LAUNCH_FWD1(DD, false)
+    if (sh.D == 128) {
+      H2O_LAUNCH_FWD(128);
+    } else {
+      H2O_LAUNCH_FWD(64);
+    }
 #undef H2O_LAUNCH_FWD
+#undef H2O_LAUNCH_FWD1
   } else {
     const int wgp = (G * sh.S + 63) / 64;
     const dim3 grid(n_heads * wgp), block(64);

@@ -81,6 +81,15 @@ SMALL_BF16 = {
                          total_len=64 + 96 * 7, cache_slots=512, recent_window=64, qk_std=1.0),
     "g2_small_chunks": dict(batch=3, n_q_heads=4, n_kv_heads=2, head_dim=128, prefill=96, chunk=5,
                             total_len=96 + 5 * 12, cache_slots=100, recent_window=9, qk_std=1.0),
+    # short chunks (S < 32): rows of several heads packed into one row block
+    "g8_short16": dict(batch=2, n_q_heads=16, n_kv_heads=2, head_dim=128, prefill=64, chunk=16,
+                       total_len=64 + 16 * 8, cache_slots=128, recent_window=16, qk_std=1.0),
+    "g4_short31_d64": dict(batch=1, n_q_heads=8, n_kv_heads=2, head_dim=64, prefill=70, chunk=31,
+                           total_len=70 + 31 * 6, cache_slots=150, recent_window=20, qk_std=1.0),
+    "g3_decode1": dict(batch=2, n_q_heads=6, n_kv_heads=2, head_dim=128, prefill=50, chunk=1,
+                       total_len=50 + 1 * 20, cache_slots=60, recent_window=8, qk_std=1.0),
+    "g1_short20": dict(batch=1, n_q_heads=2, n_kv_heads=2, head_dim=128, prefill=40, chunk=20,
+                       total_len=40 + 20 * 5, cache_slots=80, recent_window=10, qk_std=1.0),
 }
 
 
