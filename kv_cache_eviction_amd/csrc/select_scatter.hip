@@ -103,15 +103,16 @@ __device__ void block_excl_scan2(int a, int b, int* tmp, int& pa, int& pb) {
   pb = bb + ib - b;
 }
 
+// Thread t owns the SPT consecutive slots t*SPT .. t*SPT+SPT-1 (SPT*512 >= M)
+// and keeps their keys and classes in registers through every phase.
+template <int SPT>
 __global__ __launch_bounds__(kThreads) void select_kernel(
     float* __restrict__ scores, int32_t* __restrict__ pos, const float* __restrict__ partial,
     int R, int32_t* __restrict__ targets, int32_t* __restrict__ slots_out,
     float* __restrict__ step_mass, int32_t* __restrict__ status, int T, int W, int S, int M,
-    int n_cache) {
+    int n_cache, int vec) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  uint32_t* s_key = reinterpret_cast<uint32_t*>(smem);                        // [M]
-  int* s_R = reinterpret_cast<int*>(smem + 4 * static_cast<size_t>(M));      // [S]
-  uint8_t* s_fl = reinterpret_cast<uint8_t*>(smem + 4 * static_cast<size_t>(M) + 4 * static_cast<size_t>(S));
+  int* s_R = reinterpret_cast<int*>(smem);                 // [S]: target of chunk row j (flagged)
   __shared__ __attribute__((aligned(16))) uint32_t hist[3][kWavesSel / 2][256];   // per wave pair, 3 rotating
   __shared__ int s_red[3][kWavesSel];
   __shared__ int s_scan[2 * kWavesSel];
@@ -122,9 +123,11 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   const float* ph = partial + static_cast<size_t>(bh) * R * PS;
   float* sc_h = scores + static_cast<size_t>(bh) * M;
   int32_t* pos_h = pos + static_cast<size_t>(bh) * M;
+  const int m0 = tid * SPT;
 
-  // 0. the chunk keys' masses (first kMuRegs keys per thread) are fetched now
-  // and summed at the end: unconditional loads from valid rows
+  // 0. every load up front: the chunk keys' masses (first kMuRegs keys per
+  // thread, summed at the end), then the thread's slots (position, score
+  // and the R per-split masses; splits past R re-read split R-1)
   float mup[kMuRegs][kMaxSplits];
 #pragma unroll
   for (int k = 0; k < kMuRegs; ++k) {
@@ -132,47 +135,83 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
 #pragma unroll
     for (int r = 0; r < kMaxSplits; ++r) mup[k][r] = ph[static_cast<size_t>(min(r, R - 1)) * PS + M + jj];
   }
+  int pv[SPT];
+  float sv[SPT], dv[SPT];
+  if (SPT % 4 == 0 && vec && m0 + SPT <= M) {
+    // 16-byte loads of the thread's slots (rows aligned: M, S multiples of 4)
+#pragma unroll
+    for (int i = 0; i < SPT; i += 4) {
+      const int4 p4 = *reinterpret_cast<const int4*>(pos_h + m0 + i);
+      const float4 s4 = *reinterpret_cast<const float4*>(sc_h + m0 + i);
+      pv[i] = p4.x; pv[i + 1] = p4.y; pv[i + 2] = p4.z; pv[i + 3] = p4.w;
+      sv[i] = s4.x; sv[i + 1] = s4.y; sv[i + 2] = s4.z; sv[i + 3] = s4.w;
+      float4 part[kMaxSplits];
+#pragma unroll
+      for (int r = 0; r < kMaxSplits; ++r)
+        part[r] = *reinterpret_cast<const float4*>(ph + static_cast<size_t>(min(r, R - 1)) * PS + m0 + i);
+      float4 ds = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < kMaxSplits; ++r) {
+        if (r < R) {
+          ds.x += part[r].x;
+          ds.y += part[r].y;
+          ds.z += part[r].z;
+          ds.w += part[r].w;
+        }
+      }
+      dv[i] = ds.x; dv[i + 1] = ds.y; dv[i + 2] = ds.z; dv[i + 3] = ds.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int m = min(m0 + i, M - 1);
+      pv[i] = pos_h[m];
+      sv[i] = sc_h[m];
+      float part[kMaxSplits];
+#pragma unroll
+      for (int r = 0; r < kMaxSplits; ++r) part[r] = ph[static_cast<size_t>(min(r, R - 1)) * PS + m];
+      float ds = 0.f;
+#pragma unroll
+      for (int r = 0; r < kMaxSplits; ++r) ds += (r < R) ? part[r] : 0.f;
+      dv[i] = ds;
+    }
+  }
 
-  // 1. scores after this step's mass; slot classes; AND/OR of candidate keys
-  int my_free = 0, my_cand = 0;     // wave-uniform counts (ballots)
+  // 1. scores after this step's mass, slot classes (bit masks), candidate
+  // AND/OR, counts
+  uint32_t key[SPT];
+  uint32_t fmask = 0, cmask = 0;
   uint32_t k_and = 0xffffffffu, k_or = 0u;
-#pragma unroll 2
-  for (int m = tid; m < M; m += kThreads) {
-    const int p = pos_h[m];
-    float s = sc_h[m];
-    float part[kMaxSplits];
 #pragma unroll
-    for (int r = 0; r < kMaxSplits; ++r) part[r] = ph[static_cast<size_t>(min(r, R - 1)) * PS + m];
-    float ds = 0.f;
-#pragma unroll
-    for (int r = 0; r < kMaxSplits; ++r) ds += (r < R) ? part[r] : 0.f;
-    if (m >= n_cache) ds = 0.f;
-    uint8_t fl = kFree;
-    if (p >= 0) {
-      s += ds;
-      fl = (p < T - W) ? kCand : kKeep;
+  for (int i = 0; i < SPT; ++i) {
+    const int m = m0 + i;
+    const bool exists = m < M;
+    float ds = m < n_cache ? dv[i] : 0.f;
+    float sc = sv[i];
+    if (pv[i] >= 0) {
+      sc += ds;
+      if (pv[i] < T - W) cmask |= 1u << i;
     } else {
       ds = 0.f;
+      if (exists) fmask |= 1u << i;
     }
-    if (step_mass) step_mass[static_cast<size_t>(bh) * PS + m] = ds;
-    const uint32_t key = order_key(s);
-    s_key[m] = key;
-    s_fl[m] = fl;
-    my_free += __builtin_popcountll(__ballot(fl == kFree));
-    my_cand += __builtin_popcountll(__ballot(fl == kCand));
-    if (fl == kCand) {
-      k_and &= key;
-      k_or |= key;
+    if (!exists) cmask &= ~(1u << i);
+    if (step_mass && exists) step_mass[static_cast<size_t>(bh) * PS + m] = ds;
+    key[i] = order_key(sc);
+    if ((cmask >> i) & 1u) {
+      k_and &= key[i];
+      k_or |= key[i];
     }
   }
   for (int i = tid; i < 2 * (kWavesSel / 2) * 256; i += kThreads) (&hist[0][0][0])[i] = 0;
   // 2. counts (free | candidates << 16: each at most M <= 16384) and the
   // candidates' common bits, one barrier
   {
-    const int packed = my_free | (my_cand << 16);
+    const int cnt = __builtin_popcount(fmask) | (__builtin_popcount(cmask) << 16);
+    const int wsum = __builtin_amdgcn_readlane(wave_incl_scan(cnt), 63);
     const uint32_t wa = wave_and(k_and), wo = wave_or(k_or);
     if (lane == 0) {
-      s_red[0][wave] = packed;
+      s_red[0][wave] = wsum;
       s_red[1][wave] = static_cast<int>(wa);
       s_red[2][wave] = static_cast<int>(wo);
     }
@@ -190,8 +229,9 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   const int n_f = min(S, n_free);
   const int n_e = S - n_f;
   if (n_cand < n_e) {                      // infeasible adopted state: no slot is written
-    for (int m = tid; m < M; m += kThreads)
-      if (s_fl[m] != kFree) sc_h[m] = key_value(s_key[m]);
+#pragma unroll
+    for (int i = 0; i < SPT; ++i)
+      if (m0 + i < M && !((fmask >> i) & 1u)) sc_h[m0 + i] = key_value(key[i]);
     for (int jj = tid; jj < S; jj += kThreads) targets[static_cast<size_t>(bh) * S + jj] = -1;
     if (tid == 0) atomicOr(status, 1);
     return;
@@ -215,11 +255,9 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       const uint32_t dmask = (top >= 7 ? 0xffu : ((1u << (top + 1)) - 1u)) << shift;
       uint32_t (*h)[256] = hist[pass % 3];
       uint32_t* hw = h[wave >> 1];
-      for (int m = tid; m < M; m += kThreads) {
-        if (s_fl[m] != kCand) continue;
-        const uint32_t u = s_key[m];
-        if ((u & pmask) == prefix) atomicAdd(&hw[(u & dmask) >> shift], 1u);
-      }
+#pragma unroll
+      for (int i = 0; i < SPT; ++i)
+        if (((cmask >> i) & 1u) && (key[i] & pmask) == prefix) atomicAdd(&hw[(key[i] & dmask) >> shift], 1u);
       __syncthreads();
       for (int i = tid; i < (kWavesSel / 2) * 256; i += kThreads) (&hist[(pass + 2) % 3][0][0])[i] = 0;
       int c[4] = {0, 0, 0, 0}, sum = 0;
@@ -259,53 +297,57 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     k_eq = kk;      // how many candidates with key == thr are taken (lowest slots)
   }
 
-  // 4. targets in ascending slot order: each thread owns a contiguous slot
-  // range.  One scan of (free | equal << 16, below) gives each range's first
-  // target index: the free targets are the first n_f free slots and the
-  // equal ones the first k_eq candidates with key == thr.
-  const int per = (M + kThreads - 1) / kThreads;
-  const int lo = min(M, tid * per), hi = min(M, lo + per);
-  int c_free = 0, c_eq = 0, c_lt = 0;
-  for (int m = lo; m < hi; ++m) {
-    const uint8_t fl = s_fl[m];
-    c_free += fl == kFree;
-    if (n_e > 0 && fl == kCand) {
-      const uint32_t u = s_key[m];
-      c_lt += u < thr;
-      c_eq += u == thr;
+  // 4. targets in ascending slot order.  One scan of (free | equal << 16,
+  // below) gives each thread's first target index: the free targets are the
+  // first n_f free slots and the equal ones the first k_eq candidates with
+  // key == thr.
+  int c_eq = 0, c_lt = 0;
+  if (n_e > 0) {
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const bool cand = (cmask >> i) & 1u;
+      c_lt += cand && key[i] < thr;
+      c_eq += cand && key[i] == thr;
     }
   }
   int p_fe, p_lt;
-  block_excl_scan2(c_free | (c_eq << 16), c_lt, s_scan, p_fe, p_lt);
+  block_excl_scan2(__builtin_popcount(fmask) | (c_eq << 16), c_lt, s_scan, p_fe, p_lt);
   int fr = p_fe & 0xffff, eq = p_fe >> 16;
   int j = min(fr, n_f) + p_lt + min(eq, k_eq);
-  for (int m = lo; m < hi; ++m) {
-    const uint8_t fl = s_fl[m];
+  float nsc[SPT];                      // new scores of kept slots (targets: rewritten below)
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) {
+    const int m = m0 + i;
+    const bool fre = (fmask >> i) & 1u;
     bool t = false;
-    if (fl == kFree) {
+    if (fre) {
       t = fr < n_f;
       ++fr;
-    } else if (fl == kCand && n_e > 0) {
-      const uint32_t u = s_key[m];
-      t = (u < thr) || (u == thr && eq < k_eq);
-      eq += u == thr;
+    } else if (((cmask >> i) & 1u) && n_e > 0) {
+      t = (key[i] < thr) || (key[i] == thr && eq < k_eq);
+      eq += key[i] == thr;
     }
-    if (t) {
-      s_fl[m] = fl | kTarget;
-      s_R[j++] = m;
-    } else if (fl != kFree) {
-      sc_h[m] = key_value(s_key[m]);    // kept filled slot: new score
-    }
+    if (t) s_R[j++] = fre ? (m | kWasFree) : m;
+    nsc[i] = fre ? sv[i] : key_value(key[i]);
   }
-  __syncthreads();
+  if (SPT % 4 == 0 && vec && m0 + SPT <= M) {
+#pragma unroll
+    for (int i = 0; i < SPT; i += 4)
+      *reinterpret_cast<float4*>(sc_h + m0 + i) = float4{nsc[i], nsc[i + 1], nsc[i + 2], nsc[i + 3]};
+  } else {
+#pragma unroll
+    for (int i = 0; i < SPT; ++i)
+      if (m0 + i < M && !((fmask >> i) & 1u)) sc_h[m0 + i] = nsc[i];
+  }
+  __syncthreads();                     // orders these stores before the target stores below
 
   // 5. targets: score = mass from the chunk's own queries, position T + j
   auto write_target = [&](int jj, float mu) __attribute__((always_inline)) {
-    const int slot = s_R[jj];
+    const int v = s_R[jj];
+    const int slot = v & ~kWasFree;
     sc_h[slot] = mu;
     pos_h[slot] = T + jj;
-    const bool was_free = (s_fl[slot] & 3) == kFree;
-    targets[static_cast<size_t>(bh) * S + jj] = was_free ? (slot | kWasFree) : slot;
+    targets[static_cast<size_t>(bh) * S + jj] = v;
     if (slots_out) slots_out[static_cast<size_t>(bh) * S + jj] = slot;
     if (step_mass) step_mass[static_cast<size_t>(bh) * PS + M + jj] = mu;
   };
@@ -373,21 +415,33 @@ __global__ void reset_kernel(float* scores, int32_t* pos, int64_t n, int32_t* co
 }  // namespace
 
 size_t select_lds_bytes(int M, int S) {
-  return 4 * static_cast<size_t>(M) + 4 * static_cast<size_t>(S) + static_cast<size_t>(M) + 16;
+  (void)M;
+  return 4 * static_cast<size_t>(S) + 16;
 }
 
 hipError_t launch_select(const StepShape& sh, const SelectArgs& a, hipStream_t st) {
   const int n_heads = sh.B * sh.Hkv;
   const size_t lds = select_lds_bytes(sh.M, sh.S);
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(select_kernel, dim3(n_heads), dim3(kThreads), lds, st, a.scores, a.pos,
-                     a.partial, a.R, a.targets, a.slots_out, a.step_mass, a.status, a.T, sh.W, sh.S,
-                     sh.M, sh.n_cache);
-  return hipGetLastError();
+  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  const bool vec = sh.M % 4 == 0 && sh.S % 4 == 0 && al16(a.scores) && al16(a.pos) && al16(a.partial);
+  auto go = [&](auto kern) -> hipError_t {
+    if (lds > 48 * 1024) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(n_heads), dim3(kThreads), lds, st, a.scores, a.pos, a.partial, a.R,
+                       a.targets, a.slots_out, a.step_mass, a.status, a.T, sh.W, sh.S, sh.M, sh.n_cache,
+                       vec ? 1 : 0);
+    return hipGetLastError();
+  };
+  // slots per thread: the smallest power of two with 512 * SPT >= M (M <= 16384)
+  if (sh.M <= kThreads) return go(select_kernel<1>);
+  if (sh.M <= 2 * kThreads) return go(select_kernel<2>);
+  if (sh.M <= 4 * kThreads) return go(select_kernel<4>);
+  if (sh.M <= 8 * kThreads) return go(select_kernel<8>);
+  if (sh.M <= 16 * kThreads) return go(select_kernel<16>);
+  return go(select_kernel<32>);
 }
 
 hipError_t launch_scatter(const StepShape& sh, const SelectArgs& a, int dtype, hipStream_t st) {

@@ -90,6 +90,11 @@ SMALL_BF16 = {
                        total_len=50 + 1 * 20, cache_slots=60, recent_window=8, qk_std=1.0),
     "g1_short20": dict(batch=1, n_q_heads=2, n_kv_heads=2, head_dim=128, prefill=40, chunk=20,
                        total_len=40 + 20 * 5, cache_slots=80, recent_window=10, qk_std=1.0),
+    # cache sizes that give the select pass 2 and 32 slots per thread
+    "g2_m700_d64": dict(batch=1, n_q_heads=4, n_kv_heads=2, head_dim=64, prefill=600, chunk=64,
+                        total_len=600 + 64 * 4, cache_slots=700, recent_window=50, qk_std=1.0),
+    "g1_m8200_d64": dict(batch=1, n_q_heads=1, n_kv_heads=1, head_dim=64, prefill=8192, chunk=40,
+                         total_len=8192 + 40 * 3, cache_slots=8200, recent_window=64, qk_std=1.0),
 }
 
 
