@@ -46,9 +46,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     float scale, int n_heads, int wg_per_head) {
   constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
   constexpr int NCH = kBKT * CPR / 256;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[kBKT * D];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[kBKT * D];
-  __shared__ uint64_t s_valid;
+  // two buffers: the next tile is fetched into registers while the current
+  // one is computed, then stored into the other buffer
+  __shared__ __attribute__((aligned(16))) bf16_t Ks2[2][kBKT * D];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs2[2][kBKT * D];
+  __shared__ uint64_t s_valid2[2];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, col = lane & 31;
   const int bh = blockIdx.x % n_heads;
@@ -98,30 +100,52 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   const int32_t* pos_head = pos + static_cast<size_t>(bh) * M;
   const int tr_j = lane & 15, tr_r = tr_j >> 2, tr_q = tr_j & 3, tr_dg = (lane >> 4) & 1;
 
-  for (int t = 0; t < n_tiles; ++t) {
+  u32x4 fk[NCH], fv[NCH];
+  int f_pos = 0;
+  auto fetch = [&](int t) __attribute__((always_inline)) {
     const bool is_cache = t < n_ct;
     const int base = is_cache ? t * kBKT : (t - n_ct) * kBKT;
     const int lim = is_cache ? M : S;
     const bf16_t* ks = is_cache ? kc_head : kn_head;
     const bf16_t* vs = is_cache ? vc_head : vn_head;
-    __syncthreads();
 #pragma unroll
     for (int r = 0; r < NCH; ++r) {
       const int c = r * 256 + tid, key = c / CPR, ch = c % CPR;
       const int src = min(base + key, lim - 1);
-      const u32x4 kv = load_u32x4(ks + static_cast<size_t>(src) * D + ch * 8);
-      const u32x4 vv = load_u32x4(vs + static_cast<size_t>(src) * D + ch * 8);
+      fk[r] = load_u32x4(ks + static_cast<size_t>(src) * D + ch * 8);
+      fv[r] = load_u32x4(vs + static_cast<size_t>(src) * D + ch * 8);
+    }
+    if (wave == 0) f_pos = pos_head[is_cache ? min(base + lane, M - 1) : 0];
+  };
+  auto commit = [&](int t, int bf) __attribute__((always_inline)) {
+    const bool is_cache = t < n_ct;
+    const int base = is_cache ? t * kBKT : (t - n_ct) * kBKT;
+    const int lim = is_cache ? M : S;
+#pragma unroll
+    for (int r = 0; r < NCH; ++r) {
+      const int c = r * 256 + tid, key = c / CPR, ch = c % CPR;
       const int row = (key & ~31) | bkrow_of_key(key & 31);
-      store_u32x4(&Ks[row * D + 8 * bchunk<CPR>(row, ch)], kv);
-      store_u32x4(&Vs[row * D + 8 * bchunk<CPR>(row, ch)], vv);
+      store_u32x4(&Ks2[bf][row * D + 8 * bchunk<CPR>(row, ch)], fk[r]);
+      store_u32x4(&Vs2[bf][row * D + 8 * bchunk<CPR>(row, ch)], fv[r]);
     }
     if (wave == 0) {
-      const int key = base + lane;
-      const int pv = pos_head[is_cache ? min(key, M - 1) : 0];
-      const uint64_t m = __ballot(key < lim && (!is_cache || pv >= 0));
-      if (lane == 0) s_valid = m;
+      const uint64_t m = __ballot(base + lane < lim && (!is_cache || f_pos >= 0));
+      if (lane == 0) s_valid2[bf] = m;
     }
+  };
+
+  // buffer bf is rewritten two tiles after it was read, behind the barrier
+  // of the tile in between
+  if (n_tiles > 0) fetch(0);
+  for (int t = 0; t < n_tiles; ++t) {
+    const int bf = t & 1;
+    commit(t, bf);
     __syncthreads();
+    if (t + 1 < n_tiles) fetch(t + 1);
+    const bool is_cache = t < n_ct;
+    const int base = is_cache ? t * kBKT : (t - n_ct) * kBKT;
+    const bf16_t* Ks = Ks2[bf];
+    const bf16_t* Vs = Vs2[bf];
     if (!active || (!is_cache && base > qb * 32 + 31)) continue;
     // S^T and dP^T (keys x queries): register r of lane l <-> key 16(l/32) + r (+32 kb)
     f32x16 s0 = zero16(), s1 = zero16(), p0 = zero16(), p1 = zero16();
@@ -136,7 +160,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
       p0 = mfma32x32x16(va, dof[st], p0);
       p1 = mfma32x32x16(vb, dof[st], p1);
     }
-    const uint64_t vm = s_valid;
+    const uint64_t vm = s_valid2[bf];
     const bool causal = !is_cache && (base + kBKT - 1 > qb * 32);
     const uint32_t bits0 = static_cast<uint32_t>(vm >> (16 * hf)) & 0xffffu;
     const uint32_t bits1 = static_cast<uint32_t>(vm >> (32 + 16 * hf)) & 0xffffu;
@@ -197,11 +221,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     int n_ct, int n_tiles) {
   constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
   constexpr int NCH = 32 * CPR / 256;      // 16-byte chunks per thread per 32-row block
-  __shared__ __attribute__((aligned(16))) bf16_t Qs[32 * D];
-  __shared__ __attribute__((aligned(16))) bf16_t Gs[32 * D];
-  __shared__ __attribute__((aligned(16))) float s_lse2[32];
-  __shared__ __attribute__((aligned(16))) float s_D[32];
-  __shared__ __attribute__((aligned(16))) int s_irow[32];
+  // two buffers: the next row block is fetched into registers while the
+  // current one is computed, then stored into the other buffer
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][32 * D];
+  __shared__ __attribute__((aligned(16))) bf16_t Gs[2][32 * D];
+  __shared__ __attribute__((aligned(16))) float s_lse2[2][32];
+  __shared__ __attribute__((aligned(16))) float s_D[2][32];
+  __shared__ __attribute__((aligned(16))) int s_irow[2][32];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, col = lane & 31;
   const int bh = blockIdx.x % n_heads;
@@ -243,40 +269,58 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const float* lhead = lse + static_cast<size_t>(b * Hq + kvh * G) * S;
   const float* dhead = Dws + static_cast<size_t>(b * Hq + kvh * G) * S;
   const int tr_j = lane & 15, tr_r = tr_j >> 2, tr_q = tr_j & 3, tr_dg = (lane >> 4) & 1;
-  const int wave_lim = min(lim, wave_key0 + 32);          // keys of this wave that exist
+  const bool has_keys = wave_key0 < lim;                 // some key of this wave exists
 
-  for (int r0 = 0; r0 < n_rows; r0 += 32) {
-    // chunk keys only see queries i >= key: skip blocks whose queries all precede the tile
-    if (!is_cache) {
-      const int r1 = min(r0 + 31, n_rows - 1);
-      if (r0 / S == r1 / S && (r1 % S) < base) continue;
-    }
-    __syncthreads();
+  // chunk keys only see queries i >= key: blocks whose queries all precede
+  // the tile are skipped; next_block(r0) is the first block after r0 to do
+  auto skipped = [&](int r0) __attribute__((always_inline)) {
+    const int r1 = min(r0 + 31, n_rows - 1);
+    return !is_cache && r0 / S == r1 / S && (r1 % S) < base;
+  };
+  auto next_block = [&](int r0) __attribute__((always_inline)) {
+    r0 += 32;
+    while (r0 < n_rows && skipped(r0)) r0 += 32;
+    return r0;
+  };
+  u32x4 fq[NCH], fg[NCH];
+  float f_l = 0.f, f_d = 0.f;
+  auto fetch = [&](int r0) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int idx = c * 256 + tid, row = idx / CPR, ch = idx % CPR;
       const int r = min(r0 + row, n_rows - 1);
-      const u32x4 q = load_u32x4(qhead + static_cast<size_t>(r) * D + ch * 8);
-      const u32x4 go = load_u32x4(ghead + static_cast<size_t>(r) * D + ch * 8);
-      store_u32x4(&Qs[row * D + 8 * bchunk<CPR>(row, ch)], q);
-      store_u32x4(&Gs[row * D + 8 * bchunk<CPR>(row, ch)], go);
+      fq[c] = load_u32x4(qhead + static_cast<size_t>(r) * D + ch * 8);
+      fg[c] = load_u32x4(ghead + static_cast<size_t>(r) * D + ch * 8);
+    }
+    if (tid < 32) {
+      const int rc = min(r0 + tid, n_rows - 1);
+      f_l = lhead[rc];
+      f_d = dhead[rc];
+    }
+  };
+  auto commit = [&](int r0, int bf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int idx = c * 256 + tid, row = idx / CPR, ch = idx % CPR;
+      store_u32x4(&Qs[bf][row * D + 8 * bchunk<CPR>(row, ch)], fq[c]);
+      store_u32x4(&Gs[bf][row * D + 8 * bchunk<CPR>(row, ch)], fg[c]);
     }
     if (tid < 32) {
       const int r = r0 + tid;
-      const int rc = min(r, n_rows - 1);
-      const float lv = lhead[rc], dv_ = dhead[rc];
-      s_lse2[tid] = r < n_rows ? lv * kLog2e : __builtin_huge_valf();
-      s_D[tid] = r < n_rows ? dv_ : 0.f;
-      s_irow[tid] = r < n_rows ? r % S : -1;
+      s_lse2[bf][tid] = r < n_rows ? f_l * kLog2e : __builtin_huge_valf();
+      s_D[bf][tid] = r < n_rows ? f_d : 0.f;
+      s_irow[bf][tid] = r < n_rows ? r % S : -1;
     }
-    __syncthreads();
-    if (wave_key0 >= wave_lim) continue;
+  };
+  auto compute = [&](int bf) __attribute__((always_inline)) {
+    const bf16_t* qs = Qs[bf];
+    const bf16_t* gs = Gs[bf];
     // S and dP (queries x keys): register r of lane l <-> row 8(r/4) + 4(l/32) + r%4
     f32x16 s = zero16(), p = zero16();
 #pragma unroll
     for (int st = 0; st < DS; ++st) {
-      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qs[col * D + 8 * bchunk<CPR>(col, 2 * st + hf)]);
-      const bf16x8 ga = *reinterpret_cast<const bf16x8*>(&Gs[col * D + 8 * bchunk<CPR>(col, 2 * st + hf)]);
+      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&qs[col * D + 8 * bchunk<CPR>(col, 2 * st + hf)]);
+      const bf16x8 ga = *reinterpret_cast<const bf16x8*>(&gs[col * D + 8 * bchunk<CPR>(col, 2 * st + hf)]);
       s = mfma32x32x16(qa, kf[st], s);
       p = mfma32x32x16(ga, vf[st], p);
     }
@@ -284,9 +328,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
       const int row0 = 8 * a4 + 4 * hf;
-      const f32x4 l2 = *reinterpret_cast<const f32x4*>(&s_lse2[row0]);
-      const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&s_D[row0]);
-      const int4 iv = *reinterpret_cast<const int4*>(&s_irow[row0]);
+      const f32x4 l2 = *reinterpret_cast<const f32x4*>(&s_lse2[bf][row0]);
+      const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&s_D[bf][row0]);
+      const int4 iv = *reinterpret_cast<const int4*>(&s_irow[bf][row0]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * a4 + e;
@@ -307,14 +351,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int d = db * 32 + tr_dg * 16 + 4 * tr_q;
-        const bf16x4 g0 = lds_read_tr16(&Gs[ra * D + 8 * bchunk<CPR>(ra, d >> 3) + (d & 7)]);
-        const bf16x4 g1 = lds_read_tr16(&Gs[rbx * D + 8 * bchunk<CPR>(rbx, d >> 3) + (d & 7)]);
-        const bf16x4 q0 = lds_read_tr16(&Qs[ra * D + 8 * bchunk<CPR>(ra, d >> 3) + (d & 7)]);
-        const bf16x4 q1 = lds_read_tr16(&Qs[rbx * D + 8 * bchunk<CPR>(rbx, d >> 3) + (d & 7)]);
+        const bf16x4 g0 = lds_read_tr16(&gs[ra * D + 8 * bchunk<CPR>(ra, d >> 3) + (d & 7)]);
+        const bf16x4 g1 = lds_read_tr16(&gs[rbx * D + 8 * bchunk<CPR>(rbx, d >> 3) + (d & 7)]);
+        const bf16x4 q0 = lds_read_tr16(&qs[ra * D + 8 * bchunk<CPR>(ra, d >> 3) + (d & 7)]);
+        const bf16x4 q1 = lds_read_tr16(&qs[rbx * D + 8 * bchunk<CPR>(rbx, d >> 3) + (d & 7)]);
         dv[db] = mfma32x32x16(__builtin_shufflevector(g0, g1, 0, 1, 2, 3, 4, 5, 6, 7), pb, dv[db]);
         dk[db] = mfma32x32x16(__builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7), db8, dk[db]);
       }
     }
+  };
+
+  // buffer bf is rewritten two blocks after it was read, behind the barrier
+  // of the block in between
+  int r0 = skipped(0) ? next_block(0) : 0;
+  if (r0 < n_rows) fetch(r0);
+  int bf = 0;
+  while (r0 < n_rows) {
+    commit(r0, bf);
+    __syncthreads();
+    const int rn = next_block(r0);
+    if (rn < n_rows) fetch(rn);
+    if (has_keys) compute(bf);
+    r0 = rn;
+    bf ^= 1;
   }
   if (key >= lim) return;
   bf16_t* ko = (is_cache ? dKc + static_cast<size_t>(bh) * M * D : dKn + static_cast<size_t>(bh) * S * D) +
