@@ -259,7 +259,8 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       for (int i = 0; i < SPT; ++i)
         if (((cmask >> i) & 1u) && (key[i] & pmask) == prefix) atomicAdd(&hw[(key[i] & dmask) >> shift], 1u);
       __syncthreads();
-      for (int i = tid; i < (kWavesSel / 2) * 256; i += kThreads) (&hist[(pass + 2) % 3][0][0])[i] = 0;
+#pragma unroll
+      for (int i = 0; i < (kWavesSel / 2) * 256 / kThreads; ++i) (&hist[(pass + 2) % 3][0][0])[tid + i * kThreads] = 0;
       int c[4] = {0, 0, 0, 0}, sum = 0;
 #pragma unroll
       for (int wp = 0; wp < kWavesSel / 2; ++wp) {
@@ -271,16 +272,17 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) sum += c[q];
+      // the cumulative counts are monotone, so exactly one (lane, q) has
+      // kk in (cb, cb + c[q]]: no ordering between the q tests is needed
       int cb = wave_incl_scan(sum) - sum;
       int digit = 0, before = 0;
       bool found = false;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        if (!found && cb < kk && kk <= cb + c[q]) {
-          found = true;
-          digit = 4 * lane + q;
-          before = cb;
-        }
+        const bool hit = cb < kk && kk <= cb + c[q];
+        digit = hit ? 4 * lane + q : digit;
+        before = hit ? cb : before;
+        found = found || hit;
         cb += c[q];
       }
       const uint64_t bal = __ballot(found);
