@@ -303,6 +303,9 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": recorded_traffic("attn_fwd_bf16_kernel", w.name),
                 "avg_launch_us": round(attn_avg_ms * 1e3, 3), "algorithmic_flops_per_launch": round(per_launch)}
         metric = "H2O chunk-step TFLOP/s + tokens/s at 64k ctx, 8B-GQA shape; % of roofline"
+        if w.name != "llama8b_64k":
+            metric = "H2O chunk-step TFLOP/s + tokens/s at %dk ctx, G=%d d=%d%s; %% of roofline" % (
+                w.total_len // 1024, w.group, w.head_dim, ", with the backward" if backward else "")
         unit = "TFLOP/s"
         value = round(tflops, 3)
     tokens_per_s = tokens / (ms_per_step * 1e-3)

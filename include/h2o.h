@@ -113,6 +113,10 @@ H2O_API size_t h2o_workspace_bytes(const h2o_config* cfg);
  *   as they are) and tokens_seen must be 0.
  * adopt = 1: the buffers already hold a valid state after `tokens_seen`
  *   tokens (resume from a snapshot); nothing but the workspace is touched.
+ *   The K/V rows of free slots (position < 0) must hold finite values (zeros,
+ *   say): the attention reads them as part of whole tiles and gives them
+ *   zero weight, which keeps NaN or Inf bit patterns in unused memory from
+ *   reaching the output only if the values themselves are finite.
  * The workspace counters are cleared on `stream` in both cases.
  * Errors: H2O_ERR_NULL, H2O_ERR_CONFIG, H2O_ERR_WORKSPACE, H2O_ERR_STATE
  * (adopt = 0 with tokens_seen != 0, or tokens_seen < 0), H2O_ERR_HIP. */
