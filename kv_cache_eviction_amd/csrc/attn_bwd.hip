@@ -17,10 +17,11 @@
 //     K rows sit in LDS in MFMA-row order, which keeps every aligned group of
 //     4 keys in 4 consecutive rows, so the same tile serves the K rows of S^T
 //     (16-byte reads) and K^T of dQ^T = K^T dS^T (transpose reads).
-//   * bwd_dkdv_kernel: one wave per 32 keys held in registers, loops over all
-//     query rows of the KV group (S = Q K^T, lane = key), accumulating
-//     dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T from transpose
-//     reads of the staged row block.
+//   * bwd_dkdv_kernel: 128 keys per workgroup (K and V rows in LDS), one wave
+//     per 32 keys and row set; the two row sets split the query rows of the
+//     KV group (S = Q K^T, lane = key), accumulating dV^T += dO^T P and
+//     dK^T += Q^T dS with dO^T and Q^T from transpose reads of the staged
+//     row block, and fold their sums at the end.
 #include "h2o_device.h"
 #include "h2o_launch.h"
 
@@ -209,10 +210,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------- dK and dV
-constexpr int kKeysPerWG = 128;     // 4 waves x 32 keys
+constexpr int kKeysPerWG = 128;     // 4 key groups x 32 keys
 
+// 8 waves: key group kg = wave % 4 owns 32 keys (lane = key column), row set
+// rs = wave / 4 takes every other needed query row block; the two row sets
+// fold their dK/dV at the end.  The workgroup's K and V rows sit in LDS and
+// are read as the B operands of every block, so a wave holds only its dK/dV
+// accumulators and the block in flight: two waves fit on each SIMD.
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
     const int32_t* __restrict__ pos, const bf16_t* __restrict__ Kn, const bf16_t* __restrict__ Vn,
     const bf16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dws,
@@ -220,16 +226,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     bf16_t* __restrict__ dVn, int Hq, int Hkv, int S, int M, float c2, float scale, int n_heads,
     int n_ct, int n_tiles) {
   constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
-  constexpr int NCH = 32 * CPR / 256;      // 16-byte chunks per thread per 32-row block
-  // two buffers: the next row block is fetched into registers while the
-  // current one is computed, then stored into the other buffer
-  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][32 * D];
-  __shared__ __attribute__((aligned(16))) bf16_t Gs[2][32 * D];
-  __shared__ __attribute__((aligned(16))) float s_lse2[2][32];
-  __shared__ __attribute__((aligned(16))) float s_D[2][32];
-  __shared__ __attribute__((aligned(16))) int s_irow[2][32];
+  constexpr int NCH = 32 * CPR / 256;              // chunks per thread of a row set per 32-row block
+  constexpr int NKV = kKeysPerWG * CPR / 512;      // chunks per thread of the key rows
+  __shared__ __attribute__((aligned(16))) bf16_t Kl[kKeysPerWG * D];
+  __shared__ __attribute__((aligned(16))) bf16_t Vl[kKeysPerWG * D];
+  // [row set][buffer]: the next row block is fetched into registers while
+  // the current one is computed, then stored into the other buffer
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][2][32 * D];
+  __shared__ __attribute__((aligned(16))) bf16_t Gs[2][2][32 * D];
+  __shared__ __attribute__((aligned(16))) float s_lse2[2][2][32];
+  __shared__ __attribute__((aligned(16))) float s_D[2][2][32];
+  __shared__ __attribute__((aligned(16))) int s_irow[2][2][32];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, col = lane & 31;
+  const int kg = wave & 3, rs = wave >> 2;
+  const int ltid = tid & 255;                      // thread index within the row set
   const int bh = blockIdx.x % n_heads;
   const int tile = static_cast<int>(blockIdx.x) / n_heads;
   const int b = bh / Hkv, kvh = bh - b * Hkv;
@@ -237,24 +248,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const bool is_cache = tile < n_ct;
   const int base = (is_cache ? tile : tile - n_ct) * kKeysPerWG;
   const int lim = is_cache ? M : S;
-  const int key = base + wave * 32 + col;                 // this lane's key column
+  const int key = base + kg * 32 + col;            // this lane's key column
   const bf16_t* kh = is_cache ? Kc + static_cast<size_t>(bh) * M * D : Kn + static_cast<size_t>(bh) * S * D;
   const bf16_t* vh = is_cache ? Vc + static_cast<size_t>(bh) * M * D : Vn + static_cast<size_t>(bh) * S * D;
   const int pv = pos[static_cast<size_t>(bh) * M + (is_cache ? min(key, M - 1) : 0)];
   const bool key_ok = key < lim && (!is_cache || pv >= 0);
-  const int wave_key0 = base + wave * 32;
+  const bool has_keys = base + kg * 32 < lim;      // some key of this wave exists
 
-  // the wave's keys and values: B operands of S = Q K^T and dP = dO V^T (lane = key)
-  bf16x8 kf[DS], vf[DS];
-  {
-    const size_t off = static_cast<size_t>(min(key, lim - 1)) * D;
+  // the workgroup's K and V rows (row r = key base + r; rows past the end
+  // repeat the last row and get zero weight)
 #pragma unroll
-    for (int st = 0; st < DS; ++st) {
-      const bf16x8 k = load_bf16x8(kh + off + 16 * st + 8 * hf);
-      const bf16x8 v = load_bf16x8(vh + off + 16 * st + 8 * hf);
-      kf[st] = key_ok ? k : bf16x8{};
-      vf[st] = key_ok ? v : bf16x8{};
-    }
+  for (int c = 0; c < NKV; ++c) {
+    const int idx = c * 512 + tid, row = idx / CPR, ch = idx % CPR;
+    const size_t src = static_cast<size_t>(min(base + row, lim - 1)) * D + ch * 8;
+    store_u32x4(&Kl[row * D + 8 * bchunk<CPR>(row, ch)], load_u32x4(kh + src));
+    store_u32x4(&Vl[row * D + 8 * bchunk<CPR>(row, ch)], load_u32x4(vh + src));
   }
   f32x16 dk[DB], dv[DB];
 #pragma unroll
@@ -269,7 +277,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const float* lhead = lse + static_cast<size_t>(b * Hq + kvh * G) * S;
   const float* dhead = Dws + static_cast<size_t>(b * Hq + kvh * G) * S;
   const int tr_j = lane & 15, tr_r = tr_j >> 2, tr_q = tr_j & 3, tr_dg = (lane >> 4) & 1;
-  const bool has_keys = wave_key0 < lim;                 // some key of this wave exists
+  const int krow = kg * 32 + col;                  // LDS row of this lane's key
 
   // chunk keys only see queries i >= key: blocks whose queries all precede
   // the tile are skipped; next_block(r0) is the first block after r0 to do
@@ -287,13 +295,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   auto fetch = [&](int r0) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int idx = c * 256 + tid, row = idx / CPR, ch = idx % CPR;
+      const int idx = c * 256 + ltid, row = idx / CPR, ch = idx % CPR;
       const int r = min(r0 + row, n_rows - 1);
       fq[c] = load_u32x4(qhead + static_cast<size_t>(r) * D + ch * 8);
       fg[c] = load_u32x4(ghead + static_cast<size_t>(r) * D + ch * 8);
     }
-    if (tid < 32) {
-      const int rc = min(r0 + tid, n_rows - 1);
+    if (ltid < 32) {
+      const int rc = min(r0 + ltid, n_rows - 1);
       f_l = lhead[rc];
       f_d = dhead[rc];
     }
@@ -301,36 +309,39 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   auto commit = [&](int r0, int bf) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int idx = c * 256 + tid, row = idx / CPR, ch = idx % CPR;
-      store_u32x4(&Qs[bf][row * D + 8 * bchunk<CPR>(row, ch)], fq[c]);
-      store_u32x4(&Gs[bf][row * D + 8 * bchunk<CPR>(row, ch)], fg[c]);
+      const int idx = c * 256 + ltid, row = idx / CPR, ch = idx % CPR;
+      store_u32x4(&Qs[rs][bf][row * D + 8 * bchunk<CPR>(row, ch)], fq[c]);
+      store_u32x4(&Gs[rs][bf][row * D + 8 * bchunk<CPR>(row, ch)], fg[c]);
     }
-    if (tid < 32) {
-      const int r = r0 + tid;
-      s_lse2[bf][tid] = r < n_rows ? f_l * kLog2e : __builtin_huge_valf();
-      s_D[bf][tid] = r < n_rows ? f_d : 0.f;
-      s_irow[bf][tid] = r < n_rows ? r % S : -1;
+    if (ltid < 32) {
+      const int r = r0 + ltid;
+      s_lse2[rs][bf][ltid] = r < n_rows ? f_l * kLog2e : __builtin_huge_valf();
+      s_D[rs][bf][ltid] = r < n_rows ? f_d : 0.f;
+      s_irow[rs][bf][ltid] = r < n_rows ? r % S : -1;
     }
   };
   auto compute = [&](int bf) __attribute__((always_inline)) {
-    const bf16_t* qs = Qs[bf];
-    const bf16_t* gs = Gs[bf];
+    const bf16_t* qs = Qs[rs][bf];
+    const bf16_t* gs = Gs[rs][bf];
     // S and dP (queries x keys): register r of lane l <-> row 8(r/4) + 4(l/32) + r%4
     f32x16 s = zero16(), p = zero16();
 #pragma unroll
     for (int st = 0; st < DS; ++st) {
+      const int kc = 8 * bchunk<CPR>(krow, 2 * st + hf);
       const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&qs[col * D + 8 * bchunk<CPR>(col, 2 * st + hf)]);
       const bf16x8 ga = *reinterpret_cast<const bf16x8*>(&gs[col * D + 8 * bchunk<CPR>(col, 2 * st + hf)]);
-      s = mfma32x32x16(qa, kf[st], s);
-      p = mfma32x32x16(ga, vf[st], p);
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&Kl[krow * D + kc]);
+      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&Vl[krow * D + kc]);
+      s = mfma32x32x16(qa, kb, s);
+      p = mfma32x32x16(ga, vb, p);
     }
     f32x8 pp[2], dd[2];
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
       const int row0 = 8 * a4 + 4 * hf;
-      const f32x4 l2 = *reinterpret_cast<const f32x4*>(&s_lse2[bf][row0]);
-      const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&s_D[bf][row0]);
-      const int4 iv = *reinterpret_cast<const int4*>(&s_irow[bf][row0]);
+      const f32x4 l2 = *reinterpret_cast<const f32x4*>(&s_lse2[rs][bf][row0]);
+      const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&s_D[rs][bf][row0]);
+      const int4 iv = *reinterpret_cast<const int4*>(&s_irow[rs][bf][row0]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * a4 + e;
@@ -338,7 +349,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         const bool ok = key_ok && (is_cache || key <= qi);
         const float pr = ok ? fast_exp2(fmaf(s[r], c2, -l2[e])) : 0.f;
         pp[r >> 3][r & 7] = pr;
-        dd[r >> 3][r & 7] = pr * (p[r] - dv4[e]);
+        dd[r >> 3][r & 7] = ok ? pr * (p[r] - dv4[e]) : 0.f;
       }
     }
     // dV^T += dO^T P and dK^T += Q^T dS: MFMA u contracts over the rows held
@@ -361,21 +372,52 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     }
   };
 
-  // buffer bf is rewritten two blocks after it was read, behind the barrier
-  // of the block in between
-  int r0 = skipped(0) ? next_block(0) : 0;
+  // The needed blocks in order are split alternately: row set 0 takes the
+  // 1st, 3rd, ..., row set 1 the 2nd, 4th, ... (ra, rb: the two sets'
+  // current blocks, tracked by every wave).  Buffer (rs, bf) is rewritten two
+  // iterations after it was read, behind the barrier of the one in between.
+  int ra = skipped(0) ? next_block(0) : 0;
+  int rb = ra < n_rows ? next_block(ra) : n_rows;
+  int r0 = rs ? rb : ra;
   if (r0 < n_rows) fetch(r0);
   int bf = 0;
-  while (r0 < n_rows) {
-    commit(r0, bf);
-    __syncthreads();
-    const int rn = next_block(r0);
+  while (ra < n_rows) {
+    if (r0 < n_rows) commit(r0, bf);
+    __syncthreads();                   // also orders the key rows' stores before the first reads
+    const int na = rb < n_rows ? next_block(rb) : n_rows;
+    const int nb = na < n_rows ? next_block(na) : n_rows;
+    const int rn = rs ? nb : na;
     if (rn < n_rows) fetch(rn);
-    if (has_keys) compute(bf);
+    if (r0 < n_rows && has_keys) compute(bf);
+    ra = na;
+    rb = nb;
     r0 = rn;
     bf ^= 1;
   }
-  if (key >= lim) return;
+
+  // fold row set 1's dK, dV into row set 0's, one 32-row block of the
+  // accumulators per round through the query buffers
+  __syncthreads();
+  float* xo = reinterpret_cast<float*>(&Qs[0][0][0]);     // 16 x 256 floats per round
+  const int xs = kg * 64 + lane;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      f32x16& acc = h ? dv[db] : dk[db];
+      if (rs == 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[r * 256 + xs] = acc[r];
+      }
+      __syncthreads();
+      if (rs == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] += xo[r * 256 + xs];
+      }
+      __syncthreads();
+    }
+  }
+  if (rs == 1 || key >= lim) return;
   bf16_t* ko = (is_cache ? dKc + static_cast<size_t>(bh) * M * D : dKn + static_cast<size_t>(bh) * S * D) +
                static_cast<size_t>(key) * D;
   bf16_t* vo = (is_cache ? dVc + static_cast<size_t>(bh) * M * D : dVn + static_cast<size_t>(bh) * S * D) +
@@ -422,7 +464,7 @@ hipError_t launch_backward(const StepShape& sh, const BackwardArgs& a, hipStream
   const int n_ct = (sh.M + kKeysPerWG - 1) / kKeysPerWG;
   const int n_tiles = n_ct + (sh.S + kKeysPerWG - 1) / kKeysPerWG;
 #define H2O_LAUNCH_DKDV(DD)                                                                            \
-  hipLaunchKernelGGL(bwd_dkdv_kernel<DD>, dim3(n_heads * n_tiles), dim3(256), 0, st,                   \
+  hipLaunchKernelGGL(bwd_dkdv_kernel<DD>, dim3(n_heads * n_tiles), dim3(512), 0, st,                   \
                      static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k_cache),          \
                      static_cast<const bf16_t*>(a.v_cache), a.pos, static_cast<const bf16_t*>(a.k_new), \
                      static_cast<const bf16_t*>(a.v_new), static_cast<const bf16_t*>(a.d_out), a.lse, \
