@@ -314,6 +314,132 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
   }
 }
 
+// Short chunks (G*S <= 64 rows per KV group): one 64-row block holds every
+// query row, so it is staged once and each wave walks its keys in 64-key
+// groups, loading the next group's K fragments while it computes the
+// current one.  A workgroup takes kDecKeys consecutive keys of the head's
+// key sequence (the n_cache cache slots, then the S chunk keys), so the
+// cache streams from HBM once per step (one row split).
+constexpr int kDecKeys = 2304;        // keys per workgroup: 4 waves x 9 groups x 64
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void score_dec_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Kn,
+    const float* __restrict__ lse, float* __restrict__ partial, int Hq, int Hkv, int S, int M,
+    int n_cache, float c2, int n_heads) {
+  constexpr int DS = D / 16, CPR = D / 8, RBY = 2 * D;
+  constexpr int NG = kDecKeys / 256;          // key groups per wave
+  constexpr int NQ = kRB * CPR / 256;         // 16-byte query chunks per thread
+  __shared__ __attribute__((aligned(16))) char qs[kRB * RBY];
+  __shared__ __attribute__((aligned(16))) float s_l2[kRB];
+  __shared__ __attribute__((aligned(16))) int s_qi[kRB];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, hf = lane >> 5, col = lane & 31;
+  const int bh = blockIdx.x % n_heads;
+  const int wgi = static_cast<int>(blockIdx.x) / n_heads;
+  const int b = bh / Hkv, kvh = bh - b * Hkv;
+  const int G = Hq / Hkv;
+  const int n_rows = G * S;                   // <= kRB; row u is query row u of the group
+  const int n_keys = n_cache + S;             // key v: cache slot v, or chunk key v - n_cache
+  const int base = wgi * kDecKeys;
+  const bf16_t* kc_head = Kc + static_cast<size_t>(bh) * M * D;
+  const bf16_t* kn_head = Kn + static_cast<size_t>(bh) * S * D;
+  const bf16_t* qhead = Q + static_cast<size_t>(b * Hq + kvh * G) * S * D;
+  const float* lhead = lse + static_cast<size_t>(b * Hq + kvh * G) * S;
+
+  // the wave's key groups: keys base + 256 k + 64 wave + (0..63), k < NG
+  auto load_keys = [&](int k, bf16x8 (&kf)[2][DS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int v = base + 256 * k + 64 * wave + 32 * kb + col;
+      const bool ok = v < n_keys;
+      const bf16_t* krow = v < n_cache ? kc_head + static_cast<size_t>(v) * D
+                                       : kn_head + static_cast<size_t>(ok ? v - n_cache : 0) * D;
+#pragma unroll
+      for (int st = 0; st < DS; ++st) {
+        const bf16x8 x = load_bf16x8(krow + 16 * st + 8 * hf);
+        kf[kb][st] = ok ? x : bf16x8{};
+      }
+    }
+  };
+  bf16x8 kA[2][DS], kB[2][DS];
+  const int n_groups = min(NG, max(0, (n_keys - base - 64 * wave + 255) / 256));
+  if (n_groups > 0) load_keys(0, kA);
+
+  // the rows (zero past the end, lse +inf so that P = 0 there)
+#pragma unroll
+  for (int c = 0; c < NQ; ++c) {
+    const int idx = c * 256 + tid, row = idx / CPR, ch = idx % CPR;
+    const u32x4 x = load_u32x4(qhead + static_cast<size_t>(min(row, n_rows - 1)) * D + ch * 8);
+    const u32x4 z = {0, 0, 0, 0};
+    store_u32x4(qs + row * RBY + 16 * q_chunk<CPR>(row, ch), row < n_rows ? x : z);
+  }
+  if (tid < kRB) {
+    const bool ok = tid < n_rows;
+    s_l2[tid] = ok ? lhead[min(tid, n_rows - 1)] * kLog2e : __builtin_huge_valf();
+    s_qi[tid] = ok ? tid % S : -1;
+  }
+  __syncthreads();
+
+  uint32_t q_rd[DS];
+#pragma unroll
+  for (int st = 0; st < DS; ++st) q_rd[st] = col * RBY + 16 * q_chunk<CPR>(col, 2 * st + hf);
+  float* out = partial + static_cast<size_t>(bh) * (static_cast<size_t>(M) + S);
+
+  // one 64-key group: S = Q K^T over both 32-row halves, P, column sums
+  auto group = [&](int k, const bf16x8 (&kf)[2][DS]) __attribute__((always_inline)) {
+    const int v0 = base + 256 * k + 64 * wave + col, v1 = v0 + 32;   // this lane's two keys
+    const int j0 = v0 - n_cache, j1 = v1 - n_cache;                   // chunk index (< 0: cache)
+    float cs0[4] = {0.f, 0.f, 0.f, 0.f}, cs1[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x16 a0 = zero16(), a1 = zero16();
+#pragma unroll
+      for (int st = 0; st < DS; ++st) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qs + h * 32 * RBY + q_rd[st]);
+        a0 = mfma32x32x16(qa, kf[0][st], a0);
+        a1 = mfma32x32x16(qa, kf[1][st], a1);
+      }
+      // accumulator register r of lane l: row 32h + 8(r/4) + 4hf + r%4;
+      // a chunk key j is seen by rows whose query index reaches j
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int row0 = h * 32 + 8 * a4 + 4 * hf;
+        const f32x4 l2v = *reinterpret_cast<const f32x4*>(&s_l2[row0]);
+        const int4 qiv = *reinterpret_cast<const int4*>(&s_qi[row0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * a4 + e;
+          const int qi = e == 0 ? qiv.x : e == 1 ? qiv.y : e == 2 ? qiv.z : qiv.w;
+          const float p0 = fast_exp2(fmaf(a0[r], c2, -l2v[e]));
+          const float p1 = fast_exp2(fmaf(a1[r], c2, -l2v[e]));
+          cs0[e] += j0 <= qi ? p0 : 0.f;
+          cs1[e] += j1 <= qi ? p1 : 0.f;
+        }
+      }
+    }
+    float t0 = (cs0[0] + cs0[1]) + (cs0[2] + cs0[3]);
+    float t1 = (cs1[0] + cs1[1]) + (cs1[2] + cs1[3]);
+    t0 += xor32(t0);
+    t1 += xor32(t1);
+    if (hf == 0) {
+      if (v0 < n_keys) out[v0 < n_cache ? v0 : M + j0] = t0;
+      if (v1 < n_keys) out[v1 < n_cache ? v1 : M + j1] = t1;
+    }
+  };
+  // two register sets, alternating, so that the next group's loads are in
+  // flight during the current group's MFMAs
+  for (int k = 0; k < n_groups; k += 2) {
+    if (k + 1 < n_groups) load_keys(k + 1, kB);
+    group(k, kA);
+    if (k + 1 >= n_groups) break;
+    if (k + 2 < n_groups) load_keys(k + 2, kA);
+    group(k + 1, kB);
+  }
+}
+
 // fp32: one thread per key column, query rows streamed through LDS; one row
 // split, so each workgroup finalizes its own columns.
 template <int D>
@@ -391,7 +517,18 @@ int score_row_splits(const StepShape& sh, int dtype) {
 hipError_t launch_score(const StepShape& sh, const ScoreArgs& a, int dtype, hipStream_t st) {
   const int n_heads = sh.B * sh.Hkv;
   const float c2 = sh.scale * kLog2e;
-  if (dtype == kBF16) {
+  if (dtype == kBF16 && sh.Hq / sh.Hkv * sh.S <= kRB) {
+    // short chunks: every query row in one block, keys streamed per wave
+    const int n_wg = (sh.n_cache + sh.S + kDecKeys - 1) / kDecKeys;
+#define H2O_LAUNCH_SCORE_DEC(DD)                                                                   \
+  hipLaunchKernelGGL(score_dec_kernel<DD>, dim3(n_heads * n_wg), dim3(256), 0, st,                 \
+                     static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k_cache),      \
+                     static_cast<const bf16_t*>(a.k_new), a.lse, a.partial, sh.Hq, sh.Hkv, sh.S,   \
+                     sh.M, sh.n_cache, c2, n_heads)
+    if (sh.D == 128) H2O_LAUNCH_SCORE_DEC(128);
+    else H2O_LAUNCH_SCORE_DEC(64);
+#undef H2O_LAUNCH_SCORE_DEC
+  } else if (dtype == kBF16) {
     const int n_ct = (sh.n_cache + kCT - 1) / kCT;
     const int n_tiles = n_ct + (sh.S + kCT - 1) / kCT;
     const dim3 grid(n_heads * n_tiles * a.R), block(256);
