@@ -12,7 +12,7 @@
 // where dK and dV of a KV head sum over the G query heads of its group.
 //
 // Two kernels, both deterministic (no atomics):
-//   * bwd_dq_kernel: one wave per 32-query row block (the forward's layout:
+//   * bwd_dq_kernel: one wave per 32-query row block, 8 per workgroup (the forward's layout:
 //     S^T = K Q^T, lane = query), loops over the key tiles; also writes D.
 //     K rows sit in LDS in MFMA-row order, which keeps every aligned group of
 //     4 keys in 4 consecutive rows, so the same tile serves the K rows of S^T
@@ -29,7 +29,7 @@ namespace h2o {
 namespace {
 
 constexpr int kBKT = 64;     // keys per LDS tile (dq kernel)
-constexpr int kBWaves = 4;
+constexpr int kBWaves = 8;     // row blocks (waves) per dQ workgroup
 
 __device__ __forceinline__ int bkrow_of_key(int k) {
   return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3);
@@ -39,14 +39,14 @@ __device__ __forceinline__ int bchunk(int row, int c) { return c ^ (row & (CPR -
 
 // ---------------------------------------------------------------- dQ and D
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
     const int32_t* __restrict__ pos, const bf16_t* __restrict__ Kn, const bf16_t* __restrict__ Vn,
     const bf16_t* __restrict__ Oo, const bf16_t* __restrict__ dO, const float* __restrict__ lse,
     float* __restrict__ Dws, bf16_t* __restrict__ dQ, int Hq, int Hkv, int S, int M, float c2,
     float scale, int n_heads, int wg_per_head) {
   constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
-  constexpr int NCH = kBKT * CPR / 256;
+  constexpr int NCH = kBKT * CPR / 512;
   // two buffers: the next tile is fetched into registers while the current
   // one is computed, then stored into the other buffer
   __shared__ __attribute__((aligned(16))) bf16_t Ks2[2][kBKT * D];
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     const bf16_t* vs = is_cache ? vc_head : vn_head;
 #pragma unroll
     for (int r = 0; r < NCH; ++r) {
-      const int c = r * 256 + tid, key = c / CPR, ch = c % CPR;
+      const int c = r * 512 + tid, key = c / CPR, ch = c % CPR;
       const int src = min(base + key, lim - 1);
       fk[r] = load_u32x4(ks + static_cast<size_t>(src) * D + ch * 8);
       fv[r] = load_u32x4(vs + static_cast<size_t>(src) * D + ch * 8);
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     const int lim = is_cache ? M : S;
 #pragma unroll
     for (int r = 0; r < NCH; ++r) {
-      const int c = r * 256 + tid, key = c / CPR, ch = c % CPR;
+      const int c = r * 512 + tid, key = c / CPR, ch = c % CPR;
       const int row = (key & ~31) | bkrow_of_key(key & 31);
       store_u32x4(&Ks2[bf][row * D + 8 * bchunk<CPR>(row, ch)], fk[r]);
       store_u32x4(&Vs2[bf][row * D + 8 * bchunk<CPR>(row, ch)], fv[r]);
@@ -148,40 +148,34 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     const bf16_t* Ks = Ks2[bf];
     const bf16_t* Vs = Vs2[bf];
     if (!active || (!is_cache && base > qb * 32 + 31)) continue;
-    // S^T and dP^T (keys x queries): register r of lane l <-> key 16(l/32) + r (+32 kb)
-    f32x16 s0 = zero16(), s1 = zero16(), p0 = zero16(), p1 = zero16();
-#pragma unroll
-    for (int st = 0; st < DS; ++st) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[col * D + 8 * bchunk<CPR>(col, 2 * st + hf)]);
-      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&Ks[(32 + col) * D + 8 * bchunk<CPR>(32 + col, 2 * st + hf)]);
-      const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vs[col * D + 8 * bchunk<CPR>(col, 2 * st + hf)]);
-      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&Vs[(32 + col) * D + 8 * bchunk<CPR>(32 + col, 2 * st + hf)]);
-      s0 = mfma32x32x16(ka, qf[st], s0);
-      s1 = mfma32x32x16(kb, qf[st], s1);
-      p0 = mfma32x32x16(va, dof[st], p0);
-      p1 = mfma32x32x16(vb, dof[st], p1);
-    }
     const uint64_t vm = s_valid2[bf];
     const bool causal = !is_cache && (base + kBKT - 1 > qb * 32);
-    const uint32_t bits0 = static_cast<uint32_t>(vm >> (16 * hf)) & 0xffffu;
-    const uint32_t bits1 = static_cast<uint32_t>(vm >> (32 + 16 * hf)) & 0xffffu;
     const int lim_i = causal ? qi - base - 16 * hf : 1 << 30;
-    f32x8 d8[4];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const bool ok0 = ((bits0 >> r) & 1u) && (r <= lim_i);
-      const bool ok1 = ((bits1 >> r) & 1u) && (32 + r <= lim_i);
-      const float pa = ok0 ? fast_exp2(fmaf(s0[r], c2, -lse2)) : 0.f;
-      const float pb = ok1 ? fast_exp2(fmaf(s1[r], c2, -lse2)) : 0.f;
-      d8[r >> 3][r & 7] = pa * (p0[r] - Di);
-      d8[2 + (r >> 3)][r & 7] = pb * (p1[r] - Di);
-    }
-    // dQ^T += K^T dS^T: MFMA (kb,u) covers keys 32kb + 16(l/32) + 8u + e
+    // one 32-key half at a time (keeps two accumulators live, not four)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      // S^T and dP^T of keys 32kb..: register r of lane l <-> key 32kb + 16(l/32) + r
+      f32x16 sh = zero16(), ph = zero16();
+#pragma unroll
+      for (int st = 0; st < DS; ++st) {
+        const int kr = 32 * kb + col;
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[kr * D + 8 * bchunk<CPR>(kr, 2 * st + hf)]);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vs[kr * D + 8 * bchunk<CPR>(kr, 2 * st + hf)]);
+        sh = mfma32x32x16(ka, qf[st], sh);
+        ph = mfma32x32x16(va, dof[st], ph);
+      }
+      const uint32_t bits = static_cast<uint32_t>(vm >> (32 * kb + 16 * hf)) & 0xffffu;
+      f32x8 d8[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool ok = ((bits >> r) & 1u) && (32 * kb + r <= lim_i);
+        const float pa = ok ? fast_exp2(fmaf(sh[r], c2, -lse2)) : 0.f;
+        d8[r >> 3][r & 7] = ok ? pa * (ph[r] - Di) : 0.f;
+      }
+      // dQ^T += K^T dS^T: MFMA u covers keys 32kb + 16(l/32) + 8u + e
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const bf16x8 ds = to_bf16x8(d8[2 * kb + u]);
+        const bf16x8 ds = to_bf16x8(d8[u]);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const int d = db * 32 + tr_dg * 16 + 4 * tr_q;
@@ -450,7 +444,7 @@ hipError_t launch_backward(const StepShape& sh, const BackwardArgs& a, hipStream
   const int wgp = (n_rb + kBWaves - 1) / kBWaves;
   float* Dws = static_cast<float*>(a.workspace);
 #define H2O_LAUNCH_DQ(DD)                                                                              \
-  hipLaunchKernelGGL(bwd_dq_kernel<DD>, dim3(n_heads * wgp), dim3(256), 0, st,                         \
+  hipLaunchKernelGGL(bwd_dq_kernel<DD>, dim3(n_heads * wgp), dim3(512), 0, st,                         \
                      static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k_cache),          \
                      static_cast<const bf16_t*>(a.v_cache), a.pos, static_cast<const bf16_t*>(a.k_new), \
                      static_cast<const bf16_t*>(a.v_new), static_cast<const bf16_t*>(a.out),          \
