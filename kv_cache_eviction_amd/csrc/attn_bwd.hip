@@ -34,8 +34,19 @@ constexpr int kBWaves = 8;     // row blocks (waves) per dQ workgroup
 __device__ __forceinline__ int bkrow_of_key(int k) {
   return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3);
 }
+// Swizzled 16-byte chunk of a tile row (CPR chunks per row).  A tile here is
+// read two ways: by rows (16 lanes, 16 consecutive rows, one chunk each) and
+// by transpose reads (32 lanes, 4 consecutive rows x 4 consecutive chunks).
+// The XOR mask is a bijection over each 16 rows and gives the 4 rows of an
+// aligned group distinct high chunk bits, so both patterns hit all 64 banks
+// once.  Rows of D = 64 are 128 bytes: even and odd rows use opposite bank
+// halves and the mask runs over row / 2.
 template <int CPR>
-__device__ __forceinline__ int bchunk(int row, int c) { return c ^ (row & (CPR - 1)); }
+__device__ __forceinline__ int bchunk(int row, int c) {
+  static_assert(CPR == 8 || CPR == 16, "head dims 64 and 128");
+  if constexpr (CPR == 16) return c ^ (((row & 3) << 2) | ((row >> 2) & 3));
+  return c ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
 
 // ---------------------------------------------------------------- dQ and D
 template <int D>
