@@ -22,6 +22,8 @@
 //     KV group (S = Q K^T, lane = key), accumulating dV^T += dO^T P and
 //     dK^T += Q^T dS with dO^T and Q^T from transpose reads of the staged
 //     row block, and fold their sums at the end.
+#include <type_traits>
+
 #include "h2o_device.h"
 #include "h2o_launch.h"
 
@@ -231,19 +233,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     bf16_t* __restrict__ dVn, int Hq, int Hkv, int S, int M, float c2, float scale, int n_heads,
     int n_ct, int n_tiles) {
   constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
-  constexpr int NCH = 32 * CPR / 256;              // chunks per thread of a row set per 32-row block
+  constexpr int RB = 2 * D;                        // bytes per row
+  constexpr int TB = 32 * RB;                      // bytes per 32-row block
+  constexpr int NCH = 32 * CPR / 256;              // 16-byte copies per thread of a row set per block
   constexpr int NKV = kKeysPerWG * CPR / 512;      // chunks per thread of the key rows
-  __shared__ __attribute__((aligned(16))) bf16_t Kl[kKeysPerWG * D];
-  __shared__ __attribute__((aligned(16))) bf16_t Vl[kKeysPerWG * D];
-  // [row set][buffer]: the next row block is fetched into registers while
-  // the current one is computed, then stored into the other buffer
-  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][2][32 * D];
-  __shared__ __attribute__((aligned(16))) bf16_t Gs[2][2][32 * D];
-  __shared__ __attribute__((aligned(16))) float s_lse2[2][2][32];
-  __shared__ __attribute__((aligned(16))) float s_D[2][2][32];
-  __shared__ __attribute__((aligned(16))) int s_irow[2][2][32];
+  // LDS: Q and dO blocks of the two row sets in two buffers -- the next block
+  // is copied in while the current one is computed; one array per buffer, so
+  // the compiler sees that reads of one do not wait for copies into the
+  // other --, the workgroup's K and V rows, and the per-row scalars
+  // [buffer][row set][32]
+  __shared__ __attribute__((aligned(16))) char q_b0[2 * TB], q_b1[2 * TB], g_b0[2 * TB], g_b1[2 * TB];
+  __shared__ __attribute__((aligned(16))) char kv_rows[2 * kKeysPerWG * RB];
+  __shared__ __attribute__((aligned(16))) float s_lse2[2][64], s_D[2][64];
+  __shared__ __attribute__((aligned(16))) int s_irow[2][64];
+  constexpr int kV = kKeysPerWG * RB;              // V rows after the K rows
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, col = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = wave & 3, rs = wave >> 2;
   const int ltid = tid & 255;                      // thread index within the row set
   const int bh = blockIdx.x % n_heads;
@@ -266,8 +272,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   for (int c = 0; c < NKV; ++c) {
     const int idx = c * 512 + tid, row = idx / CPR, ch = idx % CPR;
     const size_t src = static_cast<size_t>(min(base + row, lim - 1)) * D + ch * 8;
-    store_u32x4(&Kl[row * D + 8 * bchunk<CPR>(row, ch)], load_u32x4(kh + src));
-    store_u32x4(&Vl[row * D + 8 * bchunk<CPR>(row, ch)], load_u32x4(vh + src));
+    const int o = row * RB + 16 * bchunk<CPR>(row, ch);
+    store_u32x4(kv_rows + o, load_u32x4(kh + src));
+    store_u32x4(kv_rows + kV + o, load_u32x4(vh + src));
   }
   f32x16 dk[DB], dv[DB];
 #pragma unroll
@@ -281,8 +288,32 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   const bf16_t* ghead = dO + static_cast<size_t>(b * Hq + kvh * G) * S * D;
   const float* lhead = lse + static_cast<size_t>(b * Hq + kvh * G) * S;
   const float* dhead = Dws + static_cast<size_t>(b * Hq + kvh * G) * S;
+  // rows past the group's end read as zeros (and get lse = +inf below)
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qhead, static_cast<uint32_t>(n_rows) * RB);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(ghead, static_cast<uint32_t>(n_rows) * RB);
   const int tr_j = lane & 15, tr_r = tr_j >> 2, tr_q = tr_j & 3, tr_dg = (lane >> 4) & 1;
   const int krow = kg * 32 + col;                  // LDS row of this lane's key
+
+  // Lane byte offsets into a block or the key rows.  Swizzled chunk c of row
+  // r sits at r*RB + 16*(c ^ mask(r)); a constant change of c is then an XOR
+  // of the offset, so each read below costs one v_xor from these bases.
+  //   a_row: row col, chunk hf (chunk 2st+hf = a_row ^ 32st)
+  //   a_key: K row krow, chunk hf
+  //   a_tr : transpose read of rows 4hf+tr_r, element 16 tr_dg + 4 tr_q
+  //          (+32 db: ^ 64db; rows +16u: + 16u*RB; rows +8: ^ 32, + 8*RB)
+  const uint32_t a_row = col * RB + 16 * bchunk<CPR>(col, hf);
+  const uint32_t a_key = krow * RB + 16 * bchunk<CPR>(krow, hf);
+  const int trow = 4 * hf + tr_r;
+  const uint32_t a_tr = trow * RB + 16 * bchunk<CPR>(trow, 2 * tr_dg + (tr_q >> 1)) + 8 * (tr_q & 1);
+  // copy lanes: slot s = row*CPR + physical chunk of a block receives the
+  // logical chunk that the swizzle puts there
+  const int wl = wave & 3;                         // wave within the row set
+  uint32_t cp_off[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int sl = c * 256 + wl * 64 + lane, row = sl / CPR;
+    cp_off[c] = row * RB + 16 * bchunk<CPR>(row, sl % CPR);
+  }
 
   // chunk keys only see queries i >= key: blocks whose queries all precede
   // the tile are skipped; next_block(r0) is the first block after r0 to do
@@ -295,15 +326,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     while (r0 < n_rows && skipped(r0)) r0 += 32;
     return r0;
   };
-  u32x4 fq[NCH], fg[NCH];
   float f_l = 0.f, f_d = 0.f;
-  auto fetch = [&](int r0) __attribute__((always_inline)) {
+  // block r0 of this row set -> buffer bf (copies land in LDS asynchronously)
+  auto fetch = [&](int r0, auto bfc) __attribute__((always_inline)) {
+    constexpr int bf = decltype(bfc)::value;
+    const uint32_t soff = static_cast<uint32_t>(r0) * RB;
+    char* qd = (bf ? q_b1 : q_b0) + rs * TB + wl * 1024;
+    char* gd = (bf ? g_b1 : g_b0) + rs * TB + wl * 1024;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int idx = c * 256 + ltid, row = idx / CPR, ch = idx % CPR;
-      const int r = min(r0 + row, n_rows - 1);
-      fq[c] = load_u32x4(qhead + static_cast<size_t>(r) * D + ch * 8);
-      fg[c] = load_u32x4(ghead + static_cast<size_t>(r) * D + ch * 8);
+      dma16(rq, qd + c * 4096, cp_off[c], soff);
+      dma16(rg, gd + c * 4096, cp_off[c], soff);
     }
     if (ltid < 32) {
       const int rc = min(r0 + ltid, n_rows - 1);
@@ -311,47 +344,50 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       f_d = dhead[rc];
     }
   };
-  auto commit = [&](int r0, int bf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int idx = c * 256 + ltid, row = idx / CPR, ch = idx % CPR;
-      store_u32x4(&Qs[rs][bf][row * D + 8 * bchunk<CPR>(row, ch)], fq[c]);
-      store_u32x4(&Gs[rs][bf][row * D + 8 * bchunk<CPR>(row, ch)], fg[c]);
-    }
+  auto commit = [&](int r0, auto bfc) __attribute__((always_inline)) {
+    constexpr int bf = decltype(bfc)::value;
     if (ltid < 32) {
-      const int r = r0 + ltid;
-      s_lse2[rs][bf][ltid] = r < n_rows ? f_l * kLog2e : __builtin_huge_valf();
-      s_D[rs][bf][ltid] = r < n_rows ? f_d : 0.f;
-      s_irow[rs][bf][ltid] = r < n_rows ? r % S : -1;
+      const int r = r0 + ltid, o = rs * 32 + ltid;
+      s_lse2[bf][o] = r < n_rows ? f_l * kLog2e : __builtin_huge_valf();
+      s_D[bf][o] = r < n_rows ? f_d : 0.f;
+      s_irow[bf][o] = r < n_rows ? r % S : -1;
     }
   };
-  auto compute = [&](int bf) __attribute__((always_inline)) {
-    const bf16_t* qs = Qs[rs][bf];
-    const bf16_t* gs = Gs[rs][bf];
+  // chunk tiles: key k sees query i only if k <= i (cache tiles: every query;
+  // rows past the group's end carry i = -1 and lse = +inf)
+  const int key_thr = !key_ok ? 0x7fffffff : is_cache ? -0x40000000 : key;
+  auto compute = [&](auto bfc) __attribute__((always_inline)) {
+    constexpr int bf = decltype(bfc)::value;
+    const char* qs = bf ? q_b1 : q_b0;
+    const char* gs = bf ? g_b1 : g_b0;
+    const uint32_t blk = rs * TB;
+    uint32_t ak = a_key;
+    asm volatile("" : "+v"(ak));                   // per-step offsets stay in the loop
+    const uint32_t aq = a_row + blk;
     // S and dP (queries x keys): register r of lane l <-> row 8(r/4) + 4(l/32) + r%4
     f32x16 s = zero16(), p = zero16();
 #pragma unroll
     for (int st = 0; st < DS; ++st) {
-      const int kc = 8 * bchunk<CPR>(krow, 2 * st + hf);
-      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&qs[col * D + 8 * bchunk<CPR>(col, 2 * st + hf)]);
-      const bf16x8 ga = *reinterpret_cast<const bf16x8*>(&gs[col * D + 8 * bchunk<CPR>(col, 2 * st + hf)]);
-      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&Kl[krow * D + kc]);
-      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&Vl[krow * D + kc]);
+      const uint32_t oq = aq ^ (32 * st), ok = ak ^ (32 * st);
+      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qs + oq);
+      const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gs + oq);
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(kv_rows + ok);
+      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(kv_rows + kV + ok);
       s = mfma32x32x16(qa, kb, s);
       p = mfma32x32x16(ga, vb, p);
     }
     f32x8 pp[2], dd[2];
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
-      const int row0 = 8 * a4 + 4 * hf;
-      const f32x4 l2 = *reinterpret_cast<const f32x4*>(&s_lse2[rs][bf][row0]);
-      const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&s_D[rs][bf][row0]);
-      const int4 iv = *reinterpret_cast<const int4*>(&s_irow[rs][bf][row0]);
+      const int row0 = rs * 32 + 8 * a4 + 4 * hf;
+      const f32x4 l2 = *reinterpret_cast<const f32x4*>(&s_lse2[bf][row0]);
+      const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&s_D[bf][row0]);
+      const int4 iv = *reinterpret_cast<const int4*>(&s_irow[bf][row0]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * a4 + e;
         const int qi = e == 0 ? iv.x : e == 1 ? iv.y : e == 2 ? iv.z : iv.w;
-        const bool ok = key_ok && (is_cache || key <= qi);
+        const bool ok = key_thr <= qi;
         const float pr = ok ? fast_exp2(fmaf(s[r], c2, -l2[e])) : 0.f;
         pp[r >> 3][r & 7] = pr;
         dd[r >> 3][r & 7] = ok ? pr * (p[r] - dv4[e]) : 0.f;
@@ -359,18 +395,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     }
     // dV^T += dO^T P and dK^T += Q^T dS: MFMA u contracts over the rows held
     // in registers 8u..8u+7, i.e. rows 16u + 4(l/32) + {0..3, 8..11}
+    const uint32_t at0 = a_tr + blk, at1 = at0 ^ 32;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const bf16x8 pb = to_bf16x8(pp[u]);
       const bf16x8 db8 = to_bf16x8(dd[u]);
-      const int ra = 16 * u + 4 * hf + tr_r, rbx = ra + 8;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int d = db * 32 + tr_dg * 16 + 4 * tr_q;
-        const bf16x4 g0 = lds_read_tr16(&gs[ra * D + 8 * bchunk<CPR>(ra, d >> 3) + (d & 7)]);
-        const bf16x4 g1 = lds_read_tr16(&gs[rbx * D + 8 * bchunk<CPR>(rbx, d >> 3) + (d & 7)]);
-        const bf16x4 q0 = lds_read_tr16(&qs[ra * D + 8 * bchunk<CPR>(ra, d >> 3) + (d & 7)]);
-        const bf16x4 q1 = lds_read_tr16(&qs[rbx * D + 8 * bchunk<CPR>(rbx, d >> 3) + (d & 7)]);
+        const uint32_t o0 = (at0 ^ (64 * db)) + 16 * u * RB;
+        const uint32_t o1 = (at1 ^ (64 * db)) + (16 * u + 8) * RB;
+        const bf16x4 g0 = lds_read_tr16(reinterpret_cast<const bf16_t*>(gs + o0));
+        const bf16x4 g1 = lds_read_tr16(reinterpret_cast<const bf16_t*>(gs + o1));
+        const bf16x4 q0 = lds_read_tr16(reinterpret_cast<const bf16_t*>(qs + o0));
+        const bf16x4 q1 = lds_read_tr16(reinterpret_cast<const bf16_t*>(qs + o1));
         dv[db] = mfma32x32x16(__builtin_shufflevector(g0, g1, 0, 1, 2, 3, 4, 5, 6, 7), pb, dv[db]);
         dk[db] = mfma32x32x16(__builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7), db8, dk[db]);
       }
@@ -379,31 +416,38 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 
   // The needed blocks in order are split alternately: row set 0 takes the
   // 1st, 3rd, ..., row set 1 the 2nd, 4th, ... (ra, rb: the two sets'
-  // current blocks, tracked by every wave).  Buffer (rs, bf) is rewritten two
-  // iterations after it was read, behind the barrier of the one in between.
+  // current blocks, tracked by every wave).  A buffer is refilled one
+  // iteration after it was read, behind that iteration's barrier.
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
   int ra = skipped(0) ? next_block(0) : 0;
   int rb = ra < n_rows ? next_block(ra) : n_rows;
   int r0 = rs ? rb : ra;
-  if (r0 < n_rows) fetch(r0);
-  int bf = 0;
-  while (ra < n_rows) {
-    if (r0 < n_rows) commit(r0, bf);
-    __syncthreads();                   // also orders the key rows' stores before the first reads
+  if (r0 < n_rows) fetch(r0, I0{});
+  // one iteration on buffer bf; false once every block is done
+  auto step = [&](auto bfc) __attribute__((always_inline)) {
+    using BN = std::integral_constant<int, decltype(bfc)::value ^ 1>;
+    if (ra >= n_rows) return false;
+    if (r0 < n_rows) commit(r0, bfc);
+    wait_vmem_all();                   // this wave's copies of the block have landed
+    barrier_lds();                     // ... and every wave's; also orders the key rows' stores
     const int na = rb < n_rows ? next_block(rb) : n_rows;
     const int nb = na < n_rows ? next_block(na) : n_rows;
     const int rn = rs ? nb : na;
-    if (rn < n_rows) fetch(rn);
-    if (r0 < n_rows && has_keys) compute(bf);
+    if (rn < n_rows) fetch(rn, BN{});
+    if (r0 < n_rows && has_keys) compute(bfc);
     ra = na;
     rb = nb;
     r0 = rn;
-    bf ^= 1;
+    return true;
+  };
+  while (step(I0{}) && step(I1{})) {
   }
 
   // fold row set 1's dK, dV into row set 0's, one 32-row block of the
   // accumulators per round through the query buffers
   __syncthreads();
-  float* xo = reinterpret_cast<float*>(&Qs[0][0][0]);     // 16 x 256 floats per round
+  float* xo = reinterpret_cast<float*>(kv_rows);     // 16 x 256 floats per round
   const int xs = kg * 64 + lane;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
