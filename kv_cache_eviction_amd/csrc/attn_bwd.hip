@@ -353,11 +353,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       s_irow[bf][o] = r < n_rows ? r % S : -1;
     }
   };
-  // chunk tiles: key k sees query i only if k <= i (cache tiles: every query;
-  // rows past the group's end carry i = -1 and lse = +inf)
-  const int key_thr = !key_ok ? 0x7fffffff : is_cache ? -0x40000000 : key;
-  auto compute = [&](auto bfc) __attribute__((always_inline)) {
+  // chunk tiles: key k sees query i only if k <= i (rows past the group's end
+  // carry i = -1 and lse = +inf).  Cache tiles need no mask per element: a
+  // key's dK/dV columns depend on no other key, so a lane whose slot is empty
+  // just stores zeros at the end (its K/V rows are finite).
+  const int key_thr = key_ok ? key : 0x7fffffff;
+  auto compute = [&](auto bfc, auto causal_c) __attribute__((always_inline)) {
     constexpr int bf = decltype(bfc)::value;
+    constexpr bool causal = decltype(causal_c)::value;
     const char* qs = bf ? q_b1 : q_b0;
     const char* gs = bf ? g_b1 : g_b0;
     const uint32_t blk = rs * TB;
@@ -382,15 +385,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       const int row0 = rs * 32 + 8 * a4 + 4 * hf;
       const f32x4 l2 = *reinterpret_cast<const f32x4*>(&s_lse2[bf][row0]);
       const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&s_D[bf][row0]);
-      const int4 iv = *reinterpret_cast<const int4*>(&s_irow[bf][row0]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * a4 + e;
-        const int qi = e == 0 ? iv.x : e == 1 ? iv.y : e == 2 ? iv.z : iv.w;
-        const bool ok = key_thr <= qi;
-        const float pr = ok ? fast_exp2(fmaf(s[r], c2, -l2[e])) : 0.f;
-        pp[r >> 3][r & 7] = pr;
-        dd[r >> 3][r & 7] = ok ? pr * (p[r] - dv4[e]) : 0.f;
+        const float pe = fast_exp2(fmaf(s[r], c2, -l2[e]));
+        if constexpr (causal) {
+          const int4 iv = *reinterpret_cast<const int4*>(&s_irow[bf][row0]);
+          const int qi = e == 0 ? iv.x : e == 1 ? iv.y : e == 2 ? iv.z : iv.w;
+          const bool ok = key_thr <= qi;
+          const float pr = ok ? pe : 0.f;
+          pp[r >> 3][r & 7] = pr;
+          dd[r >> 3][r & 7] = ok ? pr * (p[r] - dv4[e]) : 0.f;
+        } else {
+          pp[r >> 3][r & 7] = pe;
+          dd[r >> 3][r & 7] = pe * (p[r] - dv4[e]);
+        }
       }
     }
     // dV^T += dO^T P and dK^T += Q^T dS: MFMA u contracts over the rows held
@@ -425,7 +434,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   int r0 = rs ? rb : ra;
   if (r0 < n_rows) fetch(r0, I0{});
   // one iteration on buffer bf; false once every block is done
-  auto step = [&](auto bfc) __attribute__((always_inline)) {
+  auto step = [&](auto bfc, auto causal_c) __attribute__((always_inline)) {
     using BN = std::integral_constant<int, decltype(bfc)::value ^ 1>;
     if (ra >= n_rows) return false;
     if (r0 < n_rows) commit(r0, bfc);
@@ -435,13 +444,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const int nb = na < n_rows ? next_block(na) : n_rows;
     const int rn = rs ? nb : na;
     if (rn < n_rows) fetch(rn, BN{});
-    if (r0 < n_rows && has_keys) compute(bfc);
+    if (r0 < n_rows && has_keys) compute(bfc, causal_c);
     ra = na;
     rb = nb;
     r0 = rn;
     return true;
   };
-  while (step(I0{}) && step(I1{})) {
+  if (is_cache) {
+    while (step(I0{}, std::false_type{}) && step(I1{}, std::false_type{})) {
+    }
+  } else {
+    while (step(I0{}, std::true_type{}) && step(I1{}, std::true_type{})) {
+    }
   }
 
   // fold row set 1's dK, dV into row set 0's, one 32-row block of the
@@ -467,6 +481,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     }
   }
   if (rs == 1 || key >= lim) return;
+  if (!key_ok) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      dk[db] = zero16();
+      dv[db] = zero16();
+    }
+  }
   bf16_t* ko = (is_cache ? dKc + static_cast<size_t>(bh) * M * D : dKn + static_cast<size_t>(bh) * S * D) +
                static_cast<size_t>(key) * D;
   bf16_t* vo = (is_cache ? dVc + static_cast<size_t>(bh) * M * D : dVn + static_cast<size_t>(bh) * S * D) +
