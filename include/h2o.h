@@ -168,7 +168,8 @@ H2O_API h2o_status h2o_get_scores(const h2o_cache* c, float* scores_out,
  * Outputs (every element written): dq [B,Hq,s,d]; dk_cache, dv_cache
  * [B,Hkv,M,d] (zero at free slots); dk_new, dv_new [B,Hkv,s,d]; all bf16.
  * dK/dV of a KV head sum over the G query heads of its group.
- * workspace >= h2o_backward_workspace_bytes(cfg, s) (holds dO . O per row).
+ * workspace >= h2o_backward_workspace_bytes(cfg, s) (holds dO . O per row and
+ * the fp32 partial dK/dV of the chunk keys; contents need no initialisation).
  * Deterministic (no atomics).  Errors: H2O_ERR_NULL, H2O_ERR_CONFIG,
  * H2O_ERR_UNSUPPORTED (fp32 configs), H2O_ERR_SHAPE (s < 1 or s larger than
  * max(max_chunk, max_prefill)), H2O_ERR_WORKSPACE, H2O_ERR_HIP. */

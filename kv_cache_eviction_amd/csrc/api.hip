@@ -341,7 +341,7 @@ int32_t h2o_last_hip_error(const h2o_cache* c) { return c ? c->last_hip_error : 
 
 size_t h2o_backward_workspace_bytes(const h2o_config* cfg, int32_t s) {
   if (h2o_validate_config(cfg) != H2O_OK || s < 1) return 0;
-  return h2o::backward_workspace_bytes(cfg->batch, cfg->n_q_heads, s);
+  return h2o::backward_workspace_bytes(cfg->batch, cfg->n_q_heads, cfg->n_kv_heads, s, cfg->head_dim);
 }
 
 h2o_status h2o_chunk_backward(const h2o_config* cfg, const void* q, const void* k_cache,
@@ -357,7 +357,7 @@ h2o_status h2o_chunk_backward(const h2o_config* cfg, const void* q, const void* 
   if (r != H2O_OK) return r;
   if (cfg->dtype != H2O_BF16) return H2O_ERR_UNSUPPORTED;
   if (s < 1 || s > max_len(cfg)) return H2O_ERR_SHAPE;
-  if (workspace_bytes < h2o::backward_workspace_bytes(cfg->batch, cfg->n_q_heads, s))
+  if (workspace_bytes < h2o::backward_workspace_bytes(cfg->batch, cfg->n_q_heads, cfg->n_kv_heads, s, cfg->head_dim))
     return H2O_ERR_WORKSPACE;
   h2o::StepShape sh;
   sh.B = cfg->batch;

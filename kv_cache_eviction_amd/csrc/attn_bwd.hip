@@ -218,6 +218,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
 
 // ---------------------------------------------------------------- dK and dV
 constexpr int kKeysPerWG = 128;     // 4 key groups x 32 keys
+// A chunk-key tile only sees the queries at or after its first key, so its
+// work shrinks along the chunk; each chunk tile's query rows are split into
+// kPieces equal pieces, taken by separate workgroups that write fp32 partial
+// dK/dV for a reduction kernel.  With the cache tiles whole, the workgroups
+// then fill the CUs evenly instead of leaving a last, half-empty round.
+constexpr int kPieces = 4;
 
 // 8 waves: key group kg = wave % 4 owns 32 keys (lane = key column), row set
 // rs = wave / 4 takes every other needed query row block; the two row sets
@@ -229,9 +235,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
     const int32_t* __restrict__ pos, const bf16_t* __restrict__ Kn, const bf16_t* __restrict__ Vn,
     const bf16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dws,
-    bf16_t* __restrict__ dKc, bf16_t* __restrict__ dVc, bf16_t* __restrict__ dKn,
-    bf16_t* __restrict__ dVn, int Hq, int Hkv, int S, int M, float c2, float scale, int n_heads,
-    int n_ct, int n_tiles) {
+    bf16_t* __restrict__ dKc, bf16_t* __restrict__ dVc, float* __restrict__ part, int Hq,
+    int Hkv, int S, int M, float c2, float scale, int n_heads, int n_ct, int n_cht) {
   constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
   constexpr int RB = 2 * D;                        // bytes per row
   constexpr int TB = 32 * RB;                      // bytes per 32-row block
@@ -253,11 +258,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   const int kg = wave & 3, rs = wave >> 2;
   const int ltid = tid & 255;                      // thread index within the row set
   const int bh = blockIdx.x % n_heads;
-  const int tile = static_cast<int>(blockIdx.x) / n_heads;
+  const int tix = static_cast<int>(blockIdx.x) / n_heads;     // cache tiles, then (chunk tile, piece)
   const int b = bh / Hkv, kvh = bh - b * Hkv;
   const int G = Hq / Hkv;
-  const bool is_cache = tile < n_ct;
-  const int base = (is_cache ? tile : tile - n_ct) * kKeysPerWG;
+  const bool is_cache = tix < n_ct;
+  const int cti = is_cache ? 0 : (tix - n_ct) / kPieces;
+  const int piece = is_cache ? 0 : tix - n_ct - cti * kPieces;
+  const int base = (is_cache ? tix : cti) * kKeysPerWG;
   const int lim = is_cache ? M : S;
   const int key = base + kg * 32 + col;            // this lane's key column
   const bf16_t* kh = is_cache ? Kc + static_cast<size_t>(bh) * M * D : Kn + static_cast<size_t>(bh) * S * D;
@@ -284,6 +291,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   }
 
   const int n_rows = G * S;
+  // rows [r_lo, r_hi) of the group are this workgroup's: all of them for a
+  // cache tile; for a chunk tile, piece p of the needed rows (g, i >= base)
+  // numbered o = g*(S - base) + i - base, o in [p*N/P, (p+1)*N/P)
+  int r_lo = 0, r_hi = n_rows;
+  if (!is_cache) {
+    const int L = S - base, N = G * L;
+    const int o_lo = piece * N / kPieces, o_hi = (piece + 1) * N / kPieces;
+    r_lo = o_lo < N ? (o_lo / L) * S + base + o_lo % L : n_rows;
+    r_hi = o_hi < N ? (o_hi / L) * S + base + o_hi % L : n_rows;
+  }
   const bf16_t* qhead = Q + static_cast<size_t>(b * Hq + kvh * G) * S * D;   // rows g*S + i
   const bf16_t* ghead = dO + static_cast<size_t>(b * Hq + kvh * G) * S * D;
   const float* lhead = lse + static_cast<size_t>(b * Hq + kvh * G) * S;
@@ -323,7 +340,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   };
   auto next_block = [&](int r0) __attribute__((always_inline)) {
     r0 += 32;
-    while (r0 < n_rows && skipped(r0)) r0 += 32;
+    while (r0 < r_hi && skipped(r0)) r0 += 32;
     return r0;
   };
   float f_l = 0.f, f_d = 0.f;
@@ -348,9 +365,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     constexpr int bf = decltype(bfc)::value;
     if (ltid < 32) {
       const int r = r0 + ltid, o = rs * 32 + ltid;
-      s_lse2[bf][o] = r < n_rows ? f_l * kLog2e : __builtin_huge_valf();
-      s_D[bf][o] = r < n_rows ? f_d : 0.f;
-      s_irow[bf][o] = r < n_rows ? r % S : -1;
+      const bool mine = r >= r_lo && r < r_hi;
+      s_lse2[bf][o] = mine ? f_l * kLog2e : __builtin_huge_valf();
+      s_D[bf][o] = mine ? f_d : 0.f;
+      s_irow[bf][o] = mine ? r % S : -1;
     }
   };
   // chunk tiles: key k sees query i only if k <= i (rows past the group's end
@@ -429,22 +447,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   // iteration after it was read, behind that iteration's barrier.
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  int ra = skipped(0) ? next_block(0) : 0;
-  int rb = ra < n_rows ? next_block(ra) : n_rows;
+  const int r_first = r_lo & ~31;
+  int ra = r_lo >= r_hi ? r_hi : skipped(r_first) ? next_block(r_first) : r_first;
+  int rb = ra < r_hi ? next_block(ra) : r_hi;
   int r0 = rs ? rb : ra;
-  if (r0 < n_rows) fetch(r0, I0{});
+  if (r0 < r_hi) fetch(r0, I0{});
   // one iteration on buffer bf; false once every block is done
   auto step = [&](auto bfc, auto causal_c) __attribute__((always_inline)) {
     using BN = std::integral_constant<int, decltype(bfc)::value ^ 1>;
-    if (ra >= n_rows) return false;
-    if (r0 < n_rows) commit(r0, bfc);
+    if (ra >= r_hi) return false;
+    if (r0 < r_hi) commit(r0, bfc);
     wait_vmem_all();                   // this wave's copies of the block have landed
     barrier_lds();                     // ... and every wave's; also orders the key rows' stores
-    const int na = rb < n_rows ? next_block(rb) : n_rows;
-    const int nb = na < n_rows ? next_block(na) : n_rows;
+    const int na = rb < r_hi ? next_block(rb) : r_hi;
+    const int nb = na < r_hi ? next_block(na) : r_hi;
     const int rn = rs ? nb : na;
-    if (rn < n_rows) fetch(rn, BN{});
-    if (r0 < n_rows && has_keys) compute(bfc, causal_c);
+    if (rn < r_hi) fetch(rn, BN{});
+    if (r0 < r_hi && has_keys) compute(bfc, causal_c);
     ra = na;
     rb = nb;
     r0 = rn;
@@ -488,28 +507,76 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       dv[db] = zero16();
     }
   }
-  bf16_t* ko = (is_cache ? dKc + static_cast<size_t>(bh) * M * D : dKn + static_cast<size_t>(bh) * S * D) +
-               static_cast<size_t>(key) * D;
-  bf16_t* vo = (is_cache ? dVc + static_cast<size_t>(bh) * M * D : dVn + static_cast<size_t>(bh) * S * D) +
-               static_cast<size_t>(key) * D;
   // accumulator register r of lane l: d = 32 db + 8(r/4) + 4(l/32) + r%4, key column l%32
+  if (is_cache) {
+    bf16_t* ko = dKc + (static_cast<size_t>(bh) * M + key) * D;
+    bf16_t* vo = dVc + (static_cast<size_t>(bh) * M + key) * D;
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < DB; ++db) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      f32x4 kv = {dk[db][4 * a] * scale, dk[db][4 * a + 1] * scale, dk[db][4 * a + 2] * scale,
-                  dk[db][4 * a + 3] * scale};
-      f32x4 vv = {dv[db][4 * a], dv[db][4 * a + 1], dv[db][4 * a + 2], dv[db][4 * a + 3]};
-      *reinterpret_cast<bf16x4*>(ko + db * 32 + 8 * a + 4 * hf) = to_bf16x4(kv);
-      *reinterpret_cast<bf16x4*>(vo + db * 32 + 8 * a + 4 * hf) = to_bf16x4(vv);
+      for (int a = 0; a < 4; ++a) {
+        f32x4 kv = {dk[db][4 * a] * scale, dk[db][4 * a + 1] * scale, dk[db][4 * a + 2] * scale,
+                    dk[db][4 * a + 3] * scale};
+        f32x4 vv = {dv[db][4 * a], dv[db][4 * a + 1], dv[db][4 * a + 2], dv[db][4 * a + 3]};
+        *reinterpret_cast<bf16x4*>(ko + db * 32 + 8 * a + 4 * hf) = to_bf16x4(kv);
+        *reinterpret_cast<bf16x4*>(vo + db * 32 + 8 * a + 4 * hf) = to_bf16x4(vv);
+      }
+    }
+  } else {
+    // partials [dK | dV][piece][head][key < n_cht * 128][d], unscaled
+    const size_t s_pad = static_cast<size_t>(n_cht) * kKeysPerWG;
+    float* ko = part + ((static_cast<size_t>(piece) * n_heads + bh) * s_pad + key) * D;
+    float* vo = ko + static_cast<size_t>(kPieces) * n_heads * s_pad * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        f32x4 kv = {dk[db][4 * a], dk[db][4 * a + 1], dk[db][4 * a + 2], dk[db][4 * a + 3]};
+        f32x4 vv = {dv[db][4 * a], dv[db][4 * a + 1], dv[db][4 * a + 2], dv[db][4 * a + 3]};
+        *reinterpret_cast<f32x4*>(ko + db * 32 + 8 * a + 4 * hf) = kv;
+        *reinterpret_cast<f32x4*>(vo + db * 32 + 8 * a + 4 * hf) = vv;
+      }
     }
   }
 }
 
+// dK/dV of the chunk keys: sum of the kPieces partials in piece order
+// (deterministic), dK scaled, written in bf16.  One thread per 4 elements.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_chunk_reduce_kernel(const float* __restrict__ part,
+                                                               bf16_t* __restrict__ dKn,
+                                                               bf16_t* __restrict__ dVn, int S,
+                                                               int n_heads, int n_cht, float scale) {
+  constexpr int C4 = D / 4;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<int64_t>(n_heads) * S * C4) return;
+  const int c4 = static_cast<int>(idx % C4);
+  const int64_t kr = idx / C4;                     // bh * S + key
+  const int key = static_cast<int>(kr % S), bh = static_cast<int>(kr / S);
+  const size_t s_pad = static_cast<size_t>(n_cht) * kKeysPerWG;
+  const size_t ps = static_cast<size_t>(n_heads) * s_pad * D;      // one piece
+  const float* src = part + (static_cast<size_t>(bh) * s_pad + key) * D + 4 * c4;
+  f32x4 sk = *reinterpret_cast<const f32x4*>(src);
+  f32x4 sv = *reinterpret_cast<const f32x4*>(src + kPieces * ps);
+#pragma unroll
+  for (int p = 1; p < kPieces; ++p) {
+    sk += *reinterpret_cast<const f32x4*>(src + p * ps);
+    sv += *reinterpret_cast<const f32x4*>(src + kPieces * ps + p * ps);
+  }
+  *reinterpret_cast<bf16x4*>(dKn + kr * D + 4 * c4) = to_bf16x4(sk * scale);
+  *reinterpret_cast<bf16x4*>(dVn + kr * D + 4 * c4) = to_bf16x4(sv);
+}
+
 }  // namespace
 
-size_t backward_workspace_bytes(int B, int Hq, int S) {
-  return static_cast<size_t>(B) * Hq * S * sizeof(float);
+// D_i per query row, then the chunk tiles' partial dK/dV
+static size_t backward_d_bytes(int B, int Hq, int S) {
+  return (static_cast<size_t>(B) * Hq * S * sizeof(float) + 255) & ~static_cast<size_t>(255);
+}
+size_t backward_workspace_bytes(int B, int Hq, int Hkv, int S, int D) {
+  const size_t n_cht = (static_cast<size_t>(S) + kKeysPerWG - 1) / kKeysPerWG;
+  return backward_d_bytes(B, Hq, S) +
+         2 * static_cast<size_t>(kPieces) * B * Hkv * n_cht * kKeysPerWG * D * sizeof(float);
 }
 
 hipError_t launch_backward(const StepShape& sh, const BackwardArgs& a, hipStream_t st) {
@@ -519,6 +586,7 @@ hipError_t launch_backward(const StepShape& sh, const BackwardArgs& a, hipStream
   const int n_rb = G * ((sh.S + 31) / 32);
   const int wgp = (n_rb + kBWaves - 1) / kBWaves;
   float* Dws = static_cast<float*>(a.workspace);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + backward_d_bytes(sh.B, sh.Hq, sh.S));
 #define H2O_LAUNCH_DQ(DD)                                                                              \
   hipLaunchKernelGGL(bwd_dq_kernel<DD>, dim3(n_heads * wgp), dim3(512), 0, st,                         \
                      static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k_cache),          \
@@ -532,18 +600,29 @@ hipError_t launch_backward(const StepShape& sh, const BackwardArgs& a, hipStream
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_ct = (sh.M + kKeysPerWG - 1) / kKeysPerWG;
-  const int n_tiles = n_ct + (sh.S + kKeysPerWG - 1) / kKeysPerWG;
+  const int n_cht = (sh.S + kKeysPerWG - 1) / kKeysPerWG;
 #define H2O_LAUNCH_DKDV(DD)                                                                            \
-  hipLaunchKernelGGL(bwd_dkdv_kernel<DD>, dim3(n_heads * n_tiles), dim3(512), 0, st,                   \
+  hipLaunchKernelGGL(bwd_dkdv_kernel<DD>, dim3(n_heads * (n_ct + n_cht * kPieces)), dim3(512), 0, st,  \
                      static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k_cache),          \
                      static_cast<const bf16_t*>(a.v_cache), a.pos, static_cast<const bf16_t*>(a.k_new), \
                      static_cast<const bf16_t*>(a.v_new), static_cast<const bf16_t*>(a.d_out), a.lse, \
-                     Dws, static_cast<bf16_t*>(a.dk_cache), static_cast<bf16_t*>(a.dv_cache),         \
-                     static_cast<bf16_t*>(a.dk_new), static_cast<bf16_t*>(a.dv_new), sh.Hq, sh.Hkv,   \
-                     sh.S, sh.M, c2, sh.scale, n_heads, n_ct, n_tiles)
+                     Dws, static_cast<bf16_t*>(a.dk_cache), static_cast<bf16_t*>(a.dv_cache), part,   \
+                     sh.Hq, sh.Hkv, sh.S, sh.M, c2, sh.scale, n_heads, n_ct, n_cht)
   if (sh.D == 128) H2O_LAUNCH_DKDV(128);
   else H2O_LAUNCH_DKDV(64);
 #undef H2O_LAUNCH_DKDV
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n_red = static_cast<int64_t>(n_heads) * sh.S * (sh.D / 4);
+  const unsigned red_blocks = static_cast<unsigned>((n_red + 255) / 256);
+  if (sh.D == 128)
+    hipLaunchKernelGGL(bwd_chunk_reduce_kernel<128>, dim3(red_blocks), dim3(256), 0, st, part,
+                       static_cast<bf16_t*>(a.dk_new), static_cast<bf16_t*>(a.dv_new), sh.S, n_heads, n_cht,
+                       sh.scale);
+  else
+    hipLaunchKernelGGL(bwd_chunk_reduce_kernel<64>, dim3(red_blocks), dim3(256), 0, st, part,
+                       static_cast<bf16_t*>(a.dk_new), static_cast<bf16_t*>(a.dv_new), sh.S, n_heads, n_cht,
+                       sh.scale);
   return hipGetLastError();
 }
 

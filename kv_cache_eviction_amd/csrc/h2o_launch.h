@@ -67,7 +67,7 @@ struct BackwardArgs {
   void* dv_cache;
   void* dk_new;
   void* dv_new;
-  void* workspace;         // >= backward_workspace_bytes: D_i = dO_i . O_i
+  void* workspace;         // >= backward_workspace_bytes: D_i = dO_i . O_i, partial dK/dV
 };
 
 enum Dtype { kBF16 = 0, kFP32 = 1 };
@@ -77,7 +77,7 @@ hipError_t launch_score(const StepShape& sh, const ScoreArgs& a, int dtype, hipS
 hipError_t launch_select(const StepShape& sh, const SelectArgs& a, hipStream_t st);
 hipError_t launch_scatter(const StepShape& sh, const SelectArgs& a, int dtype, hipStream_t st);
 hipError_t launch_backward(const StepShape& sh, const BackwardArgs& a, hipStream_t st);
-size_t backward_workspace_bytes(int B, int Hq, int S);
+size_t backward_workspace_bytes(int B, int Hq, int Hkv, int S, int D);
 hipError_t launch_reset(float* scores, int32_t* pos, int64_t n_slots, int32_t* counters,
                         int64_t n_counters, hipStream_t st);
 
