@@ -36,6 +36,9 @@ constexpr int kBWaves = 8;     // row blocks (waves) per dQ workgroup
 __device__ __forceinline__ int bkrow_of_key(int k) {
   return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3);
 }
+__device__ __forceinline__ int key_of_bkrow(int r) {
+  return ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3);
+}
 // Swizzled 16-byte chunk of a tile row (CPR chunks per row).  A tile here is
 // read two ways: by rows (16 lanes, 16 consecutive rows, one chunk each) and
 // by transpose reads (32 lanes, 4 consecutive rows x 4 consecutive chunks).
@@ -59,14 +62,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     float* __restrict__ Dws, bf16_t* __restrict__ dQ, int Hq, int Hkv, int S, int M, float c2,
     float scale, int n_heads, int wg_per_head) {
   constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
-  constexpr int NCH = kBKT * CPR / 512;
-  // two buffers: the next tile is fetched into registers while the current
-  // one is computed, then stored into the other buffer
-  __shared__ __attribute__((aligned(16))) bf16_t Ks2[2][kBKT * D];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs2[2][kBKT * D];
+  constexpr int RB = 2 * D;                        // bytes per row
+  constexpr int NCH = kBKT * CPR / 512;            // 16-byte copies per thread per tile and tensor
+  // two buffers: the next key tile is copied into one while the current one
+  // is computed from the other; one array per buffer, so reads of one never
+  // wait for copies into the other
+  __shared__ __attribute__((aligned(16))) char k_b0[kBKT * RB], k_b1[kBKT * RB];
+  __shared__ __attribute__((aligned(16))) char v_b0[kBKT * RB], v_b1[kBKT * RB];
   __shared__ uint64_t s_valid2[2];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, col = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bh = blockIdx.x % n_heads;
   const int wgi = wg_per_head - 1 - static_cast<int>(blockIdx.x) / n_heads;
   const int b = bh / Hkv, kvh = bh - b * Hkv;
@@ -114,53 +120,62 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   const int32_t* pos_head = pos + static_cast<size_t>(bh) * M;
   const int tr_j = lane & 15, tr_r = tr_j >> 2, tr_q = tr_j & 3, tr_dg = (lane >> 4) & 1;
 
-  u32x4 fk[NCH], fv[NCH];
+  const __amdgpu_buffer_rsrc_t rkc = make_rsrc(kc_head, static_cast<uint32_t>(M) * RB);
+  const __amdgpu_buffer_rsrc_t rvc = make_rsrc(vc_head, static_cast<uint32_t>(M) * RB);
+  const __amdgpu_buffer_rsrc_t rkn = make_rsrc(kn_head, static_cast<uint32_t>(S) * RB);
+  const __amdgpu_buffer_rsrc_t rvn = make_rsrc(vn_head, static_cast<uint32_t>(S) * RB);
+  // Tile rows sit in MFMA-row order (LDS row R holds key (R & ~31) | key_of_bkrow(R & 31)),
+  // chunks swizzled.  Copy lanes: slot s = R*CPR + physical chunk receives the
+  // logical chunk the swizzle puts there; keys past the end read as zeros.
+  uint32_t cp_off[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int sl = c * 512 + wave * 64 + lane, R = sl / CPR;
+    const int key = (R & ~31) | key_of_bkrow(R & 31);
+    cp_off[c] = key * RB + 16 * bchunk<CPR>(R, sl % CPR);
+  }
+  // Lane byte offsets (a constant change of the chunk is an XOR of the offset):
+  //   a_row: row col, chunk hf (chunk 2st+hf: ^ 32st; rows +32kb: + 32kb*RB)
+  //   a_tr : transpose read of rows 4hf+tr_r, element 16 tr_dg + 4 tr_q
+  //          (+32 db: ^ 64db; rows +16u+32kb: + that*RB; rows +8: ^ 32, + 8*RB)
+  const uint32_t a_row = col * RB + 16 * bchunk<CPR>(col, hf);
+  const int trow = 4 * hf + tr_r;
+  const uint32_t a_tr = trow * RB + 16 * bchunk<CPR>(trow, 2 * tr_dg + (tr_q >> 1)) + 8 * (tr_q & 1);
+
   int f_pos = 0;
-  auto fetch = [&](int t) __attribute__((always_inline)) {
+  auto fetch = [&](int t, auto bfc) __attribute__((always_inline)) {
+    constexpr int bf = decltype(bfc)::value;
     const bool is_cache = t < n_ct;
     const int base = is_cache ? t * kBKT : (t - n_ct) * kBKT;
-    const int lim = is_cache ? M : S;
-    const bf16_t* ks = is_cache ? kc_head : kn_head;
-    const bf16_t* vs = is_cache ? vc_head : vn_head;
+    const uint32_t soff = static_cast<uint32_t>(base) * RB;
+    char* kd = (bf ? k_b1 : k_b0) + wave * 1024;
+    char* vd = (bf ? v_b1 : v_b0) + wave * 1024;
 #pragma unroll
-    for (int r = 0; r < NCH; ++r) {
-      const int c = r * 512 + tid, key = c / CPR, ch = c % CPR;
-      const int src = min(base + key, lim - 1);
-      fk[r] = load_u32x4(ks + static_cast<size_t>(src) * D + ch * 8);
-      fv[r] = load_u32x4(vs + static_cast<size_t>(src) * D + ch * 8);
+    for (int c = 0; c < NCH; ++c) {
+      dma16(is_cache ? rkc : rkn, kd + c * 8192, cp_off[c], soff);
+      dma16(is_cache ? rvc : rvn, vd + c * 8192, cp_off[c], soff);
     }
     if (wave == 0) f_pos = pos_head[is_cache ? min(base + lane, M - 1) : 0];
   };
-  auto commit = [&](int t, int bf) __attribute__((always_inline)) {
+  auto commit = [&](int t, auto bfc) __attribute__((always_inline)) {
+    constexpr int bf = decltype(bfc)::value;
     const bool is_cache = t < n_ct;
     const int base = is_cache ? t * kBKT : (t - n_ct) * kBKT;
     const int lim = is_cache ? M : S;
-#pragma unroll
-    for (int r = 0; r < NCH; ++r) {
-      const int c = r * 512 + tid, key = c / CPR, ch = c % CPR;
-      const int row = (key & ~31) | bkrow_of_key(key & 31);
-      store_u32x4(&Ks2[bf][row * D + 8 * bchunk<CPR>(row, ch)], fk[r]);
-      store_u32x4(&Vs2[bf][row * D + 8 * bchunk<CPR>(row, ch)], fv[r]);
-    }
     if (wave == 0) {
       const uint64_t m = __ballot(base + lane < lim && (!is_cache || f_pos >= 0));
       if (lane == 0) s_valid2[bf] = m;
     }
   };
-
-  // buffer bf is rewritten two tiles after it was read, behind the barrier
-  // of the tile in between
-  if (n_tiles > 0) fetch(0);
-  for (int t = 0; t < n_tiles; ++t) {
-    const int bf = t & 1;
-    commit(t, bf);
-    __syncthreads();
-    if (t + 1 < n_tiles) fetch(t + 1);
+  auto compute = [&](int t, auto bfc) __attribute__((always_inline)) {
+    constexpr int bf = decltype(bfc)::value;
     const bool is_cache = t < n_ct;
     const int base = is_cache ? t * kBKT : (t - n_ct) * kBKT;
-    const bf16_t* Ks = Ks2[bf];
-    const bf16_t* Vs = Vs2[bf];
-    if (!active || (!is_cache && base > qb * 32 + 31)) continue;
+    if (!active || (!is_cache && base > qb * 32 + 31)) return;
+    const char* ks = bf ? k_b1 : k_b0;
+    const char* vs = bf ? v_b1 : v_b0;
+    uint32_t ar = a_row, at = a_tr;
+    asm volatile("" : "+v"(ar), "+v"(at));       // per-step offsets stay in the loop
     const uint64_t vm = s_valid2[bf];
     const bool causal = !is_cache && (base + kBKT - 1 > qb * 32);
     const int lim_i = causal ? qi - base - 16 * hf : 1 << 30;
@@ -171,9 +186,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
       f32x16 sh = zero16(), ph = zero16();
 #pragma unroll
       for (int st = 0; st < DS; ++st) {
-        const int kr = 32 * kb + col;
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[kr * D + 8 * bchunk<CPR>(kr, 2 * st + hf)]);
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vs[kr * D + 8 * bchunk<CPR>(kr, 2 * st + hf)]);
+        const uint32_t o = (ar ^ (32 * st)) + 32 * kb * RB;
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + o);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vs + o);
         sh = mfma32x32x16(ka, qf[st], sh);
         ph = mfma32x32x16(va, dof[st], ph);
       }
@@ -185,23 +200,42 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
         const float pa = ok ? fast_exp2(fmaf(sh[r], c2, -lse2)) : 0.f;
         d8[r >> 3][r & 7] = ok ? pa * (ph[r] - Di) : 0.f;
       }
-      // dQ^T += K^T dS^T: MFMA u covers keys 32kb + 16(l/32) + 8u + e
+      // dQ^T += K^T dS^T: MFMA u covers keys 32kb + 16(l/32) + 8u + e, which
+      // sit in tile rows 32kb + 16u + 4(l/32) + {0..3} and those + 8
+      const uint32_t at1 = at ^ 32;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const bf16x8 ds = to_bf16x8(d8[u]);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int d = db * 32 + tr_dg * 16 + 4 * tr_q;
-          const int k0 = kb * 32 + 16 * hf + 8 * u;             // keys k0 .. k0+7
-          const int r0 = (k0 & ~31) | bkrow_of_key((k0 & 31) + tr_r);
-          const int r1 = (k0 & ~31) | bkrow_of_key((k0 & 31) + 4 + tr_r);
-          const bf16x4 h0 = lds_read_tr16(&Ks[r0 * D + 8 * bchunk<CPR>(r0, d >> 3) + (d & 7)]);
-          const bf16x4 h1 = lds_read_tr16(&Ks[r1 * D + 8 * bchunk<CPR>(r1, d >> 3) + (d & 7)]);
+          const uint32_t o0 = (at ^ (64 * db)) + (32 * kb + 16 * u) * RB;
+          const uint32_t o1 = (at1 ^ (64 * db)) + (32 * kb + 16 * u + 8) * RB;
+          const bf16x4 h0 = lds_read_tr16(reinterpret_cast<const bf16_t*>(ks + o0));
+          const bf16x4 h1 = lds_read_tr16(reinterpret_cast<const bf16_t*>(ks + o1));
           const bf16x8 a = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
           acc[db] = mfma32x32x16(a, ds, acc[db]);
         }
       }
     }
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  // a buffer is refilled one tile after it was read, behind that tile's barrier
+  if (n_tiles > 0) fetch(0, I0{});
+  int t = 0;
+  auto step = [&](auto bfc) __attribute__((always_inline)) {
+    using BN = std::integral_constant<int, decltype(bfc)::value ^ 1>;
+    if (t >= n_tiles) return false;
+    commit(t, bfc);
+    wait_vmem_all();                   // this wave's copies of tile t have landed
+    barrier_lds();                     // ... and every wave's
+    if (t + 1 < n_tiles) fetch(t + 1, BN{});
+    compute(t, bfc);
+    ++t;
+    return true;
+  };
+  while (step(I0{}) && step(I1{})) {
   }
   if (!qok) return;
   bf16_t* out = dQ + row_off;
