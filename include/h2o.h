@@ -113,10 +113,11 @@ H2O_API size_t h2o_workspace_bytes(const h2o_config* cfg);
  *   as they are) and tokens_seen must be 0.
  * adopt = 1: the buffers already hold a valid state after `tokens_seen`
  *   tokens (resume from a snapshot); nothing but the workspace is touched.
- *   The K/V rows of free slots (position < 0) must hold finite values (zeros,
- *   say): the attention reads them as part of whole tiles and gives them
- *   zero weight, which keeps NaN or Inf bit patterns in unused memory from
- *   reaching the output only if the values themselves are finite.
+ * In both cases the K/V rows of free slots (position < 0) must hold finite
+ *   values (zeros, say): the attention and its backward read them as part of
+ *   whole tiles and give them zero weight, which keeps NaN or Inf bit
+ *   patterns in unused memory from reaching any output only if the values
+ *   themselves are finite.
  * The workspace counters are cleared on `stream` in both cases.
  * Errors: H2O_ERR_NULL, H2O_ERR_CONFIG, H2O_ERR_WORKSPACE, H2O_ERR_STATE
  * (adopt = 0 with tokens_seen != 0, or tokens_seen < 0), H2O_ERR_HIP. */
@@ -162,8 +163,8 @@ H2O_API h2o_status h2o_get_scores(const h2o_cache* c, float* scores_out,
  * LHF Fig. 1(b) for one chunk): gradients of sum(out * d_out) with the
  * visible sets of the forward step (every slot with position >= 0, and chunk
  * keys j <= i) and the scores held constant.  Stateless: uses `cfg` only.
- * Inputs: q [B,Hq,s,d]; the PRE-step cache k_cache, v_cache [B,Hkv,M,d] and
- * positions [B,Hkv,M]; k_new, v_new [B,Hkv,s,d]; the forward's out
+ * Inputs: q [B,Hq,s,d]; the PRE-step cache k_cache, v_cache [B,Hkv,M,d]
+ * (free-slot rows finite, as for h2o_cache_init) and positions [B,Hkv,M]; k_new, v_new [B,Hkv,s,d]; the forward's out
  * [B,Hq,s,d] and lse [B,Hq,s]; d_out [B,Hq,s,d].
  * Outputs (every element written): dq [B,Hq,s,d]; dk_cache, dv_cache
  * [B,Hkv,M,d] (zero at free slots); dk_new, dv_new [B,Hkv,s,d]; all bf16.

@@ -7,13 +7,15 @@
 // The visible sets are those of the forward step: every filled slot of the
 // pre-step cache and the chunk's keys j <= i; the scores are not
 // differentiated.  With P = softmax(scale * q.key) over the visible keys:
-//   D_i = dO_i . O_i,  dP = dO V^T,  dS = P * (dP - D),
+//   dP = dO V^T,  D_i = sum_j P_ij dP_ij (= dO_i . O_i),  dS = P * (dP - D),
 //   dq = scale * dS K,  dK = scale * dS^T Q,  dV = P^T dO,
 // where dK and dV of a KV head sum over the G query heads of its group.
 //
-// Two kernels, both deterministic (no atomics):
+// Three kernels, all deterministic (no atomics):
 //   * bwd_dq_kernel: one wave per 32-query row block, 8 per workgroup (the forward's layout:
-//     S^T = K Q^T, lane = query), loops over the key tiles; also writes D.
+//     S^T = K Q^T, lane = query), loops over the key tiles.  Its dS uses
+//     D_i = dO_i . O_i from the stored output; it accumulates the exact
+//     sum_j P_ij dP_ij on the way and writes that D for the dK/dV kernel.
 //     K rows sit in LDS in MFMA-row order, which keeps every aligned group of
 //     4 keys in 4 consecutive rows, so the same tile serves the K rows of S^T
 //     (16-byte reads) and K^T of dQ^T = K^T dS^T (transpose reads).
@@ -21,7 +23,9 @@
 //     per 32 keys and row set; the two row sets split the query rows of the
 //     KV group (S = Q K^T, lane = key), accumulating dV^T += dO^T P and
 //     dK^T += Q^T dS with dO^T and Q^T from transpose reads of the staged
-//     row block, and fold their sums at the end.
+//     row block, and fold their sums at the end.  Chunk-key tiles split
+//     their query rows into pieces that write fp32 partials;
+//   * bwd_chunk_reduce_kernel sums those partials in piece order.
 #include <type_traits>
 
 #include "h2o_device.h"
@@ -105,9 +109,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     for (int e = 0; e < 8; ++e) dsum = fmaf(static_cast<float>(go[e]), static_cast<float>(o[e]), dsum);
   }
   dsum += xor32(dsum);
+  // D_i for dS here is dO_i . O_i with the stored (bf16) output, as it must be
+  // known before the keys are walked; the exact D_i = sum_j P_ij dP_ij is
+  // accumulated along the walk and written for the dK/dV kernel, where the
+  // output's rounding would otherwise be amplified wherever dP - D cancels
   const float Di = qok ? dsum : 0.f;
+  float dex[4] = {0.f, 0.f, 0.f, 0.f};
   const float lse2 = qok ? lse[static_cast<size_t>(b * Hq + hq) * S + qi] * kLog2e : __builtin_huge_valf();
-  if (qok && hf == 0) Dws[static_cast<size_t>(b * Hq + hq) * S + qi] = Di;
 
   f32x16 acc[DB];
 #pragma unroll
@@ -197,8 +205,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const bool ok = ((bits >> r) & 1u) && (32 * kb + r <= lim_i);
+        // masked keys: pa = 0 against a finite dP (free-slot rows are finite,
+        // rows past the end read as zeros), so both products are exactly 0
         const float pa = ok ? fast_exp2(fmaf(sh[r], c2, -lse2)) : 0.f;
-        d8[r >> 3][r & 7] = ok ? pa * (ph[r] - Di) : 0.f;
+        d8[r >> 3][r & 7] = pa * (ph[r] - Di);
+        dex[r & 3] = fmaf(pa, ph[r], dex[r & 3]);
       }
       // dQ^T += K^T dS^T: MFMA u covers keys 32kb + 16(l/32) + 8u + e, which
       // sit in tile rows 32kb + 16u + 4(l/32) + {0..3} and those + 8
@@ -237,6 +248,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   };
   while (step(I0{}) && step(I1{})) {
   }
+  float dx = (dex[0] + dex[1]) + (dex[2] + dex[3]);
+  dx += xor32(dx);
+  if (qok && hf == 0) Dws[static_cast<size_t>(b * Hq + hq) * S + qi] = dx;
   if (!qok) return;
   bf16_t* out = dQ + row_off;
 #pragma unroll

@@ -82,6 +82,12 @@ BWD_SMALL = {
                     total_len=256 + 160 * 4, cache_slots=384, recent_window=64, qk_std=1.0),
     "g1_d64": dict(batch=1, n_q_heads=3, n_kv_heads=3, head_dim=64, prefill=130, chunk=70,
                    total_len=130 + 70 * 5, cache_slots=260, recent_window=17, qk_std=1.0),
+    # 6 needed rows per chunk tile: some of the 4 row pieces are empty
+    "g2_tiny_chunk3": dict(batch=1, n_q_heads=4, n_kv_heads=2, head_dim=128, prefill=40, chunk=3,
+                           total_len=40 + 3 * 5, cache_slots=48, recent_window=4, qk_std=1.0),
+    # d = 64, three chunk tiles whose row pieces cross query-head boundaries
+    "g4_d64_three_tiles": dict(batch=1, n_q_heads=8, n_kv_heads=2, head_dim=64, prefill=256, chunk=300,
+                               total_len=256 + 300 * 4, cache_slots=640, recent_window=64, qk_std=1.0),
 }
 
 
