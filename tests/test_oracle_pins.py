@@ -392,3 +392,89 @@ def test_backward_matches_torch_autograd():
     np.testing.assert_allclose(grads[2], tV.grad.numpy(), atol=1e-12)
     np.testing.assert_allclose(grads[3], tk.grad.numpy(), atol=1e-12)
     np.testing.assert_allclose(grads[4], tv.grad.numpy(), atol=1e-12)
+
+
+# ---------------------------------------------------------------- gradient through the buffer
+# oracle/recurrence_grad.py differentiates the whole row with the eviction
+# decisions held fixed.  Pinned against: the step oracle's forward, the
+# single-step textbook gradient, plain causal attention when nothing is
+# evicted, and central differences with evictions.
+from oracle import recurrence_grad as rg  # noqa: E402
+
+
+def _row_case(seed, B, Hq, Hkv, d, lens, M, W):
+    rng = np.random.default_rng(seed)
+    chunks = _rand_chunks(rng, B, Hq, Hkv, d, lens)
+    scale = 1.0 / math.sqrt(d)
+    _, hist = orc.run_sequence(chunks, M, W=W, scale=scale, keep_history=True)
+    targets = [h["targets"] for h in hist]
+    d_outs = [rng.standard_normal(c[0].shape) for c in chunks]
+    return chunks, targets, d_outs, hist, scale
+
+
+def test_row_forward_matches_chunk_steps():
+    chunks, targets, _, hist, scale = _row_case(31, 2, 4, 2, 8, [8, 4, 4, 4, 4, 4], M=12, W=2)
+    assert any(len(e) for h in hist for per_b in h["evicted"] for e in per_b if e is not None)
+    t = lambda x: torch.from_numpy(np.asarray(x, dtype=np.float64))
+    outs = rg.row_forward([t(c[0]) for c in chunks], [t(c[1]) for c in chunks], [t(c[2]) for c in chunks],
+                          targets, 12, scale)
+    for c, o in enumerate(outs):
+        np.testing.assert_allclose(o.numpy(), hist[c]["out"], rtol=0, atol=1e-12, err_msg=f"chunk {c}")
+
+
+def test_row_grads_of_one_chunk_are_the_step_gradient():
+    chunks, targets, d_outs, _, scale = _row_case(32, 1, 4, 2, 8, [7], M=10, W=2)
+    (dq, dk, dv), = rg.row_grads(chunks, d_outs, targets, 10, scale)
+    K, V, _, pos = orc.empty_state(1, 2, 10, 8)
+    ref = orc.chunk_backward(K, V, pos, *chunks[0], d_outs[0], scale)
+    np.testing.assert_allclose(dq, ref[0], atol=1e-12)
+    np.testing.assert_allclose(dk, ref[3], atol=1e-12)
+    np.testing.assert_allclose(dv, ref[4], atol=1e-12)
+
+
+def test_row_grads_without_eviction_are_causal_attention_grads():
+    lens = [10, 5, 5, 4]
+    chunks, targets, d_outs, _, scale = _row_case(33, 1, 4, 2, 8, lens, M=32, W=3)
+    grads = rg.row_grads(chunks, d_outs, targets, 32, scale)
+    G = 2
+    q = torch.tensor(np.concatenate([c[0] for c in chunks], axis=2), requires_grad=True)
+    k = torch.tensor(np.concatenate([c[1] for c in chunks], axis=2), requires_grad=True)
+    v = torch.tensor(np.concatenate([c[2] for c in chunks], axis=2), requires_grad=True)
+    out = F.scaled_dot_product_attention(q, k.repeat_interleave(G, dim=1), v.repeat_interleave(G, dim=1),
+                                         is_causal=True, scale=scale)
+    (out * torch.from_numpy(np.concatenate(d_outs, axis=2))).sum().backward()
+    t0 = 0
+    for c, n in enumerate(lens):
+        for got, ref in zip(grads[c], (q.grad, k.grad, v.grad)):
+            np.testing.assert_allclose(got, ref.numpy()[:, :, t0:t0 + n], atol=1e-12, err_msg=f"chunk {c}")
+        t0 += n
+
+
+def test_row_grads_match_central_differences_with_evictions():
+    M = 9
+    chunks, targets, d_outs, hist, scale = _row_case(34, 1, 2, 1, 4, [6, 3, 3, 3], M=M, W=2)
+    assert any(len(e) for h in hist[1:] for per_b in h["evicted"] for e in per_b if e is not None)
+    grads = rg.row_grads(chunks, d_outs, targets, M, scale)
+
+    def loss(ch):
+        t = lambda x: torch.from_numpy(np.asarray(x, dtype=np.float64))
+        outs = rg.row_forward([t(c[0]) for c in ch], [t(c[1]) for c in ch], [t(c[2]) for c in ch],
+                              targets, M, scale)
+        return sum(float((o * t(g)).sum()) for o, g in zip(outs, d_outs))
+
+    rng = np.random.default_rng(35)
+    eps = 1e-6
+    work = [[np.array(x) for x in c] for c in chunks]
+    for c in range(len(chunks)):
+        for a in range(3):
+            x = work[c][a]
+            for _ in range(4):
+                idx = tuple(int(rng.integers(0, s)) for s in x.shape)
+                old = x[idx]
+                x[idx] = old + eps
+                lp = loss(work)
+                x[idx] = old - eps
+                lm = loss(work)
+                x[idx] = old
+                np.testing.assert_allclose(grads[c][a][idx], (lp - lm) / (2 * eps), rtol=1e-5, atol=1e-8,
+                                           err_msg=f"chunk {c} tensor {a} index {idx}")
