@@ -142,7 +142,10 @@ H2O_API h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k,
  *   step_mass [B,Hkv,M+s] fp32: the step's mass per cache slot (0 for slots
  *     that were free) followed by mu_j per chunk key;
  *   k_old, v_old [B,Hkv,s,d]: the rows the step overwrote (zeros where a
- *     free slot was filled) -- the buffer delta of LHF Fig. 1(c).
+ *     free slot was filled) -- the buffer delta of LHF Fig. 1(c);
+ *   pos_old [B,Hkv,s] int32: the position slot R_j held before the step (-1
+ *     where a free slot was filled).  slots_out, k_old/v_old and pos_old
+ *     together let h2o_recurrence_backward_step undo the step.
  * Errors: H2O_ERR_NULL; H2O_ERR_SHAPE unless 1 <= s <= max_chunk.
  * If a state adopted through h2o_cache_init has fewer evictable slots than
  * the step needs, no slot of that (b, head) is written (K/V and positions
@@ -151,7 +154,7 @@ H2O_API h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k,
 H2O_API h2o_status h2o_chunk_step(h2o_cache* c, const void* q, const void* k_new,
                           const void* v_new, int32_t s, void* out, float* lse,
                           int32_t* slots_out, float* step_mass, void* k_old,
-                          void* v_old, void* stream);
+                          void* v_old, int32_t* pos_old, void* stream);
 
 /* Enqueues device-to-device copies of the scores [B,Hkv,M] into scores_out
  * and, if positions_out != NULL, of the positions.  Errors: H2O_ERR_NULL,
@@ -186,6 +189,46 @@ H2O_API h2o_status h2o_chunk_backward(const h2o_config* cfg, const void* q,
 /* Host only: workspace bytes h2o_chunk_backward needs for chunk length s
  * (0 if the config is invalid or s < 1). */
 H2O_API size_t h2o_backward_workspace_bytes(const h2o_config* cfg, int32_t s);
+
+/* One step of the backward walk through the KV buffer over a row of chunks
+ * (LHF Fig. 1(b), with the buffer kept as the deltas of Fig. 1(c)): the
+ * cache after a step depends on every earlier chunk's keys and values, so a
+ * chunk token's key/value gradient collects the gradient of every later step
+ * that read the slot the token was written to, up to the step that
+ * overwrote it.  Call it for the steps in reverse order (last chunk first,
+ * the prefill last).  For step c it
+ *   1. undoes the step on the cache: rows slots[b,h,j] of k_cache/v_cache get
+ *      k_old/v_old[b,h,j] and their positions pos_old[b,h,j] (the delta that
+ *      h2o_chunk_step exported), leaving the cache as step c saw it;
+ *   2. runs the frozen-eviction backward of the step on that cache (as
+ *      h2o_chunk_backward): dq [B,Hq,s,d] (dtype) is the step's query
+ *      gradient, and the cache gradient dK_c, dV_c is kept in the workspace;
+ *   3. routes: for token j written to slot m = slots[b,h,j],
+ *      gk[b,h,j] = dk_new[b,h,j] + acc_k[b,h,m] (fp32 [B,Hkv,s,d]: the
+ *      token key's total gradient), then acc_k[b,h,m] = 0, and for every
+ *      slot acc_k += dK_c; the same for v.
+ * acc_k, acc_v: fp32 [B,Hkv,M,d], zero before the last step's call, carried
+ *   between the calls (each slot holds the gradient owed to its occupant).
+ * The prefill is undone as a step whose slots are 0..n-1 of every head,
+ *   pos_old = -1 and k_old = v_old = zeros.  Scores are neither read nor
+ *   changed.  q, k_new, v_new, out, lse, d_out: the step's forward inputs and
+ *   outputs and the output gradient, as for h2o_chunk_backward.
+ * A slot index outside [0, M) (a step that wrote nothing for that head) is
+ *   skipped by the undo and the routing.
+ * workspace >= h2o_recurrence_workspace_bytes(cfg, s).  Deterministic.
+ * Errors: H2O_ERR_NULL, H2O_ERR_CONFIG, H2O_ERR_UNSUPPORTED (fp32 configs),
+ * H2O_ERR_SHAPE (s < 1 or s larger than max(max_chunk, max_prefill)),
+ * H2O_ERR_WORKSPACE, H2O_ERR_HIP. */
+H2O_API h2o_status h2o_recurrence_backward_step(
+    const h2o_config* cfg, void* k_cache, void* v_cache, int32_t* positions,
+    const int32_t* slots, const void* k_old, const void* v_old, const int32_t* pos_old,
+    const void* q, const void* k_new, const void* v_new, int32_t s, const void* out,
+    const float* lse, const void* d_out, float* acc_k, float* acc_v, void* dq, float* gk,
+    float* gv, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host only: workspace bytes h2o_recurrence_backward_step needs for step
+ * length s (0 if the config is invalid or s < 1). */
+H2O_API size_t h2o_recurrence_workspace_bytes(const h2o_config* cfg, int32_t s);
 
 /* Tokens seen so far (T). */
 H2O_API int64_t h2o_tokens_seen(const h2o_cache* c);

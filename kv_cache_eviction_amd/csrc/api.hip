@@ -129,7 +129,7 @@ h2o::StepShape shape_of(const h2o_cache* c, int s) {
 }
 
 h2o_status run_step(h2o_cache* c, const void* q, const void* k, const void* v, int32_t s, void* out,
-                    float* lse, int32_t* slots_out, float* step_mass, void* k_old, void* v_old,
+                    float* lse, int32_t* slots_out, int32_t* pos_old, float* step_mass, void* k_old, void* v_old,
                     hipStream_t st) {
   const h2o::StepShape sh = shape_of(c, s);
   float* lse_buf = lse ? lse : reinterpret_cast<float*>(c->ws + c->lay.lse_off);
@@ -146,7 +146,7 @@ h2o_status run_step(h2o_cache* c, const void* q, const void* k, const void* v, i
   if (r != H2O_OK) return r;
   int32_t* targets = reinterpret_cast<int32_t*>(c->ws + c->lay.targets_off);
   h2o::SelectArgs xa{c->k_cache, c->v_cache, c->scores, c->pos, k, v, partial, R, targets,
-                     slots_out, step_mass, k_old, v_old, status, static_cast<int32_t>(c->T)};
+                     slots_out, pos_old, step_mass, k_old, v_old, status, static_cast<int32_t>(c->T)};
   r = timed(c, 2, st, [&] { return h2o::launch_select(sh, xa, st); });
   if (r != H2O_OK) return r;
   r = timed(c, 4, st, [&] { return h2o::launch_scatter(sh, xa, dtype, st); });
@@ -154,6 +154,38 @@ h2o_status run_step(h2o_cache* c, const void* q, const void* k, const void* v, i
   c->T += s;
   if (c->filled >= 0) c->filled = c->filled + s > c->cfg.cache_slots ? c->cfg.cache_slots : c->filled + s;
   return H2O_OK;
+}
+
+h2o::StepShape backward_shape(const h2o_config* cfg, int32_t s) {
+  h2o::StepShape sh;
+  sh.B = cfg->batch;
+  sh.Hq = cfg->n_q_heads;
+  sh.Hkv = cfg->n_kv_heads;
+  sh.D = cfg->head_dim;
+  sh.S = s;
+  sh.M = cfg->cache_slots;
+  sh.W = cfg->recent_window;
+  sh.n_cache = cfg->cache_slots;
+  sh.scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / sqrtf(static_cast<float>(cfg->head_dim));
+  return sh;
+}
+
+// recurrence step workspace: the backward's, then its bf16 outputs dK/dV of
+// the cache and dk/dv of the chunk
+struct RecLayout {
+  size_t bwd, dkc, dvc, dkn, dvn, total;
+};
+RecLayout rec_layout(const h2o_config* cfg, int32_t s) {
+  const size_t cache_rows = static_cast<size_t>(cfg->batch) * cfg->n_kv_heads * cfg->cache_slots * cfg->head_dim * 2;
+  const size_t new_rows = static_cast<size_t>(cfg->batch) * cfg->n_kv_heads * s * cfg->head_dim * 2;
+  RecLayout l;
+  l.bwd = 0;
+  l.dkc = align_up(h2o::backward_workspace_bytes(cfg->batch, cfg->n_q_heads, cfg->n_kv_heads, s, cfg->head_dim));
+  l.dvc = l.dkc + align_up(cache_rows);
+  l.dkn = l.dvc + align_up(cache_rows);
+  l.dvn = l.dkn + align_up(new_rows);
+  l.total = l.dvn + align_up(new_rows);
+  return l;
 }
 
 }  // namespace
@@ -247,18 +279,18 @@ h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k, const void* v
   if (!c || !q || !k || !v || !out) return H2O_ERR_NULL;
   if (n < 1 || n > c->cfg.max_prefill) return H2O_ERR_SHAPE;
   if (c->T != 0) return H2O_ERR_STATE;
-  return run_step(c, q, k, v, n, out, lse, nullptr, nullptr, nullptr, nullptr,
+  return run_step(c, q, k, v, n, out, lse, nullptr, nullptr, nullptr, nullptr, nullptr,
                   static_cast<hipStream_t>(stream));
 }
 
 h2o_status h2o_chunk_step(h2o_cache* c, const void* q, const void* k_new, const void* v_new, int32_t s,
                           void* out, float* lse, int32_t* slots_out, float* step_mass, void* k_old,
-                          void* v_old, void* stream) {
+                          void* v_old, int32_t* pos_old, void* stream) {
   if (!c || !q || !k_new || !v_new || !out) return H2O_ERR_NULL;
   if ((k_old == nullptr) != (v_old == nullptr)) return H2O_ERR_NULL;
   if (s < 1 || s > c->cfg.max_chunk) return H2O_ERR_SHAPE;
   if (c->T + s > INT32_MAX) return H2O_ERR_STATE;
-  return run_step(c, q, k_new, v_new, s, out, lse, slots_out, step_mass, k_old, v_old,
+  return run_step(c, q, k_new, v_new, s, out, lse, slots_out, pos_old, step_mass, k_old, v_old,
                   static_cast<hipStream_t>(stream));
 }
 
@@ -359,19 +391,46 @@ h2o_status h2o_chunk_backward(const h2o_config* cfg, const void* q, const void* 
   if (s < 1 || s > max_len(cfg)) return H2O_ERR_SHAPE;
   if (workspace_bytes < h2o::backward_workspace_bytes(cfg->batch, cfg->n_q_heads, cfg->n_kv_heads, s, cfg->head_dim))
     return H2O_ERR_WORKSPACE;
-  h2o::StepShape sh;
-  sh.B = cfg->batch;
-  sh.Hq = cfg->n_q_heads;
-  sh.Hkv = cfg->n_kv_heads;
-  sh.D = cfg->head_dim;
-  sh.S = s;
-  sh.M = cfg->cache_slots;
-  sh.W = cfg->recent_window;
-  sh.n_cache = cfg->cache_slots;
-  sh.scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / sqrtf(static_cast<float>(cfg->head_dim));
+  const h2o::StepShape sh = backward_shape(cfg, s);
   h2o::BackwardArgs a{q, k_cache, v_cache, positions, k_new, v_new, out, lse, d_out,
                       dq, dk_cache, dv_cache, dk_new, dv_new, workspace};
   const hipError_t e = h2o::launch_backward(sh, a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? H2O_OK : H2O_ERR_HIP;
+}
+
+size_t h2o_recurrence_workspace_bytes(const h2o_config* cfg, int32_t s) {
+  if (h2o_validate_config(cfg) != H2O_OK || s < 1) return 0;
+  return rec_layout(cfg, s).total;
+}
+
+h2o_status h2o_recurrence_backward_step(const h2o_config* cfg, void* k_cache, void* v_cache,
+                                        int32_t* positions, const int32_t* slots, const void* k_old,
+                                        const void* v_old, const int32_t* pos_old, const void* q,
+                                        const void* k_new, const void* v_new, int32_t s, const void* out,
+                                        const float* lse, const void* d_out, float* acc_k, float* acc_v,
+                                        void* dq, float* gk, float* gv, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  if (!cfg || !k_cache || !v_cache || !positions || !slots || !k_old || !v_old || !pos_old || !q ||
+      !k_new || !v_new || !out || !lse || !d_out || !acc_k || !acc_v || !dq || !gk || !gv || !workspace)
+    return H2O_ERR_NULL;
+  h2o_status r = h2o_validate_config(cfg);
+  if (r != H2O_OK) return r;
+  if (cfg->dtype != H2O_BF16) return H2O_ERR_UNSUPPORTED;
+  if (s < 1 || s > max_len(cfg)) return H2O_ERR_SHAPE;
+  const RecLayout l = rec_layout(cfg, s);
+  if (workspace_bytes < l.total) return H2O_ERR_WORKSPACE;
+  const h2o::StepShape sh = backward_shape(cfg, s);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  h2o::RecurrenceArgs ra{k_cache, v_cache, positions, slots, k_old, v_old, pos_old,
+                         ws + l.dkc, ws + l.dvc, ws + l.dkn, ws + l.dvn, acc_k, acc_v, gk, gv};
+  hipError_t e = h2o::launch_undo_step(sh, ra, cfg->dtype, st);
+  if (e != hipSuccess) return H2O_ERR_HIP;
+  h2o::BackwardArgs a{q, k_cache, v_cache, positions, k_new, v_new, out, lse, d_out,
+                      dq, ws + l.dkc, ws + l.dvc, ws + l.dkn, ws + l.dvn, ws + l.bwd};
+  e = h2o::launch_backward(sh, a, st);
+  if (e != hipSuccess) return H2O_ERR_HIP;
+  e = h2o::launch_route(sh, ra, st);
   return e == hipSuccess ? H2O_OK : H2O_ERR_HIP;
 }
 

@@ -45,6 +45,7 @@ struct SelectArgs {
   int R;
   int32_t* targets;     // [B*Hkv][S] workspace: target slot of row j (flagged if it was free)
   int32_t* slots_out;   // nullable
+  int32_t* pos_old;     // nullable: positions the written slots held before the step
   float* step_mass;     // nullable
   void* k_old;          // nullable
   void* v_old;          // nullable
@@ -70,6 +71,25 @@ struct BackwardArgs {
   void* workspace;         // >= backward_workspace_bytes: D_i = dO_i . O_i, partial dK/dV
 };
 
+// One step of the backward walk through the buffer (recurrence.hip).
+struct RecurrenceArgs {
+  void* k_cache;          // post-step cache in, pre-step cache out
+  void* v_cache;
+  int32_t* pos;
+  const int32_t* slots;   // [B*Hkv][S] the step's delta
+  const void* k_old;
+  const void* v_old;
+  const int32_t* pos_old;
+  const void* dk_cache;   // the step's backward outputs (bf16)
+  const void* dv_cache;
+  const void* dk_new;
+  const void* dv_new;
+  float* acc_k;           // [B*Hkv][M][d] carried across the walk
+  float* acc_v;
+  float* gk;              // [B*Hkv][S][d] total gradients of the step's tokens
+  float* gv;
+};
+
 enum Dtype { kBF16 = 0, kFP32 = 1 };
 
 hipError_t launch_attn_fwd(const StepShape& sh, const AttnArgs& a, int dtype, hipStream_t st);
@@ -78,6 +98,8 @@ hipError_t launch_select(const StepShape& sh, const SelectArgs& a, hipStream_t s
 hipError_t launch_scatter(const StepShape& sh, const SelectArgs& a, int dtype, hipStream_t st);
 hipError_t launch_backward(const StepShape& sh, const BackwardArgs& a, hipStream_t st);
 size_t backward_workspace_bytes(int B, int Hq, int Hkv, int S, int D);
+hipError_t launch_undo_step(const StepShape& sh, const RecurrenceArgs& a, int dtype, hipStream_t st);
+hipError_t launch_route(const StepShape& sh, const RecurrenceArgs& a, hipStream_t st);
 hipError_t launch_reset(float* scores, int32_t* pos, int64_t n_slots, int32_t* counters,
                         int64_t n_counters, hipStream_t st);
 

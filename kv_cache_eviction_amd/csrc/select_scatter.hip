@@ -109,7 +109,7 @@ template <int SPT>
 __global__ __launch_bounds__(kThreads) void select_kernel(
     float* __restrict__ scores, int32_t* __restrict__ pos, const float* __restrict__ partial,
     int R, int32_t* __restrict__ targets, int32_t* __restrict__ slots_out,
-    float* __restrict__ step_mass, int32_t* __restrict__ status, int T, int W, int S, int M,
+    int32_t* __restrict__ pos_old, float* __restrict__ step_mass, int32_t* __restrict__ status, int T, int W, int S, int M,
     int n_cache, int vec) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   int* s_R = reinterpret_cast<int*>(smem);                 // [S]: target of chunk row j (flagged)
@@ -348,6 +348,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     const int v = s_R[jj];
     const int slot = v & ~kWasFree;
     sc_h[slot] = mu;
+    if (pos_old) pos_old[static_cast<size_t>(bh) * S + jj] = pos_h[slot];
     pos_h[slot] = T + jj;
     targets[static_cast<size_t>(bh) * S + jj] = v;
     if (slots_out) slots_out[static_cast<size_t>(bh) * S + jj] = slot;
@@ -433,7 +434,7 @@ hipError_t launch_select(const StepShape& sh, const SelectArgs& a, hipStream_t s
       if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3(n_heads), dim3(kThreads), lds, st, a.scores, a.pos, a.partial, a.R,
-                       a.targets, a.slots_out, a.step_mass, a.status, a.T, sh.W, sh.S, sh.M, sh.n_cache,
+                       a.targets, a.slots_out, a.pos_old, a.step_mass, a.status, a.T, sh.W, sh.S, sh.M, sh.n_cache,
                        vec ? 1 : 0);
     return hipGetLastError();
   };

@@ -29,6 +29,7 @@ KERNEL_IDS = {"attn_fwd": 0, "score": 1, "select": 2, "reset": 3, "scatter": 4}
 EXPORTED = [
     "h2o_validate_config", "h2o_workspace_bytes", "h2o_cache_init", "h2o_prefill",
     "h2o_chunk_step", "h2o_get_scores", "h2o_chunk_backward", "h2o_backward_workspace_bytes",
+    "h2o_recurrence_backward_step", "h2o_recurrence_workspace_bytes",
     "h2o_tokens_seen", "h2o_device_status", "h2o_set_timing", "h2o_get_timing",
     "h2o_cache_destroy", "h2o_status_str", "h2o_last_hip_error",
 ]
@@ -60,10 +61,13 @@ def _load():
         "h2o_workspace_bytes": (SZ, [cfgp]),
         "h2o_cache_init": (I32, [cfgp, P, P, P, P, P, SZ, I32, I64, P, ctypes.POINTER(P)]),
         "h2o_prefill": (I32, [P, P, P, P, I32, P, P, P]),
-        "h2o_chunk_step": (I32, [P, P, P, P, I32, P, P, P, P, P, P, P]),
+        "h2o_chunk_step": (I32, [P, P, P, P, I32, P, P, P, P, P, P, P, P]),
         "h2o_get_scores": (I32, [P, P, P, P]),
         "h2o_chunk_backward": (I32, [cfgp, P, P, P, P, P, P, I32, P, P, P, P, P, P, P, P, P, SZ, P]),
         "h2o_backward_workspace_bytes": (SZ, [cfgp, I32]),
+        "h2o_recurrence_backward_step": (I32, [cfgp, P, P, P, P, P, P, P, P, P, P, I32, P, P, P, P, P, P, P,
+                                               P, P, SZ, P]),
+        "h2o_recurrence_workspace_bytes": (SZ, [cfgp, I32]),
         "h2o_tokens_seen": (I64, [P]),
         "h2o_device_status": (I32, [P, P, ctypes.POINTER(I32)]),
         "h2o_set_timing": (I32, [P, I32]),
@@ -189,7 +193,7 @@ def h2o_prefill(handle, cfg: H2OConfig, q, k, v, out, lse=None, stream=None):
 
 
 def h2o_chunk_step(handle, cfg: H2OConfig, q, k_new, v_new, out, lse=None, slots_out=None,
-                   step_mass=None, k_old=None, v_old=None, stream=None):
+                   step_mass=None, k_old=None, v_old=None, pos_old=None, stream=None):
     B, Hq, Hkv, d, M = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.cache_slots
     s = q.shape[2]
     _expect(q, "q", (B, Hq, s, d), cfg.torch_dtype)
@@ -201,9 +205,10 @@ def h2o_chunk_step(handle, cfg: H2OConfig, q, k_new, v_new, out, lse=None, slots
     _expect(step_mass, "step_mass", (B, Hkv, M + s), torch.float32, allow_none=True)
     _expect(k_old, "k_old", (B, Hkv, s, d), cfg.torch_dtype, allow_none=True)
     _expect(v_old, "v_old", (B, Hkv, s, d), cfg.torch_dtype, allow_none=True)
+    _expect(pos_old, "pos_old", (B, Hkv, s), torch.int32, allow_none=True)
     _check(_lib.h2o_chunk_step(handle, _ptr(q), _ptr(k_new), _ptr(v_new), s, _ptr(out), _ptr(lse),
                                _ptr(slots_out), _ptr(step_mass), _ptr(k_old), _ptr(v_old),
-                               _stream(stream)), "h2o_chunk_step")
+                               _ptr(pos_old), _stream(stream)), "h2o_chunk_step")
 
 
 def h2o_get_scores(handle, scores_out, positions_out=None, stream=None):
@@ -231,6 +236,36 @@ def h2o_chunk_backward(cfg: H2OConfig, q, k_cache, v_cache, positions, k_new, v_
                                    _ptr(k_new), _ptr(v_new), s, _ptr(out), _ptr(lse), _ptr(d_out), _ptr(dq),
                                    _ptr(dk_cache), _ptr(dv_cache), _ptr(dk_new), _ptr(dv_new),
                                    _ptr(workspace), ws_bytes, _stream(stream)), "h2o_chunk_backward")
+
+
+def h2o_recurrence_workspace_bytes(cfg: H2OConfig, s: int) -> int:
+    c = cfg.c()
+    return _lib.h2o_recurrence_workspace_bytes(ctypes.byref(c), s)
+
+
+def h2o_recurrence_backward_step(cfg: H2OConfig, k_cache, v_cache, positions, slots, k_old, v_old,
+                                 pos_old, q, k_new, v_new, out, lse, d_out, acc_k, acc_v, dq, gk, gv,
+                                 workspace, stream=None):
+    B, Hq, Hkv, d, M = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.cache_slots
+    s = q.shape[2]
+    dt, f32, i32 = cfg.torch_dtype, torch.float32, torch.int32
+    for t, name, shp, ty in [
+        (k_cache, "k_cache", (B, Hkv, M, d), dt), (v_cache, "v_cache", (B, Hkv, M, d), dt),
+        (positions, "positions", (B, Hkv, M), i32), (slots, "slots", (B, Hkv, s), i32),
+        (k_old, "k_old", (B, Hkv, s, d), dt), (v_old, "v_old", (B, Hkv, s, d), dt),
+        (pos_old, "pos_old", (B, Hkv, s), i32), (q, "q", (B, Hq, s, d), dt),
+        (k_new, "k_new", (B, Hkv, s, d), dt), (v_new, "v_new", (B, Hkv, s, d), dt),
+        (out, "out", (B, Hq, s, d), dt), (lse, "lse", (B, Hq, s), f32), (d_out, "d_out", (B, Hq, s, d), dt),
+        (acc_k, "acc_k", (B, Hkv, M, d), f32), (acc_v, "acc_v", (B, Hkv, M, d), f32),
+        (dq, "dq", (B, Hq, s, d), dt), (gk, "gk", (B, Hkv, s, d), f32), (gv, "gv", (B, Hkv, s, d), f32)]:
+        _expect(t, name, shp, ty)
+    c = cfg.c()
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    _check(_lib.h2o_recurrence_backward_step(
+        ctypes.byref(c), _ptr(k_cache), _ptr(v_cache), _ptr(positions), _ptr(slots), _ptr(k_old),
+        _ptr(v_old), _ptr(pos_old), _ptr(q), _ptr(k_new), _ptr(v_new), s, _ptr(out), _ptr(lse), _ptr(d_out),
+        _ptr(acc_k), _ptr(acc_v), _ptr(dq), _ptr(gk), _ptr(gv), _ptr(workspace), ws_bytes,
+        _stream(stream)), "h2o_recurrence_backward_step")
 
 
 def h2o_tokens_seen(handle) -> int:
@@ -300,11 +335,11 @@ class H2OCache:
         return out
 
     def chunk_step(self, q, k_new, v_new, out=None, lse=None, slots_out=None, step_mass=None,
-                   k_old=None, v_old=None, stream=None):
+                   k_old=None, v_old=None, pos_old=None, stream=None):
         if out is None:
             out = torch.empty_like(q)
         h2o_chunk_step(self.handle, self.cfg, q, k_new, v_new, out, lse, slots_out, step_mass,
-                       k_old, v_old, stream)
+                       k_old, v_old, pos_old, stream)
         return out
 
     def get_scores(self, stream=None):

@@ -88,6 +88,7 @@ def test_null_handle_calls_fail_cleanly():
     h2o = _lib_module()
     assert h2o._lib.h2o_prefill(None, None, None, None, 4, None, None, None) == h2o.H2O_ERR_NULL
     assert h2o._lib.h2o_chunk_step(None, None, None, None, 4, None, None, None, None, None, None,
-                                   None) == h2o.H2O_ERR_NULL
+                                   None, None) == h2o.H2O_ERR_NULL
+    assert h2o._lib.h2o_recurrence_backward_step(*([None] * 11), 4, *([None] * 9), 0, None) == h2o.H2O_ERR_NULL
     assert h2o._lib.h2o_tokens_seen(None) == -1
     assert h2o._lib.h2o_last_hip_error(None) == 0

@@ -261,7 +261,8 @@ def test_error_paths_leave_state_unchanged():
     with pytest.raises(h2o.H2OError) as e:
         cache.chunk_step(big, bigkv, bigkv)      # s > max_chunk
     assert e.value.status == h2o.H2O_ERR_SHAPE
-    rc = h2o._lib.h2o_chunk_step(cache.handle, None, None, None, 4, None, None, None, None, None, None, None)
+    rc = h2o._lib.h2o_chunk_step(cache.handle, None, None, None, 4, None, None, None, None, None, None, None,
+                                 None)
     assert rc == h2o.H2O_ERR_NULL
     assert cache.tokens_seen == w.prefill
     cache.chunk_step(q1, k1, v1)
