@@ -14,7 +14,13 @@ kernel (attention forward: bf16 MFMA, or HBM for the decode workload) from
 HIP events recorded by the library on the launch stream, and the fp64 CPU
 oracle timed on a bounded sample of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+With --recurrence (workloads with a backward): one step = the forward over
+the whole row with every chunk step's buffer delta recorded, then the
+backward walk through the buffer (h2o_recurrence_backward_step, last chunk
+first, the prefill last), which gives every chunk's q/k/v their total
+gradients.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--recurrence]
        python bench.py --copy-probe MB    (plain copy of known size, for
                                            scaling the HBM byte counters)
 """
@@ -52,7 +58,7 @@ def visible_pairs(w, c, T):
     return n * mv + n * (n + 1) // 2
 
 
-def algorithmic_flops(w, backward=False):
+def algorithmic_flops(w, backward=False, prefill_backward=False):
     """Attention flops of a whole sequence, per launch: list of (kind, flops)."""
     d, B, Hq = w.head_dim, w.batch, w.n_q_heads
     out = []
@@ -60,7 +66,7 @@ def algorithmic_flops(w, backward=False):
     for c in range(w.n_chunks):
         v = visible_pairs(w, c, T)
         out.append(("prefill" if c == 0 else "chunk", 4.0 * B * Hq * d * v))
-        if backward and c > 0:
+        if backward and (c > 0 or prefill_backward):
             out.append(("backward", 10.0 * B * Hq * d * v))
         T += w.chunk_bounds(c)[1]
     return out
@@ -153,6 +159,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB")
+    ap.add_argument("--recurrence", action="store_true",
+                    help="forward over the row, then the backward walk through the buffer")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the H2O step shards by batch or KV head with no "
@@ -169,6 +177,10 @@ def main():
     w = wl.workload(args.workload)
     hbm = w.name in HBM_BOUND
     backward = w.backward
+    rec = args.recurrence
+    if rec and not backward:
+        print(f"--recurrence needs a workload with a backward (not {w.name})", file=sys.stderr)
+        sys.exit(2)
     cfg = h2o.H2OConfig(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.cache_slots,
                         w.recent_window, w.chunk, w.prefill, w.dtype)
     dev = torch.device("cuda:0")
@@ -193,7 +205,28 @@ def main():
     positions = torch.empty((B, Hkv, M), dtype=torch.int32, device=dev)
     workspace = torch.empty(h2o.h2o_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    if backward:
+    if rec:
+        # every step's buffer delta (the prefill's: slots 0..n-1 of empty
+        # rows), the walk's carried fp32 slot gradients and its outputs
+        n0 = chunks[0][0].shape[2]
+        deltas = [(torch.arange(n0, dtype=torch.int32, device=dev).expand(B, Hkv, n0).contiguous(),
+                   torch.zeros_like(chunks[0][1]), torch.zeros_like(chunks[0][2]),
+                   torch.full((B, Hkv, n0), -1, dtype=torch.int32, device=dev))]
+        for c in range(1, w.n_chunks):
+            _, k, v = chunks[c]
+            deltas.append((torch.empty(k.shape[:3], dtype=torch.int32, device=dev), torch.empty_like(k),
+                           torch.empty_like(v), torch.empty(k.shape[:3], dtype=torch.int32, device=dev)))
+        d_outs = [up(wl.chunk_grad_out(w, args.seed, c)) for c in range(w.n_chunks)]
+        acc_k = torch.zeros((B, Hkv, M, d), dtype=torch.float32, device=dev)
+        acc_v = torch.zeros_like(acc_k)
+        rgrads = {}
+        for c in (0, 1):
+            q, k, _ = chunks[c]
+            rgrads[q.shape[2]] = (torch.empty_like(q), torch.empty(k.shape, dtype=torch.float32, device=dev),
+                                  torch.empty(k.shape, dtype=torch.float32, device=dev))
+        rws = torch.empty(h2o.h2o_recurrence_workspace_bytes(cfg, max(w.prefill, w.chunk)), dtype=torch.uint8,
+                          device=dev)
+    elif backward:
         # the backward needs the pre-step cache: copied before each step (part of the job)
         k_pre, v_pre, pos_pre = torch.empty_like(k_cache), torch.empty_like(v_cache), torch.empty_like(positions)
         d_outs = [up(wl.chunk_grad_out(w, args.seed, c)) if c > 0 else None for c in range(w.n_chunks)]
@@ -216,6 +249,11 @@ def main():
             marks[0].record(stream)
         for c in range(1, w.n_chunks):
             q, k, v = chunks[c]
+            if rec:
+                sl, ko, vo, po = deltas[c]
+                h2o.h2o_chunk_step(handle, cfg, q, k, v, outs[c], lses[c], slots_out=sl, k_old=ko, v_old=vo,
+                                   pos_old=po, stream=stream)
+                continue
             if backward:
                 k_pre.copy_(k_cache)
                 v_pre.copy_(v_cache)
@@ -227,6 +265,23 @@ def main():
                     e0.record(stream)
                 h2o.h2o_chunk_backward(cfg, q, k_pre, v_pre, pos_pre, k, v, outs[c], lses[c], d_outs[c],
                                        *grads, bws, stream)
+                if bwd_timing:
+                    e1.record(stream)
+                    bwd_marks.append((e0, e1))
+        if rec:
+            # the walk: last chunk first; the cache ends as the pass found it
+            acc_k.zero_()
+            acc_v.zero_()
+            for c in reversed(range(w.n_chunks)):
+                q, k, v = chunks[c]
+                sl, ko, vo, po = deltas[c]
+                dq, gk, gv = rgrads[q.shape[2]]
+                if bwd_timing:
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                h2o.h2o_recurrence_backward_step(cfg, k_cache, v_cache, positions, sl, ko, vo, po, q, k, v,
+                                                 outs[c], lses[c], d_outs[c], acc_k, acc_v, dq, gk, gv, rws,
+                                                 stream)
                 if bwd_timing:
                     e1.record(stream)
                     bwd_marks.append((e0, e1))
@@ -268,7 +323,7 @@ def main():
     if backward:
         step_ms["backward"] = sum(a.elapsed_time(b) for a, b in bwd_marks)
 
-    fl = algorithmic_flops(w, backward)
+    fl = algorithmic_flops(w, backward, prefill_backward=rec)
     attn_fl = [f for kind, f in fl if kind != "backward"]
     attn_avg_ms = attn_ms / max(attn_n, 1)
     if hbm:
@@ -303,7 +358,10 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": recorded_traffic("attn_fwd_bf16_kernel", w.name),
                 "avg_launch_us": round(attn_avg_ms * 1e3, 3), "algorithmic_flops_per_launch": round(per_launch)}
         metric = "H2O chunk-step TFLOP/s + tokens/s at 64k ctx, 8B-GQA shape; % of roofline"
-        if w.name != "llama8b_64k":
+        if rec:
+            metric = ("H2O row TFLOP/s + tokens/s at %dk ctx, G=%d d=%d: forward, then the backward walk "
+                      "through the KV buffer; %% of roofline" % (w.total_len // 1024, w.group, w.head_dim))
+        elif w.name != "llama8b_64k":
             metric = "H2O chunk-step TFLOP/s + tokens/s at %dk ctx, G=%d d=%d%s; %% of roofline" % (
                 w.total_len // 1024, w.group, w.head_dim, ", with the backward" if backward else "")
         unit = "TFLOP/s"
@@ -332,13 +390,21 @@ def main():
             "workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
             "head_dim": w.head_dim, "prefill": w.prefill, "chunk": w.chunk, "total_len": w.total_len,
             "cache_slots": w.cache_slots, "recent_window": w.recent_window,
-            "step": "%s + %d chunk steps%s" % (
+            "step": ("cache reset + prefill + %d chunk steps recording their buffer deltas, then the "
+                     "backward walk over all %d steps (last first)" % (w.n_steps, w.n_chunks)) if rec else
+                    "%s + %d chunk steps%s" % (
                 "untimed cache reset + prefill" if hbm else "cache reset + prefill", w.n_steps,
                 ", each followed by the frozen-eviction backward" if backward else ""),
         },
         "tflops": round(tflops, 3),
         "tokens_per_s": round(tokens_per_s, 1),
         "roofline": roof,
+        **({"backward_executed": {
+            "kernels": "bwd_dq + bwd_dkdv + chunk reduce" + (" + undo + route" if rec else ""),
+            "ms_per_step": round(step_ms["backward"], 3),
+            "tflops": round(sum(1.4 * f for kind, f in fl if kind == "backward") / (step_ms["backward"] * 1e-3) / 1e12, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s (14 d flops executed per visible pair and query head)"}}
+           if backward else {}),
         "kernel_ms_per_step": {k: round(v, 4) for k, v in step_ms.items()},
         "cpu_baseline": cpu,
     }
