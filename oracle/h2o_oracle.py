@@ -39,6 +39,13 @@ Readings where the pages are silent (each is listed in the design notes):
   the number of tokens seen before the chunk;
 * victims: the n_e smallest candidates ordered by (score, slot index);
 * the chunk's token j goes to the j-th smallest target slot;
+* the position policies "recent" and "sink_recent" (the pages' lr and slr
+  rows among their five KV cache policies, Tables 1 and 6; sinks after the
+  attention-sinks paper in their reference list) rank the candidates by
+  (position, slot) instead of (score, slot), so the oldest tokens go;
+  "sink_recent" also protects positions below n_sink (a config value: the
+  pages give no number).  They keep no score: the step adds no mass and a
+  written slot's score is 0;
 * softmax scale 1/sqrt(d) unless given, natural-log logsumexp, query head h
   uses KV head h // G; Q and K arrive with any positional encoding applied.
 
@@ -53,9 +60,11 @@ import math
 import numpy as np
 
 __all__ = [
-    "empty_state", "attend_head", "select_targets", "chunk_step", "prefill",
+    "POLICIES", "empty_state", "attend_head", "select_targets", "chunk_step", "prefill",
     "chunk_backward", "run_sequence",
 ]
+
+POLICIES = ("h2o", "recent", "sink_recent")
 
 
 def empty_state(B: int, Hkv: int, M: int, d: int):
@@ -114,12 +123,14 @@ def attend_head(Kc, Vc, pos, q, k_new, v_new, scale):
     return out, lse, delta_sigma, mass[nv:]
 
 
-def select_targets(sigma, pos, T: int, W: int, S: int):
+def select_targets(sigma, pos, T: int, W: int, S: int, policy: str = "h2o", n_sink: int = 0):
     """Slots a chunk of S tokens is written to (LHF §1 ¶1; H2O [72]).
 
     Free slots are used first (ascending); the remaining n_e = S - n_free
     targets are the n_e candidates with the smallest (score, slot), where a
     candidate is a filled slot outside the recent window (pos < T - W).
+    Position policies rank by (position, slot) instead; "sink_recent" also
+    excludes positions below n_sink from the candidates.
 
     Returns ``(targets, evicted, cut_gap)``: ``targets`` ascending (token j
     goes to ``targets[j]``), ``evicted`` in selection order, and the score
@@ -129,21 +140,26 @@ def select_targets(sigma, pos, T: int, W: int, S: int):
     free = np.flatnonzero(pos < 0)
     n_free = min(S, free.size)
     n_e = S - n_free
-    cand = np.flatnonzero((pos >= 0) & (pos < T - W))
+    if policy not in POLICIES:
+        raise ValueError(f"unknown policy {policy}")
+    floor = n_sink if policy == "sink_recent" else 0
+    cand = np.flatnonzero((pos >= floor) & (pos < T - W))
     if cand.size < n_e:
         raise ValueError(f"only {cand.size} evictable slots for {n_e} evictions")
-    order = np.lexsort((cand, sigma[cand]))      # primary key: score; ties: slot
+    rank_key = sigma if policy == "h2o" else pos
+    order = np.lexsort((cand, rank_key[cand]))   # primary key: score or position; ties: slot
     ranked = cand[order]
     evicted = ranked[:n_e]
     if 0 < n_e < ranked.size:
-        cut_gap = float(sigma[ranked[n_e]] - sigma[ranked[n_e - 1]])
+        cut_gap = float(rank_key[ranked[n_e]] - rank_key[ranked[n_e - 1]])
     else:
         cut_gap = math.inf
     targets = np.sort(np.concatenate([free[:n_free], evicted]))
     return targets, evicted, cut_gap
 
 
-def chunk_step(K, V, sigma, pos, T: int, q, k_new, v_new, W: int, scale=None):
+def chunk_step(K, V, sigma, pos, T: int, q, k_new, v_new, W: int, scale=None, policy: str = "h2o",
+               n_sink: int = 0):
     """One H2O chunk step on every (batch, KV head); inputs are not modified.
 
     Arrays: K, V ``[B,Hkv,M,d]``; sigma ``[B,Hkv,M]``; pos ``[B,Hkv,M]``;
@@ -172,9 +188,11 @@ def chunk_step(K, V, sigma, pos, T: int, q, k_new, v_new, W: int, scale=None):
             o, ls, ds, m = attend_head(K[b, h], V[b, h], pos[b, h], q[b, hs],
                                        k_new[b, h], v_new[b, h], scale)
             out[b, hs], lse[b, hs] = o, ls
+            if policy != "h2o":             # position policies keep no score
+                ds, m = np.zeros_like(ds), np.zeros_like(m)
             delta_sigma[b, h], mu[b, h] = ds, m
             sig = sigma[b, h] + ds          # free slots stay 0 (ds is 0 there)
-            R, E, gap = select_targets(sig, pos[b, h], T, W, S)
+            R, E, gap = select_targets(sig, pos[b, h], T, W, S, policy, n_sink)
             sig[R] = m
             K[b, h, R] = k_new[b, h]
             V[b, h, R] = v_new[b, h]
@@ -186,13 +204,13 @@ def chunk_step(K, V, sigma, pos, T: int, q, k_new, v_new, W: int, scale=None):
                 evicted=evicted, cut_gap=cut_gap)
 
 
-def prefill(K, V, sigma, pos, q, k, v, W: int, scale=None):
+def prefill(K, V, sigma, pos, q, k, v, W: int, scale=None, policy: str = "h2o", n_sink: int = 0):
     """The prefill chunk of length N_C (LHF Fig. 1(a)) into an empty cache."""
     if np.any(pos >= 0):
         raise ValueError("prefill expects an empty cache")
     if q.shape[2] > K.shape[2]:
         raise ValueError("prefill chunk longer than the cache")
-    return chunk_step(K, V, sigma, pos, 0, q, k, v, W, scale)
+    return chunk_step(K, V, sigma, pos, 0, q, k, v, W, scale, policy, n_sink)
 
 
 def chunk_backward(K, V, pos, q, k_new, v_new, d_out, scale=None):
@@ -241,7 +259,8 @@ def chunk_backward(K, V, pos, q, k_new, v_new, d_out, scale=None):
     return dq, dK, dV, dk_new, dv_new
 
 
-def run_sequence(chunks, M: int, W: int, scale=None, keep_history: bool = False):
+def run_sequence(chunks, M: int, W: int, scale=None, keep_history: bool = False, policy: str = "h2o",
+                 n_sink: int = 0):
     """Free-running H2O over a row of chunks ``[(q, k, v), ...]`` (prefill first).
 
     Returns the final state dict; with ``keep_history`` also the list of all
@@ -251,9 +270,9 @@ def run_sequence(chunks, M: int, W: int, scale=None, keep_history: bool = False)
     B, Hkv, _, d = k0.shape
     K, V, sigma, pos = empty_state(B, Hkv, M, d)
     hist = []
-    st = prefill(K, V, sigma, pos, *chunks[0], W, scale)
+    st = prefill(K, V, sigma, pos, *chunks[0], W, scale, policy, n_sink)
     hist.append(st)
     for q, k, v in chunks[1:]:
-        st = chunk_step(st["K"], st["V"], st["sigma"], st["pos"], st["T"], q, k, v, W, scale)
+        st = chunk_step(st["K"], st["V"], st["sigma"], st["pos"], st["T"], q, k, v, W, scale, policy, n_sink)
         hist.append(st)
     return (st, hist) if keep_history else st

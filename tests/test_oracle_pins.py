@@ -478,3 +478,61 @@ def test_row_grads_match_central_differences_with_evictions():
                 x[idx] = old
                 np.testing.assert_allclose(grads[c][a][idx], (lp - lm) / (2 * eps), rtol=1e-5, atol=1e-8,
                                            err_msg=f"chunk {c} tensor {a} index {idx}")
+
+
+# ---------------------------------------------------------------- position policies
+# "recent" keeps the newest tokens, "sink_recent" also the first n_sink: the
+# cache is then a closed form of T, and attention is SDPA with the matching
+# band mask over the whole sequence.
+def _policy_mask(lens, M, n_sink):
+    L = sum(lens)
+    mask = np.zeros((L, L), dtype=bool)
+    t0 = 0
+    for n in lens:
+        lo = t0 - (M - n_sink)              # oldest non-sink position held before the chunk
+        for i in range(n):
+            t = t0 + i
+            p = np.arange(L)
+            mask[t] = (p <= t) & ((p >= lo) | (p < n_sink) | (p >= t0))
+        t0 += n
+    return mask
+
+
+@pytest.mark.parametrize("policy,n_sink", [("recent", 0), ("sink_recent", 3)])
+def test_position_policies_are_banded_attention(policy, n_sink):
+    rng = np.random.default_rng(41)
+    B, Hq, Hkv, d = 1, 4, 2, 8
+    M, W = 20, 4
+    lens = [12, 6, 6, 6, 6, 6]
+    chunks = _rand_chunks(rng, B, Hq, Hkv, d, lens)
+    scale = 1.0 / math.sqrt(d)
+    _, hist = orc.run_sequence(chunks, M, W=W, scale=scale, keep_history=True, policy=policy,
+                               n_sink=n_sink)
+    qs = np.concatenate([c[0] for c in chunks], axis=2)
+    ks = np.concatenate([c[1] for c in chunks], axis=2)
+    vs = np.concatenate([c[2] for c in chunks], axis=2)
+    out_ref, lse_ref, _ = _torch_causal(qs, ks, vs, scale, mask=_policy_mask(lens, M, n_sink))
+    t0 = 0
+    for c, n in enumerate(lens):
+        np.testing.assert_allclose(hist[c]["out"], out_ref[:, :, t0:t0 + n], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(hist[c]["lse"], lse_ref[:, :, t0:t0 + n], rtol=0, atol=1e-12)
+        t0 += n
+        held = np.sort(hist[c]["pos"][0, 0][hist[c]["pos"][0, 0] >= 0])
+        keep = min(t0, M)
+        expect = np.arange(t0 - keep, t0) if t0 <= M or n_sink == 0 else \
+            np.concatenate([np.arange(n_sink), np.arange(t0 - (M - n_sink), t0)])
+        np.testing.assert_array_equal(held, expect)
+        assert (hist[c]["sigma"] == 0).all()          # no score is kept
+
+
+def test_h2o_with_window_m_minus_s_equals_recent():
+    rng = np.random.default_rng(42)
+    B, Hq, Hkv, d = 1, 2, 1, 8
+    M, S = 16, 4
+    lens = [8] + [S] * 6
+    chunks = _rand_chunks(rng, B, Hq, Hkv, d, lens)
+    a = orc.run_sequence(chunks, M, W=M - S, keep_history=True)[1]
+    b = orc.run_sequence(chunks, M, W=M - S, keep_history=True, policy="recent")[1]
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x["targets"], y["targets"])
+        np.testing.assert_allclose(x["out"], y["out"], rtol=0, atol=0)
