@@ -34,6 +34,14 @@
  * The score rule (plain cumulative sum since insertion), the step order, the
  * window test and the tie-break are readings of pages that leave them open.
  *
+ * Eviction policy (h2o_config.policy): H2O_POLICY_H2O is the step above.
+ * The position policies H2O_POLICY_RECENT and H2O_POLICY_SINK_RECENT (the
+ * pages' lr and slr rows among their five KV cache policies, Tables 1 and 6;
+ * sinks after the attention-sinks paper in their reference list) skip step
+ * 2 and rank the candidates by (position, slot index) instead, so the oldest
+ * tokens go; SINK_RECENT never evicts positions below n_sink.  They keep no
+ * score: a written slot's score is 0 and the others are left as they are.
+ *
  * Conventions for every call:
  *   - Buffer pointers are DEVICE pointers to contiguous, 16-byte aligned
  *     memory owned by the caller; the library never allocates device memory.
@@ -76,6 +84,7 @@ typedef enum {
 } h2o_status;
 
 typedef enum { H2O_BF16 = 0, H2O_FP32 = 1 } h2o_dtype;
+typedef enum { H2O_POLICY_H2O = 0, H2O_POLICY_RECENT = 1, H2O_POLICY_SINK_RECENT = 2 } h2o_policy;
 
 typedef struct {
   int32_t batch;          /* B >= 1                                               */
@@ -88,6 +97,8 @@ typedef struct {
   int32_t max_prefill;    /* largest N_C accepted by h2o_prefill (<= M)           */
   int32_t dtype;          /* h2o_dtype                                            */
   float softmax_scale;    /* <= 0 selects 1/sqrt(d)                               */
+  int32_t policy;         /* h2o_policy (0 = H2O)                                 */
+  int32_t n_sink;         /* SINK_RECENT: positions < n_sink are kept; else 0     */
 } h2o_config;
 
 typedef struct h2o_cache h2o_cache;   /* opaque host-side handle */
@@ -97,7 +108,9 @@ typedef struct h2o_cache h2o_cache;   /* opaque host-side handle */
  * 1 <= max_prefill <= M, 0 <= W and M - W >= max_chunk (a reading of the pages:
  * with it every eviction finds enough candidates), M, max_chunk and
  * max_prefill <= 16384, (Hq / Hkv) * max(max_chunk, max_prefill) <= 2^20
- * query rows per KV group, and every chunk tensor below 2^31 elements. */
+ * query rows per KV group, every chunk tensor below 2^31 elements, a known
+ * policy, n_sink = 0 unless the policy is SINK_RECENT, and for SINK_RECENT
+ * 0 <= n_sink and M - W - n_sink >= max_chunk. */
 H2O_API h2o_status h2o_validate_config(const h2o_config* cfg);
 
 /* Host only: bytes of device workspace h2o_cache_init needs for `cfg`
@@ -140,7 +153,8 @@ H2O_API h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k,
  * Optional outputs (NULL to skip):
  *   slots_out [B,Hkv,s] int32: slot R_j chunk token j was written to;
  *   step_mass [B,Hkv,M+s] fp32: the step's mass per cache slot (0 for slots
- *     that were free) followed by mu_j per chunk key;
+ *     that were free) followed by mu_j per chunk key (H2O policy only: a
+ *     position policy computes no mass and returns H2O_ERR_UNSUPPORTED);
  *   k_old, v_old [B,Hkv,s,d]: the rows the step overwrote (zeros where a
  *     free slot was filled) -- the buffer delta of LHF Fig. 1(c);
  *   pos_old [B,Hkv,s] int32: the position slot R_j held before the step (-1

@@ -125,6 +125,8 @@ h2o::StepShape shape_of(const h2o_cache* c, int s) {
   sh.W = g.recent_window;
   sh.n_cache = c->filled >= 0 ? c->filled : g.cache_slots;
   sh.scale = g.softmax_scale > 0.f ? g.softmax_scale : 1.0f / sqrtf(static_cast<float>(g.head_dim));
+  sh.policy = g.policy;
+  sh.n_sink = g.n_sink;
   return sh;
 }
 
@@ -140,10 +142,13 @@ h2o_status run_step(h2o_cache* c, const void* q, const void* k, const void* v, i
   h2o::AttnArgs aa{q, c->k_cache, c->v_cache, c->pos, k, v, out, lse_buf};
   h2o_status r = timed(c, 0, st, [&] { return h2o::launch_attn_fwd(sh, aa, dtype, st); });
   if (r != H2O_OK) return r;
-  const int R = h2o::score_row_splits(sh, dtype);
-  h2o::ScoreArgs sa{q, c->k_cache, k, lse_buf, partial, R};
-  r = timed(c, 1, st, [&] { return h2o::launch_score(sh, sa, dtype, st); });
-  if (r != H2O_OK) return r;
+  // the position policies keep no score: no mass pass
+  const int R = sh.policy == H2O_POLICY_H2O ? h2o::score_row_splits(sh, dtype) : 0;
+  if (sh.policy == H2O_POLICY_H2O) {
+    h2o::ScoreArgs sa{q, c->k_cache, k, lse_buf, partial, R};
+    r = timed(c, 1, st, [&] { return h2o::launch_score(sh, sa, dtype, st); });
+    if (r != H2O_OK) return r;
+  }
   int32_t* targets = reinterpret_cast<int32_t*>(c->ws + c->lay.targets_off);
   h2o::SelectArgs xa{c->k_cache, c->v_cache, c->scores, c->pos, k, v, partial, R, targets,
                      slots_out, pos_old, step_mass, k_old, v_old, status, static_cast<int32_t>(c->T)};
@@ -224,6 +229,11 @@ h2o_status h2o_validate_config(const h2o_config* c) {
   // every tensor offset must fit in int64 and every chunk tensor below 2^31 elements
   const int64_t big = static_cast<int64_t>(c->batch) * c->n_q_heads * max_len(c) * c->head_dim;
   if (big >= (int64_t{1} << 31)) return H2O_ERR_CONFIG;
+  if (c->policy != H2O_POLICY_H2O && c->policy != H2O_POLICY_RECENT && c->policy != H2O_POLICY_SINK_RECENT)
+    return H2O_ERR_CONFIG;
+  if (c->policy != H2O_POLICY_SINK_RECENT && c->n_sink != 0) return H2O_ERR_CONFIG;
+  if (c->n_sink < 0) return H2O_ERR_CONFIG;
+  if (static_cast<int64_t>(c->cache_slots) - c->recent_window - c->n_sink < c->max_chunk) return H2O_ERR_CONFIG;
   return H2O_OK;
 }
 
@@ -288,6 +298,7 @@ h2o_status h2o_chunk_step(h2o_cache* c, const void* q, const void* k_new, const 
                           void* v_old, int32_t* pos_old, void* stream) {
   if (!c || !q || !k_new || !v_new || !out) return H2O_ERR_NULL;
   if ((k_old == nullptr) != (v_old == nullptr)) return H2O_ERR_NULL;
+  if (step_mass && c->cfg.policy != H2O_POLICY_H2O) return H2O_ERR_UNSUPPORTED;
   if (s < 1 || s > c->cfg.max_chunk) return H2O_ERR_SHAPE;
   if (c->T + s > INT32_MAX) return H2O_ERR_STATE;
   return run_step(c, q, k_new, v_new, s, out, lse, slots_out, pos_old, step_mass, k_old, v_old,

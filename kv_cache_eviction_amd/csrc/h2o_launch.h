@@ -12,6 +12,8 @@ struct StepShape {
   int B, Hq, Hkv, D, S, M, W;
   int n_cache;
   float scale;      // softmax scale applied to q.k
+  int policy = 0;   // 0 H2O (score key), 1 recent, 2 sink_recent (position key)
+  int n_sink = 0;   // sink_recent: positions below n_sink are never evicted
 };
 
 struct AttnArgs {

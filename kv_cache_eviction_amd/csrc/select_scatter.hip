@@ -11,6 +11,12 @@
 // smallest (score, slot index); chunk token j goes to the j-th smallest
 // target slot.
 //
+// Position policies (recent, sink_recent: the pages' lr and slr rows among
+// their five KV cache policies, Tables 1 and 6; sinks after the attention-
+// sinks paper in their reference list): the same select with the position as
+// the key, so the oldest candidates go; positions below n_sink are never
+// candidates; no score is read, and a written slot gets score 0.
+//
 // Two kernels.  The select kernel runs one 512-thread workgroup per
 // (b, KV head): no other workgroup reads or writes that head's scores,
 // positions or slots, so it needs no inter-workgroup synchronisation.  It
@@ -25,6 +31,8 @@
 //      targets that were free).
 // The scatter kernel then copies the chunk's K/V rows into their slots with
 // many workgroups per head (a pure bandwidth copy, 16-byte accesses).
+#include <type_traits>
+
 #include "h2o_device.h"
 #include "h2o_launch.h"
 
@@ -105,12 +113,12 @@ __device__ void block_excl_scan2(int a, int b, int* tmp, int& pa, int& pb) {
 
 // Thread t owns the SPT consecutive slots t*SPT .. t*SPT+SPT-1 (SPT*512 >= M)
 // and keeps their keys and classes in registers through every phase.
-template <int SPT>
+template <int SPT, bool POS>
 __global__ __launch_bounds__(kThreads) void select_kernel(
     float* __restrict__ scores, int32_t* __restrict__ pos, const float* __restrict__ partial,
     int R, int32_t* __restrict__ targets, int32_t* __restrict__ slots_out,
     int32_t* __restrict__ pos_old, float* __restrict__ step_mass, int32_t* __restrict__ status, int T, int W, int S, int M,
-    int n_cache, int vec) {
+    int n_cache, int vec, int n_floor) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   int* s_R = reinterpret_cast<int*>(smem);                 // [S]: target of chunk row j (flagged)
   __shared__ __attribute__((aligned(16))) uint32_t hist[3][kWavesSel / 2][256];   // per wave pair, 3 rotating
@@ -133,11 +141,20 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   for (int k = 0; k < kMuRegs; ++k) {
     const int jj = min(tid + k * kThreads, S - 1);
 #pragma unroll
-    for (int r = 0; r < kMaxSplits; ++r) mup[k][r] = ph[static_cast<size_t>(min(r, R - 1)) * PS + M + jj];
+    for (int r = 0; r < kMaxSplits; ++r)
+      mup[k][r] = POS ? 0.f : ph[static_cast<size_t>(min(r, R - 1)) * PS + M + jj];
   }
   int pv[SPT];
   float sv[SPT], dv[SPT];
-  if (SPT % 4 == 0 && vec && m0 + SPT <= M) {
+  if constexpr (POS) {
+    // positions only: no score is read or kept
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      pv[i] = pos_h[min(m0 + i, M - 1)];
+      sv[i] = 0.f;
+      dv[i] = 0.f;
+    }
+  } else if (SPT % 4 == 0 && vec && m0 + SPT <= M) {
     // 16-byte loads of the thread's slots (rows aligned: M, S multiples of 4)
 #pragma unroll
     for (int i = 0; i < SPT; i += 4) {
@@ -190,14 +207,14 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     float sc = sv[i];
     if (pv[i] >= 0) {
       sc += ds;
-      if (pv[i] < T - W) cmask |= 1u << i;
+      if (pv[i] >= n_floor && pv[i] < T - W) cmask |= 1u << i;
     } else {
       ds = 0.f;
       if (exists) fmask |= 1u << i;
     }
     if (!exists) cmask &= ~(1u << i);
     if (step_mass && exists) step_mass[static_cast<size_t>(bh) * PS + m] = ds;
-    key[i] = order_key(sc);
+    key[i] = POS ? static_cast<uint32_t>(pv[i]) : order_key(sc);
     if ((cmask >> i) & 1u) {
       k_and &= key[i];
       k_or |= key[i];
@@ -229,9 +246,11 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   const int n_f = min(S, n_free);
   const int n_e = S - n_f;
   if (n_cand < n_e) {                      // infeasible adopted state: no slot is written
+    if constexpr (!POS) {
 #pragma unroll
-    for (int i = 0; i < SPT; ++i)
-      if (m0 + i < M && !((fmask >> i) & 1u)) sc_h[m0 + i] = key_value(key[i]);
+      for (int i = 0; i < SPT; ++i)
+        if (m0 + i < M && !((fmask >> i) & 1u)) sc_h[m0 + i] = key_value(key[i]);
+    }
     for (int jj = tid; jj < S; jj += kThreads) targets[static_cast<size_t>(bh) * S + jj] = -1;
     if (tid == 0) atomicOr(status, 1);
     return;
@@ -332,7 +351,9 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     if (t) s_R[j++] = fre ? (m | kWasFree) : m;
     nsc[i] = fre ? sv[i] : key_value(key[i]);
   }
-  if (SPT % 4 == 0 && vec && m0 + SPT <= M) {
+  if constexpr (POS) {
+    // scores are not kept
+  } else if (SPT % 4 == 0 && vec && m0 + SPT <= M) {
 #pragma unroll
     for (int i = 0; i < SPT; i += 4)
       *reinterpret_cast<float4*>(sc_h + m0 + i) = float4{nsc[i], nsc[i + 1], nsc[i + 2], nsc[i + 3]};
@@ -365,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   for (int jj = tid + kMuRegs * kThreads; jj < S; jj += kThreads) {
     float part[kMaxSplits];
 #pragma unroll
-    for (int r = 0; r < kMaxSplits; ++r) part[r] = ph[static_cast<size_t>(min(r, R - 1)) * PS + M + jj];
+    for (int r = 0; r < kMaxSplits; ++r) part[r] = POS ? 0.f : ph[static_cast<size_t>(min(r, R - 1)) * PS + M + jj];
     float mu = 0.f;
 #pragma unroll
     for (int r = 0; r < kMaxSplits; ++r) mu += (r < R) ? part[r] : 0.f;
@@ -435,16 +456,20 @@ hipError_t launch_select(const StepShape& sh, const SelectArgs& a, hipStream_t s
     }
     hipLaunchKernelGGL(kern, dim3(n_heads), dim3(kThreads), lds, st, a.scores, a.pos, a.partial, a.R,
                        a.targets, a.slots_out, a.pos_old, a.step_mass, a.status, a.T, sh.W, sh.S, sh.M, sh.n_cache,
-                       vec ? 1 : 0);
+                       vec ? 1 : 0, sh.policy == 2 ? sh.n_sink : 0);
     return hipGetLastError();
   };
   // slots per thread: the smallest power of two with 512 * SPT >= M (M <= 16384)
-  if (sh.M <= kThreads) return go(select_kernel<1>);
-  if (sh.M <= 2 * kThreads) return go(select_kernel<2>);
-  if (sh.M <= 4 * kThreads) return go(select_kernel<4>);
-  if (sh.M <= 8 * kThreads) return go(select_kernel<8>);
-  if (sh.M <= 16 * kThreads) return go(select_kernel<16>);
-  return go(select_kernel<32>);
+  auto pick = [&](auto pos_key) -> hipError_t {
+    constexpr bool P = decltype(pos_key)::value;
+    if (sh.M <= kThreads) return go(select_kernel<1, P>);
+    if (sh.M <= 2 * kThreads) return go(select_kernel<2, P>);
+    if (sh.M <= 4 * kThreads) return go(select_kernel<4, P>);
+    if (sh.M <= 8 * kThreads) return go(select_kernel<8, P>);
+    if (sh.M <= 16 * kThreads) return go(select_kernel<16, P>);
+    return go(select_kernel<32, P>);
+  };
+  return sh.policy == 0 ? pick(std::false_type{}) : pick(std::true_type{});
 }
 
 hipError_t launch_scatter(const StepShape& sh, const SelectArgs& a, int dtype, hipStream_t st) {

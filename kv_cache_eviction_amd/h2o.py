@@ -24,6 +24,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libh2o.so"
 H2O_OK, H2O_ERR_NULL, H2O_ERR_CONFIG, H2O_ERR_SHAPE, H2O_ERR_STATE = 0, 1, 2, 3, 4
 H2O_ERR_WORKSPACE, H2O_ERR_HIP, H2O_ERR_UNSUPPORTED = 5, 6, 7
 H2O_BF16, H2O_FP32 = 0, 1
+POLICIES = {"h2o": 0, "recent": 1, "sink_recent": 2}
 KERNEL_IDS = {"attn_fwd": 0, "score": 1, "select": 2, "reset": 3, "scatter": 4}
 
 EXPORTED = [
@@ -41,6 +42,7 @@ class H2OConfigC(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("cache_slots", ctypes.c_int32),
         ("recent_window", ctypes.c_int32), ("max_chunk", ctypes.c_int32),
         ("max_prefill", ctypes.c_int32), ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("policy", ctypes.c_int32), ("n_sink", ctypes.c_int32),
     ]
 
 
@@ -106,11 +108,14 @@ class H2OConfig:
     max_prefill: int
     dtype: str = "bf16"           # "bf16" | "fp32"
     softmax_scale: float = 0.0    # <= 0: 1/sqrt(head_dim)
+    policy: str = "h2o"           # "h2o" | "recent" | "sink_recent"
+    n_sink: int = 0               # sink_recent: positions below n_sink are kept
 
     def c(self) -> H2OConfigC:
         return H2OConfigC(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim,
                           self.cache_slots, self.recent_window, self.max_chunk, self.max_prefill,
-                          H2O_BF16 if self.dtype == "bf16" else H2O_FP32, self.softmax_scale)
+                          H2O_BF16 if self.dtype == "bf16" else H2O_FP32, self.softmax_scale,
+                          POLICIES.get(self.policy, -1), self.n_sink)
 
     @property
     def torch_dtype(self):

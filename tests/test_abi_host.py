@@ -61,6 +61,10 @@ def test_named_workload_configs_validate():
     dict(recent_window=-1),
     dict(softmax_scale=math.nan),
     dict(n_q_heads=1024, n_kv_heads=1),  # G * max_len above 2^20 query rows per KV group
+    dict(policy="bogus"),
+    dict(n_sink=4),                     # sinks only with the sink_recent policy
+    dict(policy="sink_recent", n_sink=-1),
+    dict(policy="sink_recent", n_sink=900),   # M - W - n_sink < max_chunk
 ])
 def test_invalid_configs_are_rejected(kw):
     h2o = _lib_module()
@@ -92,3 +96,10 @@ def test_null_handle_calls_fail_cleanly():
     assert h2o._lib.h2o_recurrence_backward_step(*([None] * 11), 4, *([None] * 9), 0, None) == h2o.H2O_ERR_NULL
     assert h2o._lib.h2o_tokens_seen(None) == -1
     assert h2o._lib.h2o_last_hip_error(None) == 0
+
+
+def test_position_policy_configs_validate():
+    h2o = _lib_module()
+    assert h2o.h2o_validate_config(_cfg(policy="recent")) == h2o.H2O_OK
+    assert h2o.h2o_validate_config(_cfg(policy="sink_recent", n_sink=4)) == h2o.H2O_OK
+    assert h2o.h2o_validate_config(_cfg(policy="sink_recent", n_sink=768)) == h2o.H2O_OK
