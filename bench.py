@@ -20,7 +20,11 @@ backward walk through the buffer (h2o_recurrence_backward_step, last chunk
 first, the prefill last), which gives every chunk's q/k/v their total
 gradients.
 
+With --policy recent | sink_recent (--n-sink N): the same step under a
+position eviction policy (no score pass; the oldest unprotected tokens go).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--recurrence]
+                       [--policy h2o|recent|sink_recent] [--n-sink N]
        python bench.py --copy-probe MB    (plain copy of known size, for
                                            scaling the HBM byte counters)
 """
@@ -102,7 +106,7 @@ def recorded_traffic(kernel, workload):
     return int(m.group(1))
 
 
-def oracle_sample(w, seed, budget_s=20.0):
+def oracle_sample(w, seed, budget_s=20.0, policy="h2o", n_sink=0):
     """Times the fp64 oracle on the first chunks of the workload (prefill plus
     as many chunk steps as fit in about `budget_s`), all heads, forward."""
     from oracle import h2o_oracle as orc
@@ -123,7 +127,7 @@ def oracle_sample(w, seed, budget_s=20.0):
     while c < w.n_chunks and elapsed < budget_s:
         q, k, v = (wl.stored_to_f64(x) for x in wl.chunk_inputs(w, seed, c, hh=hh))
         t0 = time.perf_counter()
-        st = orc.chunk_step(K, V, sig, pos, T, q, k, v, w.recent_window)
+        st = orc.chunk_step(K, V, sig, pos, T, q, k, v, w.recent_window, policy=policy, n_sink=n_sink)
         elapsed += time.perf_counter() - t0
         K, V, sig, pos, T = st["K"], st["V"], st["sigma"], st["pos"], st["T"]
         done_flops += flops[c]
@@ -161,6 +165,8 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB")
     ap.add_argument("--recurrence", action="store_true",
                     help="forward over the row, then the backward walk through the buffer")
+    ap.add_argument("--policy", default="h2o", choices=["h2o", "recent", "sink_recent"])
+    ap.add_argument("--n-sink", type=int, default=4, help="sink tokens of the sink_recent policy")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the H2O step shards by batch or KV head with no "
@@ -181,8 +187,9 @@ def main():
     if rec and not backward:
         print(f"--recurrence needs a workload with a backward (not {w.name})", file=sys.stderr)
         sys.exit(2)
+    n_sink = args.n_sink if args.policy == "sink_recent" else 0
     cfg = h2o.H2OConfig(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.cache_slots,
-                        w.recent_window, w.chunk, w.prefill, w.dtype)
+                        w.recent_window, w.chunk, w.prefill, w.dtype, policy=args.policy, n_sink=n_sink)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     hh = wl.heavy_hitters(w, args.seed)
@@ -364,13 +371,17 @@ def main():
         elif w.name != "llama8b_64k":
             metric = "H2O chunk-step TFLOP/s + tokens/s at %dk ctx, G=%d d=%d%s; %% of roofline" % (
                 w.total_len // 1024, w.group, w.head_dim, ", with the backward" if backward else "")
+        if args.policy != "h2o":
+            metric = "%s-policy chunk-step TFLOP/s + tokens/s at %dk ctx, G=%d d=%d%s; %% of roofline" % (
+                args.policy, w.total_len // 1024, w.group, w.head_dim,
+                " (n_sink %d)" % n_sink if n_sink else "")
         unit = "TFLOP/s"
         value = round(tflops, 3)
     tokens_per_s = tokens / (ms_per_step * 1e-3)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = oracle_sample(w, args.seed, args.cpu_budget)
+        cpu = oracle_sample(w, args.seed, args.cpu_budget, args.policy, n_sink)
 
     rec = {
         "metric": metric,
@@ -389,7 +400,8 @@ def main():
         "config": {
             "workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
             "head_dim": w.head_dim, "prefill": w.prefill, "chunk": w.chunk, "total_len": w.total_len,
-            "cache_slots": w.cache_slots, "recent_window": w.recent_window,
+            "cache_slots": w.cache_slots, "recent_window": w.recent_window, "policy": args.policy,
+            **({"n_sink": n_sink} if n_sink else {}),
             "step": ("cache reset + prefill + %d chunk steps recording their buffer deltas, then the "
                      "backward walk over all %d steps (last first)" % (w.n_steps, w.n_chunks)) if rec else
                     "%s + %d chunk steps%s" % (
