@@ -23,6 +23,7 @@ struct Layout {
   size_t lse_off, lse_bytes;
   size_t targets_off, targets_bytes;     // target slot list of the current step
   size_t counters_off, counters_bytes;   // the device status word
+  size_t split_off, split_bytes;         // attention key-split partial states
   size_t n_counters;                     // ints cleared at init
   size_t total;
 };
@@ -42,7 +43,9 @@ Layout layout_of(const h2o_config* c) {
   L.counters_off = L.targets_off + L.targets_bytes;
   L.n_counters = 1;
   L.counters_bytes = align_up(L.n_counters * sizeof(int32_t));
-  L.total = L.counters_off + L.counters_bytes;
+  L.split_off = L.counters_off + L.counters_bytes;
+  L.split_bytes = c->dtype == H2O_BF16 ? align_up(h2o::attn_split_bytes(c->batch, c->n_q_heads, static_cast<int>(smax), c->head_dim)) : 0;
+  L.total = L.split_off + L.split_bytes;
   return L;
 }
 
@@ -139,7 +142,8 @@ h2o_status run_step(h2o_cache* c, const void* q, const void* k, const void* v, i
   int32_t* status = reinterpret_cast<int32_t*>(c->ws + c->lay.counters_off);
   const int dtype = c->cfg.dtype;
 
-  h2o::AttnArgs aa{q, c->k_cache, c->v_cache, c->pos, k, v, out, lse_buf};
+  float* split_part = c->lay.split_bytes ? reinterpret_cast<float*>(c->ws + c->lay.split_off) : nullptr;
+  h2o::AttnArgs aa{q, c->k_cache, c->v_cache, c->pos, k, v, out, lse_buf, split_part};
   h2o_status r = timed(c, 0, st, [&] { return h2o::launch_attn_fwd(sh, aa, dtype, st); });
   if (r != H2O_OK) return r;
   // the position policies keep no score: no mass pass

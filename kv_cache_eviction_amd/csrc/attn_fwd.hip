@@ -43,6 +43,7 @@
 //     with the longest causal extent are dispatched first.
 // fp32 path: one thread per query row, scalar online softmax over K/V rows
 // broadcast from LDS (used for fp32 workloads, which are tiny).
+#include <algorithm>
 #include <type_traits>
 
 #include "h2o_device.h"
@@ -53,6 +54,7 @@ namespace {
 
 constexpr int kKT = 64;        // keys per tile
 constexpr int kRowBlocks = 4;  // row blocks (32 queries of one head) per workgroup
+constexpr int kMaxKeySplits = 4;
 constexpr int kFwdThreads = 512;
 constexpr float kRescaleSlack = 8.f;   // log2 headroom before the running maximum must move
 constexpr float kNoMax = -1e30f;       // running maximum of a query that has seen no key yet
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
     const bf16_t* __restrict__ Vc, const int32_t* __restrict__ pos,
     const bf16_t* __restrict__ Kn, const bf16_t* __restrict__ Vn,
     bf16_t* __restrict__ O, float* __restrict__ lse, int Hq, int Hkv, int S,
-    int M, int n_cache, float c2, int n_heads, int wg_per_head) {
+    int M, int n_cache, float c2, int n_heads, int wg_per_head, int n_split, float* __restrict__ part) {
   constexpr int DS = D / 16;              // MFMA k-steps over d
   constexpr int DB = D / 32;              // 32-row blocks of O^T
   constexpr int CPR = D / 8;              // 16-byte chunks per row
@@ -117,7 +119,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   const int lane = tid & 63, hf = lane >> 5, col = lane & 31;
   const int grp = wave >> 2, rbw = wave & 3;
   const int bh = blockIdx.x % n_heads;
-  const int wgi = wg_per_head - 1 - static_cast<int>(blockIdx.x) / n_heads;
+  const int wsp = static_cast<int>(blockIdx.x) / n_heads;     // (row group, key split)
+  const int wgi = wg_per_head - 1 - wsp / n_split;
+  const int split = wsp - (wsp / n_split) * n_split;
   const int b = bh / Hkv, kvh = bh - b * Hkv;
   const int G = Hq / Hkv;
   const int n_rb = DEC ? (G * S + 31) >> 5 : G * ((S + 31) >> 5);
@@ -150,7 +154,13 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   const int rb_last = min(wgi * RBW + RBW - 1, n_rb - 1);
   const int n_chunk_keys = DEC ? S : min(S, (rb_last / G + 1) * 32);
   const int n_ct = (n_cache + kKT - 1) / kKT;
-  const int n_tiles = n_ct + (n_chunk_keys + kKT - 1) / kKT;
+  const int n_tiles_all = n_ct + (n_chunk_keys + kKT - 1) / kKT;
+  // Key split (small grids): this workgroup takes global tiles
+  // [T0, T0 + n_tiles) of the row group's cache-then-chunk tile list and
+  // leaves its partial softmax state for the merge kernel.  Below, tile
+  // indices are local to that range.
+  const int T0 = split * n_tiles_all / n_split;
+  const int n_tiles = (split + 1) * n_tiles_all / n_split - T0;
   // group g takes tiles 2t + g, t < n_iter (even: the loop body is unrolled
   // by two so that LDS slot parities are compile-time); tiles past the end
   // are fully masked
@@ -218,7 +228,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
     return key < n ? off : off - static_cast<uint32_t>(key - n + 1) * RB;
   };
   auto issue_k = [&](int T, auto g, auto slot) __attribute__((always_inline)) {
-    T = min(T, n_tiles - 1);          // past the end: reload the last tile (masked)
+    T = T0 + min(T, n_tiles - 1);     // past the end: reload the last tile (masked)
     const bool is_cache = T < n_ct;
     const int base = is_cache ? T * kKT : (T - n_ct) * kKT;
     const int n = (is_cache ? n_cache : S) - base;
@@ -241,7 +251,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
     }
   };
   auto issue_v = [&](int T, auto g, auto slot) __attribute__((always_inline)) {
-    T = min(T, n_tiles - 1);          // past the end: reload the last tile (masked)
+    T = T0 + min(T, n_tiles - 1);     // past the end: reload the last tile (masked)
     const bool is_cache = T < n_ct;
     const int base = is_cache ? T * kKT : (T - n_ct) * kKT;
     const int n = (is_cache ? n_cache : S) - base;
@@ -260,9 +270,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
       for (int j = 0; j < NDMA; ++j) dma16(r, dst + j * 1024, clamp_row(vl + dv_soff(j), n), soff);
     }
   };
-  // position of this lane's key in global tile T (cache tiles; -1 = free or past the end)
+  // position of this lane's key in local tile T (cache tiles; -1 = free or past the end)
   auto load_pos = [&](int T) __attribute__((always_inline)) {
-    const int key = T * kKT + lane;
+    const int key = (T0 + T) * kKT + lane;
     const int p = pos_head[min(key, M - 1)];
     return key < n_cache ? p : -1;
   };
@@ -350,8 +360,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   // masks global tile T's scores (then the maximum mx of the raw scores is
   // recomputed over the visible ones), and moves the running maximum (with
   // O and l rescaled) only if some score exceeds it by the slack
-  auto mask_and_check = [&](f32x16& a0, f32x16& a1, float mx, int T, int posv) __attribute__((always_inline)) {
-    const bool exists = T < n_tiles;
+  auto mask_and_check = [&](f32x16& a0, f32x16& a1, float mx, int Tl, int posv) __attribute__((always_inline)) {
+    const bool exists = Tl < n_tiles;
+    const int T = T0 + Tl;
     const bool is_cache = T < n_ct;
     const int base = is_cache ? T * kKT : (T - n_ct) * kKT;
     uint64_t vm;
@@ -477,8 +488,10 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
       }
     }
   };
-  if (grp == 0) run_group(I0{});
-  else run_group(I1{});
+  if (n_tiles > 0) {                  // workgroup-uniform
+    if (grp == 0) run_group(I0{});
+    else run_group(I1{});
+  }
 
   // ---- merge the partial softmax states of a row block: writer waves pass
   // (m, l, O^T) through LDS (one 32-row block of O^T per round, through a K
@@ -529,6 +542,19 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   if (grp == 1 || kh == 1 || !active) return;
   const float l_tot = l_run + xor32(l_run);
   if (!row_ok) return;
+  if (n_split > 1) {
+    // partial state of this row and split: O unnormalised against m_run
+    // (log2 units), then m_run and the row sum; record = D + 4 floats
+    float* rec = part + ((static_cast<size_t>(b * Hq + hq) * S + qi) * n_split + split) * (D + 4);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *reinterpret_cast<f32x4*>(rec + db * 32 + 8 * a + 4 * hf) =
+            f32x4{o[db][4 * a], o[db][4 * a + 1], o[db][4 * a + 2], o[db][4 * a + 3]};
+    if (hf == 0) *reinterpret_cast<f32x4*>(rec + D) = f32x4{m_run, l_tot, 0.f, 0.f};
+    return;
+  }
   const float inv = 1.f / l_tot;
   bf16_t* orow = O + (static_cast<size_t>(b * Hq + hq) * S + qi) * D;
 #pragma unroll
@@ -541,6 +567,35 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
     }
   }
   if (hf == 0) lse[static_cast<size_t>(b * Hq + hq) * S + qi] = (m_run + log2f(l_tot)) * kLn2;
+}
+
+// Key-split merge: row r's splits combine as m = max_s m_s, weights
+// w_s = 2^(m_s - m), O = sum_s w_s O_s / sum_s w_s l_s (splits in order, so
+// the result is deterministic), lse = (m + log2 l) ln 2.  One thread per 4
+// elements of a row.
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part,
+                                                         bf16_t* __restrict__ O, float* __restrict__ lse,
+                                                         int n_split, int64_t n_rows) {
+  constexpr int C4 = D / 4, REC = D + 4;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= n_rows * C4) return;
+  const int64_t row = idx / C4;
+  const int c4 = static_cast<int>(idx - row * C4);
+  const float* rec = part + row * n_split * REC;
+  float m = kNoMax;
+  for (int sp = 0; sp < n_split; ++sp) m = fmaxf(m, rec[sp * REC + D]);
+  float l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < n_split; ++sp) {
+    const float* r = rec + sp * REC;
+    const float w = fast_exp2(r[D] - m);
+    l = fmaf(w, r[D + 1], l);
+    acc += w * *reinterpret_cast<const f32x4*>(r + 4 * c4);
+  }
+  const float inv = 1.f / l;
+  *reinterpret_cast<bf16x4*>(O + row * D + 4 * c4) = to_bf16x4(acc * inv);
+  if (c4 == 0) lse[row] = (m + log2f(l)) * kLn2;
 }
 
 // fp32: one thread per (query head in group, query) row; 64 rows per wave.
@@ -621,6 +676,11 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(
 
 }  // namespace
 
+size_t attn_split_bytes(int B, int Hq, int S, int D) {
+  const int64_t rows = std::min<int64_t>(kSplitRows, static_cast<int64_t>(B) * Hq * S * kMaxKeySplits);
+  return static_cast<size_t>(rows) * (D + 4) * sizeof(float);
+}
+
 hipError_t launch_attn_fwd(const StepShape& sh, const AttnArgs& a, int dtype, hipStream_t st) {
   const int n_heads = sh.B * sh.Hkv;
   const int G = sh.Hq / sh.Hkv;
@@ -631,14 +691,22 @@ hipError_t launch_attn_fwd(const StepShape& sh, const AttnArgs& a, int dtype, hi
     const int n_rb = dec ? (G * sh.S + 31) / 32 : G * ((sh.S + 31) / 32);
     const int rbw = dec ? 2 : kRowBlocks;
     const int wgp = (n_rb + rbw - 1) / rbw;
-    const dim3 grid(n_heads * wgp), block(kFwdThreads);
+    // small grids split the keys of each row group over several workgroups
+    // (about one round of the CUs, at least 4 tiles each) and merge after
+    int n_split = 1;
+    if (!dec && a.part != nullptr && n_heads * wgp < 128) {
+      const int n_tiles_min = (sh.n_cache + 63) / 64 + 1;
+      n_split = std::min(kMaxKeySplits, std::min(256 / (n_heads * wgp), std::max(1, n_tiles_min / 4)));
+      while (n_split > 1 && static_cast<int64_t>(sh.B) * sh.Hq * sh.S * n_split > kSplitRows) --n_split;
+    }
+    const dim3 grid(n_heads * wgp * n_split), block(kFwdThreads);
 #define H2O_LAUNCH_FWD1(DD, DEC)                                                                    \
   hipLaunchKernelGGL(HIP_KERNEL_NAME(attn_fwd_bf16_kernel<DD, DEC>), grid, block, 0, st,            \
                      static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k_cache),        \
                      static_cast<const bf16_t*>(a.v_cache), a.pos,                                  \
                      static_cast<const bf16_t*>(a.k_new), static_cast<const bf16_t*>(a.v_new),      \
                      static_cast<bf16_t*>(a.out), a.lse, sh.Hq, sh.Hkv, sh.S, sh.M, sh.n_cache, c2, \
-                     n_heads, wgp)
+                     n_heads, wgp, n_split, a.part)
 #define H2O_LAUNCH_FWD(DD) \
   if (dec) H2O_LAUNCH_FWD1(DD, true); else H2O_LAUNCH_FWD1(DD, false)
     if (sh.D == 128) {
@@ -648,6 +716,18 @@ hipError_t launch_attn_fwd(const StepShape& sh, const AttnArgs& a, int dtype, hi
     }
 #undef H2O_LAUNCH_FWD
 #undef H2O_LAUNCH_FWD1
+    if (n_split > 1) {
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const int64_t n_rows = static_cast<int64_t>(sh.B) * sh.Hq * sh.S;
+      const unsigned blocks = static_cast<unsigned>((n_rows * (sh.D / 4) + 255) / 256);
+      if (sh.D == 128)
+        hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(blocks), dim3(256), 0, st, a.part,
+                           static_cast<bf16_t*>(a.out), a.lse, n_split, n_rows);
+      else
+        hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(blocks), dim3(256), 0, st, a.part,
+                           static_cast<bf16_t*>(a.out), a.lse, n_split, n_rows);
+    }
   } else {
     const int wgp = (G * sh.S + 63) / 64;
     const dim3 grid(n_heads * wgp), block(64);

@@ -25,7 +25,12 @@ struct AttnArgs {
   const void* v_new;
   void* out;
   float* lse;
+  float* part;      // key-split partial states (workspace; NULL: never split)
 };
+
+// rows of key-split partial state the attention may use (bounds its workspace)
+constexpr int64_t kSplitRows = 65536;
+size_t attn_split_bytes(int B, int Hq, int S, int D);
 
 struct ScoreArgs {
   const void* q;

@@ -106,6 +106,11 @@ WORKLOADS: dict[str, Workload] = {
         prefill=2048, chunk=16, total_len=2048 + 256 * 16, cache_slots=2048,
         recent_window=256, hh_frac=0.01,
         note="decode-like small chunks, 32 sequences, bandwidth-bound"),
+    "llama8b_64k_s128": Workload(
+        "llama8b_64k_s128", 6, batch=1, n_q_heads=32, n_kv_heads=8, head_dim=_D, dtype="bf16",
+        prefill=2048, chunk=128, total_len=65536, cache_slots=2048, recent_window=256,
+        hh_frac=0.01, qk_std=1.0 / math.sqrt(_D),
+        note="the 64k workload with 128-token chunks (the pages' S = 128 rows)"),
     "widegqa_128k": Workload(
         "widegqa_128k", 5, batch=1, n_q_heads=64, n_kv_heads=8, head_dim=_D, dtype="bf16",
         prefill=4096, chunk=2048, total_len=131072, cache_slots=8192, recent_window=512,

@@ -143,6 +143,13 @@ def test_llama8b_64k_sampled_steps():
     _run(w, 0, {0, 1, 31, 62}, [(0, 0), (0, 5)])
 
 
+def test_llama8b_64k_s128_sampled_steps():
+    """128-token chunks: the attention splits each row group's keys over 4
+    workgroups and merges them."""
+    w = wl.workload("llama8b_64k_s128")
+    _run(w, 0, {1, 2, 17, 250, 496}, [(0, 0), (0, 6)])
+
+
 def test_llama8b_128k_sampled_steps():
     w = wl.workload("llama8b_128k")
     _run(w, 0, {1, 2, 3, 64, 126}, [(0, 3)])

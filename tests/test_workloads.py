@@ -14,6 +14,8 @@ def test_named_workloads_shapes():
     assert c4.n_steps == 256 and c4.chunk == 16 and c4.batch == 32
     c5 = wl.WORKLOADS["widegqa_128k"]
     assert c5.n_steps == 62 and c5.group == 8
+    s128 = wl.WORKLOADS["llama8b_64k_s128"]
+    assert (s128.n_steps, s128.chunk, s128.group) == (496, 128, 4)
     c1 = wl.WORKLOADS["tiny"]
     assert c1.n_steps == 12 and c1.dtype == "fp32"
     for w in wl.WORKLOADS.values():
