@@ -349,39 +349,50 @@ __global__ __launch_bounds__(256, 1) void score_dec_kernel(
   const bf16_t* qhead = Q + static_cast<size_t>(b * Hq + kvh * G) * S * D;
   const float* lhead = lse + static_cast<size_t>(b * Hq + kvh * G) * S;
 
-  // the wave's key groups: keys base + 256 k + 64 wave + (0..63), k < NG
+  // the wave's key groups: keys base + 256 k + 64 wave + (0..63), k < NG;
+  // a key past the end reads the head's first chunk row (its column is
+  // never stored)
   auto load_keys = [&](int k, bf16x8 (&kf)[2][DS]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int v = base + 256 * k + 64 * wave + 32 * kb + col;
-      const bool ok = v < n_keys;
       const bf16_t* krow = v < n_cache ? kc_head + static_cast<size_t>(v) * D
-                                       : kn_head + static_cast<size_t>(ok ? v - n_cache : 0) * D;
+                                       : kn_head + static_cast<size_t>(v < n_keys ? v - n_cache : 0) * D;
 #pragma unroll
-      for (int st = 0; st < DS; ++st) {
-        const bf16x8 x = load_bf16x8(krow + 16 * st + 8 * hf);
-        kf[kb][st] = ok ? x : bf16x8{};
-      }
+      for (int st = 0; st < DS; ++st) kf[kb][st] = load_bf16x8(krow + 16 * st + 8 * hf);
     }
   };
-  bf16x8 kA[2][DS], kB[2][DS];
-  const int n_groups = min(NG, max(0, (n_keys - base - 64 * wave + 255) / 256));
-  if (n_groups > 0) load_keys(0, kA);
+  // kSets register sets in rotation: kSets - 1 groups are in flight while
+  // one is computed (a group's compute is shorter than a load's latency).
+  // Every wave walks all NG groups (a key past the end is computed and not
+  // stored), so the loads are unconditional and the waits exact.
+  constexpr int kSets = 3;
+  static_assert(NG % kSets == 0, "whole passes over the register sets");
+  bf16x8 kset[kSets][2][DS];
 
-  // the rows (zero past the end, lse +inf so that P = 0 there)
+  // the rows (zero past the end, lse +inf so that P = 0 there); loaded
+  // before the first key groups so that staging them waits for these only
+  u32x4 qx[NQ];
 #pragma unroll
   for (int c = 0; c < NQ; ++c) {
     const int idx = c * 256 + tid, row = idx / CPR, ch = idx % CPR;
-    const u32x4 x = load_u32x4(qhead + static_cast<size_t>(min(row, n_rows - 1)) * D + ch * 8);
+    qx[c] = load_u32x4(qhead + static_cast<size_t>(min(row, n_rows - 1)) * D + ch * 8);
+  }
+  const float l_in = tid < kRB ? lhead[min(tid, n_rows - 1)] : 0.f;
+#pragma unroll
+  for (int p0 = 0; p0 < kSets - 1; ++p0) load_keys(p0, kset[p0]);
+#pragma unroll
+  for (int c = 0; c < NQ; ++c) {
+    const int idx = c * 256 + tid, row = idx / CPR, ch = idx % CPR;
     const u32x4 z = {0, 0, 0, 0};
-    store_u32x4(qs + row * RBY + 16 * q_chunk<CPR>(row, ch), row < n_rows ? x : z);
+    store_u32x4(qs + row * RBY + 16 * q_chunk<CPR>(row, ch), row < n_rows ? qx[c] : z);
   }
   if (tid < kRB) {
     const bool ok = tid < n_rows;
-    s_l2[tid] = ok ? lhead[min(tid, n_rows - 1)] * kLog2e : __builtin_huge_valf();
+    s_l2[tid] = ok ? l_in * kLog2e : __builtin_huge_valf();
     s_qi[tid] = ok ? tid % S : -1;
   }
-  __syncthreads();
+  barrier_lds();
 
   uint32_t q_rd[DS];
 #pragma unroll
@@ -429,14 +440,14 @@ __global__ __launch_bounds__(256, 1) void score_dec_kernel(
       if (v1 < n_keys) out[v1 < n_cache ? v1 : M + j1] = t1;
     }
   };
-  // two register sets, alternating, so that the next group's loads are in
-  // flight during the current group's MFMAs
-  for (int k = 0; k < n_groups; k += 2) {
-    if (k + 1 < n_groups) load_keys(k + 1, kB);
-    group(k, kA);
-    if (k + 1 >= n_groups) break;
-    if (k + 2 < n_groups) load_keys(k + 2, kA);
-    group(k + 1, kB);
+  // the last pass reloads the last group into the sets it frees (unused)
+#pragma unroll 1
+  for (int k = 0; k < NG; k += kSets) {
+#pragma unroll
+    for (int u = 0; u < kSets; ++u) {
+      load_keys(min(k + u + kSets - 1, NG - 1), kset[(u + kSets - 1) % kSets]);
+      group(k + u, kset[u]);
+    }
   }
 }
 
