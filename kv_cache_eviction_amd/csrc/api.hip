@@ -156,10 +156,12 @@ h2o_status run_step(h2o_cache* c, const void* q, const void* k, const void* v, i
   int32_t* targets = reinterpret_cast<int32_t*>(c->ws + c->lay.targets_off);
   h2o::SelectArgs xa{c->k_cache, c->v_cache, c->scores, c->pos, k, v, partial, R, targets,
                      slots_out, pos_old, step_mass, k_old, v_old, status, static_cast<int32_t>(c->T)};
-  r = timed(c, 2, st, [&] { return h2o::launch_select(sh, xa, st); });
+  r = timed(c, 2, st, [&] { return h2o::launch_select(sh, xa, dtype, st); });
   if (r != H2O_OK) return r;
-  r = timed(c, 4, st, [&] { return h2o::launch_scatter(sh, xa, dtype, st); });
-  if (r != H2O_OK) return r;
+  if (!h2o::select_copies_rows(sh)) {
+    r = timed(c, 4, st, [&] { return h2o::launch_scatter(sh, xa, dtype, st); });
+    if (r != H2O_OK) return r;
+  }
   c->T += s;
   if (c->filled >= 0) c->filled = c->filled + s > c->cfg.cache_slots ? c->cfg.cache_slots : c->filled + s;
   return H2O_OK;

@@ -101,7 +101,8 @@ enum Dtype { kBF16 = 0, kFP32 = 1 };
 
 hipError_t launch_attn_fwd(const StepShape& sh, const AttnArgs& a, int dtype, hipStream_t st);
 hipError_t launch_score(const StepShape& sh, const ScoreArgs& a, int dtype, hipStream_t st);
-hipError_t launch_select(const StepShape& sh, const SelectArgs& a, hipStream_t st);
+hipError_t launch_select(const StepShape& sh, const SelectArgs& a, int dtype, hipStream_t st);
+bool select_copies_rows(const StepShape& sh);   // the select kernel also writes the K/V rows
 hipError_t launch_scatter(const StepShape& sh, const SelectArgs& a, int dtype, hipStream_t st);
 hipError_t launch_backward(const StepShape& sh, const BackwardArgs& a, hipStream_t st);
 size_t backward_workspace_bytes(int B, int Hq, int Hkv, int S, int D);

@@ -30,7 +30,8 @@
 //   3. writes scores, positions and the target list R (with a flag for
 //      targets that were free).
 // The scatter kernel then copies the chunk's K/V rows into their slots with
-// many workgroups per head (a pure bandwidth copy, 16-byte accesses).
+// many workgroups per head (a pure bandwidth copy, 16-byte accesses); chunks
+// of at most kSelectCopyRows tokens are copied by the select kernel itself.
 #include <type_traits>
 
 #include "h2o_device.h"
@@ -43,6 +44,10 @@ constexpr int kThreads = 512;
 constexpr int kWavesSel = kThreads / 64;
 constexpr int kMaxSplits = 8;  // upper bound of the score kernel's row splits
 constexpr int kMuRegs = 2;     // chunk keys per thread whose masses are prefetched
+// chunks up to this length copy their K/V rows inside the select kernel (one
+// workgroup per head keeps up with that little data, and a launch is saved);
+// longer chunks use the many-workgroup scatter kernel
+constexpr int kSelectCopyRows = 256;
 
 enum : uint8_t { kFree = 0, kCand = 1, kKeep = 2, kTarget = 4 };
 constexpr int32_t kWasFree = 0x40000000;   // flag bit of a target-list entry
@@ -118,7 +123,9 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     float* __restrict__ scores, int32_t* __restrict__ pos, const float* __restrict__ partial,
     int R, int32_t* __restrict__ targets, int32_t* __restrict__ slots_out,
     int32_t* __restrict__ pos_old, float* __restrict__ step_mass, int32_t* __restrict__ status, int T, int W, int S, int M,
-    int n_cache, int vec, int n_floor) {
+    int n_cache, int vec, int n_floor, char* __restrict__ kc, char* __restrict__ vc,
+    const char* __restrict__ kn, const char* __restrict__ vn, char* __restrict__ k_old,
+    char* __restrict__ v_old, int row_bytes) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   int* s_R = reinterpret_cast<int*>(smem);                 // [S]: target of chunk row j (flagged)
   __shared__ __attribute__((aligned(16))) uint32_t hist[3][kWavesSel / 2][256];   // per wave pair, 3 rotating
@@ -392,6 +399,30 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     for (int r = 0; r < kMaxSplits; ++r) mu += (r < R) ? part[r] : 0.f;
     write_target(jj, mu);
   }
+
+  // short chunks (row_bytes > 0): the chunk's K/V rows go to their targets
+  // here, as scatter_kernel would copy them (the target list is complete in
+  // LDS since the barrier after step 4; each slot has one writer)
+  if (row_bytes > 0) {
+    const int cpr = row_bytes >> 4;
+    for (int idx = tid; idx < S * cpr; idx += kThreads) {
+      const int jj = idx / cpr, c = idx - jj * cpr;
+      const int t = s_R[jj];
+      const int slot = t & ~kWasFree;
+      const size_t src = (static_cast<size_t>(bh) * S + jj) * row_bytes + 16 * c;
+      const size_t dst = (static_cast<size_t>(bh) * M + slot) * row_bytes + 16 * c;
+      const u32x4 kv = load_u32x4(kn + src);
+      const u32x4 vv = load_u32x4(vn + src);
+      if (k_old) {
+        const u32x4 z = {0, 0, 0, 0};
+        const bool was_free = (t & kWasFree) != 0;
+        store_u32x4(k_old + src, was_free ? z : load_u32x4(kc + dst));
+        store_u32x4(v_old + src, was_free ? z : load_u32x4(vc + dst));
+      }
+      store_u32x4(kc + dst, kv);
+      store_u32x4(vc + dst, vv);
+    }
+  }
 }
 
 // Copies chunk row j of every (b, KV head) into its target slot; the rows of
@@ -443,7 +474,10 @@ size_t select_lds_bytes(int M, int S) {
   return 4 * static_cast<size_t>(S) + 16;
 }
 
-hipError_t launch_select(const StepShape& sh, const SelectArgs& a, hipStream_t st) {
+bool select_copies_rows(const StepShape& sh) { return sh.S <= kSelectCopyRows; }
+
+hipError_t launch_select(const StepShape& sh, const SelectArgs& a, int dtype, hipStream_t st) {
+  const int row_bytes = select_copies_rows(sh) ? sh.D * (dtype == kBF16 ? 2 : 4) : 0;
   const int n_heads = sh.B * sh.Hkv;
   const size_t lds = select_lds_bytes(sh.M, sh.S);
   auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
@@ -456,7 +490,10 @@ hipError_t launch_select(const StepShape& sh, const SelectArgs& a, hipStream_t s
     }
     hipLaunchKernelGGL(kern, dim3(n_heads), dim3(kThreads), lds, st, a.scores, a.pos, a.partial, a.R,
                        a.targets, a.slots_out, a.pos_old, a.step_mass, a.status, a.T, sh.W, sh.S, sh.M, sh.n_cache,
-                       vec ? 1 : 0, sh.policy == 2 ? sh.n_sink : 0);
+                       vec ? 1 : 0, sh.policy == 2 ? sh.n_sink : 0, static_cast<char*>(a.k_cache),
+                       static_cast<char*>(a.v_cache), static_cast<const char*>(a.k_new),
+                       static_cast<const char*>(a.v_new), static_cast<char*>(a.k_old),
+                       static_cast<char*>(a.v_old), row_bytes);
     return hipGetLastError();
   };
   // slots per thread: the smallest power of two with 512 * SPT >= M (M <= 16384)
