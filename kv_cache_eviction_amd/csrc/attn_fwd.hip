@@ -78,7 +78,7 @@ __device__ __forceinline__ int v_chunk(int row, int c) {
   return c ^ ((row & 3) << (CPR == 16 ? 2 : 1));
 }
 
-template <int D, bool DEC>
+template <int D, bool DEC, bool SKIP>
 __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc,
     const bf16_t* __restrict__ Vc, const int32_t* __restrict__ pos,
@@ -165,6 +165,21 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   // by two so that LDS slot parities are compile-time); tiles past the end
   // are fully masked
   const int n_iter = ((n_tiles + 3) >> 2) << 1;
+  // SKIP (key-split launches, whose workgroups walk only a few tiles): local
+  // tile Tl needs no work from this wave when it is past the range (fully
+  // masked) or a chunk tile after the wave's last query (wave-uniform).
+  // The long-walk variant does not test: the branches cost its main loop more
+  // than the padding tiles they would save.
+  auto skip_tile = [&](int Tl) __attribute__((always_inline)) {
+    if constexpr (!SKIP) return false;
+    if (Tl >= n_tiles) return true;
+    if constexpr (DEC) {
+      return false;
+    } else {
+      const int Tg = T0 + Tl;
+      return Tg >= n_ct && (Tg - n_ct) * kKT > qb * 32 + 31;
+    }
+  };
 
   const bf16_t* kc_head = Kc + static_cast<size_t>(bh) * M * D;
   const bf16_t* vc_head = Vc + static_cast<size_t>(bh) * M * D;
@@ -434,18 +449,24 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
     issue_v(2 + GG, g, I1{});
     wait_vmem_all();
     barrier_lds();
-    qk(g, I0{}, sc0, sc1);
+    if (!skip_tile(GG)) qk(g, I0{}, sc0, sc1);
     barrier_lds();
     issue_k(4 + GG, g, I0{});
-    auto m_phase = [&](auto par) __attribute__((always_inline)) {
+    // S^T of tile tq (K slot PN) and O += P V of tile tp (V slot par)
+    auto m_phase = [&](auto par, int tq, int tp) __attribute__((always_inline)) {
       using PN = std::integral_constant<int, decltype(par)::value ^ 1>;
-      f32x16 sn0, sn1;
-      qk(g, PN{}, sn0, sn1);
-      pv(g, par, pb);
-      sc0 = sn0;
-      sc1 = sn1;
+      if (!skip_tile(tq)) {
+        f32x16 sn0, sn1;
+        qk(g, PN{}, sn0, sn1);
+        if (!skip_tile(tp)) pv(g, par, pb);
+        sc0 = sn0;
+        sc1 = sn1;
+      } else if (!skip_tile(tp)) {
+        pv(g, par, pb);
+      }
     };
     auto v_phase = [&](int T, int posv) __attribute__((always_inline)) {
+      if (skip_tile(T)) return;
       mask_and_check(sc0, sc1, tile_max(sc0, sc1), T, posv);
       softmax(sc0, sc1, pb);
     };
@@ -454,7 +475,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
       int pos_n = pos1;                 // position of tile t+1
       auto iteration = [&](int t, auto par) __attribute__((always_inline)) {
         using PN = std::integral_constant<int, decltype(par)::value ^ 1>;
-        m_phase(par);
+        m_phase(par, 2 * (t + 1), 2 * t);
         barrier_lds();
         const int pn = load_pos(2 * (t + 2));
         issue_k(2 * (t + 3), g, PN{});
@@ -475,7 +496,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
         v_phase(2 * t + 1, pos_c);
         __builtin_amdgcn_s_waitcnt(kWaitPrev);
         barrier_lds();
-        m_phase(par);
+        m_phase(par, 2 * (t + 1) + 1, 2 * t + 1);
         barrier_lds();
         pos_c = pos_n;
         pos_n = load_pos(2 * (t + 2) + 1);
@@ -700,15 +721,17 @@ hipError_t launch_attn_fwd(const StepShape& sh, const AttnArgs& a, int dtype, hi
       while (n_split > 1 && static_cast<int64_t>(sh.B) * sh.Hq * sh.S * n_split > kSplitRows) --n_split;
     }
     const dim3 grid(n_heads * wgp * n_split), block(kFwdThreads);
-#define H2O_LAUNCH_FWD1(DD, DEC)                                                                    \
-  hipLaunchKernelGGL(HIP_KERNEL_NAME(attn_fwd_bf16_kernel<DD, DEC>), grid, block, 0, st,            \
+#define H2O_LAUNCH_FWD1(DD, DEC, SK)                                                                \
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(attn_fwd_bf16_kernel<DD, DEC, SK>), grid, block, 0, st,        \
                      static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k_cache),        \
                      static_cast<const bf16_t*>(a.v_cache), a.pos,                                  \
                      static_cast<const bf16_t*>(a.k_new), static_cast<const bf16_t*>(a.v_new),      \
                      static_cast<bf16_t*>(a.out), a.lse, sh.Hq, sh.Hkv, sh.S, sh.M, sh.n_cache, c2, \
                      n_heads, wgp, n_split, a.part)
-#define H2O_LAUNCH_FWD(DD) \
-  if (dec) H2O_LAUNCH_FWD1(DD, true); else H2O_LAUNCH_FWD1(DD, false)
+#define H2O_LAUNCH_FWD(DD)                          \
+  if (dec) H2O_LAUNCH_FWD1(DD, true, false);        \
+  else if (n_split > 1) H2O_LAUNCH_FWD1(DD, false, true); \
+  else H2O_LAUNCH_FWD1(DD, false, false)
     if (sh.D == 128) {
       H2O_LAUNCH_FWD(128);
     } else {
