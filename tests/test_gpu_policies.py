@@ -5,7 +5,7 @@ the position array must match bit-exactly at every step; outputs use the
 forward's bounds (max |dO| <= 2e-2, rel-RMS <= 5e-3) and lse max abs 1e-3.
 No score is kept: the scores stay 0.  The S < 32 short-chunk path and
 d = 64 are covered as well as a chunk longer than 1024 (the select kernel's
-tail loop)."""
+tail loop), and the fp32 path."""
 from __future__ import annotations
 
 import math
@@ -30,6 +30,9 @@ CASES = {
     "sink_recent_short_s12": ("sink_recent", 8, dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128,
                                                      prefill=64, chunk=12, total_len=64 + 12 * 8,
                                                      cache_slots=96, recent_window=8, qk_std=1.0)),
+    "sink_recent_fp32_d64": ("sink_recent", 2, dict(batch=1, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                                                    dtype="fp32", prefill=64, chunk=32, total_len=64 + 32 * 6,
+                                                    cache_slots=96, recent_window=8, qk_std=1.0)),
     "recent_long_chunk_1100": ("recent", 0, dict(batch=1, n_q_heads=2, n_kv_heads=1, head_dim=128,
                                                  prefill=1200, chunk=1100, total_len=1200 + 1100 * 3,
                                                  cache_slots=2400, recent_window=100, qk_std=1.0)),
