@@ -45,6 +45,9 @@
  * Conventions for every call:
  *   - Buffer pointers are DEVICE pointers to contiguous, 16-byte aligned
  *     memory owned by the caller; the library never allocates device memory.
+ *     A non-NULL buffer pointer that is not 16-byte aligned is refused with
+ *     H2O_ERR_ALIGN before anything is enqueued (the kernels move 16-byte
+ *     pieces).
  *   - Element type of q/k/v/out/cache is the config's dtype (bf16 or fp32);
  *     scores, lse and masses are fp32; positions and slot ids are int32.
  *   - Layouts: q, out [B, Hq, S, d]; k, v [B, Hkv, S, d]; cache K, V
@@ -80,7 +83,8 @@ typedef enum {
   H2O_ERR_STATE = 4,       /* call not allowed in the current cache state        */
   H2O_ERR_WORKSPACE = 5,   /* workspace smaller than h2o_workspace_bytes()       */
   H2O_ERR_HIP = 6,         /* a HIP call failed; see h2o_last_hip_error()        */
-  H2O_ERR_UNSUPPORTED = 7  /* valid request the library does not implement       */
+  H2O_ERR_UNSUPPORTED = 7, /* valid request the library does not implement       */
+  H2O_ERR_ALIGN = 8        /* a buffer pointer is not 16-byte aligned            */
 } h2o_status;
 
 typedef enum { H2O_BF16 = 0, H2O_FP32 = 1 } h2o_dtype;

@@ -6,6 +6,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <initializer_list>
 #include <vector>
 
 #include "h2o.h"
@@ -17,6 +18,13 @@ constexpr int kTimedKernels = 5;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// true if some non-null pointer is not 16-byte aligned
+bool misaligned(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (reinterpret_cast<uintptr_t>(p) & 15u) return true;
+  return false;
+}
 
 struct Layout {
   size_t partial_off, partial_bytes;
@@ -213,6 +221,7 @@ const char* h2o_status_str(h2o_status s) {
     case H2O_ERR_WORKSPACE: return "workspace too small";
     case H2O_ERR_HIP: return "HIP error";
     case H2O_ERR_UNSUPPORTED: return "unsupported request";
+    case H2O_ERR_ALIGN: return "buffer pointer not 16-byte aligned";
   }
   return "unknown status";
 }
@@ -253,6 +262,7 @@ h2o_status h2o_cache_init(const h2o_config* cfg, void* k_cache, void* v_cache, f
                           int64_t tokens_seen, void* stream, h2o_cache** out) {
   if (!cfg || !k_cache || !v_cache || !scores || !positions || !workspace || !out) return H2O_ERR_NULL;
   *out = nullptr;
+  if (misaligned({k_cache, v_cache, scores, positions, workspace})) return H2O_ERR_ALIGN;
   h2o_status r = h2o_validate_config(cfg);
   if (r != H2O_OK) return r;
   if (tokens_seen < 0 || (!adopt && tokens_seen != 0) || tokens_seen > INT32_MAX) return H2O_ERR_STATE;
@@ -293,6 +303,7 @@ h2o_status h2o_cache_init(const h2o_config* cfg, void* k_cache, void* v_cache, f
 h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k, const void* v, int32_t n, void* out,
                        float* lse, void* stream) {
   if (!c || !q || !k || !v || !out) return H2O_ERR_NULL;
+  if (misaligned({q, k, v, out, lse})) return H2O_ERR_ALIGN;
   if (n < 1 || n > c->cfg.max_prefill) return H2O_ERR_SHAPE;
   if (c->T != 0) return H2O_ERR_STATE;
   return run_step(c, q, k, v, n, out, lse, nullptr, nullptr, nullptr, nullptr, nullptr,
@@ -304,6 +315,7 @@ h2o_status h2o_chunk_step(h2o_cache* c, const void* q, const void* k_new, const 
                           void* v_old, int32_t* pos_old, void* stream) {
   if (!c || !q || !k_new || !v_new || !out) return H2O_ERR_NULL;
   if ((k_old == nullptr) != (v_old == nullptr)) return H2O_ERR_NULL;
+  if (misaligned({q, k_new, v_new, out, lse, slots_out, step_mass, k_old, v_old, pos_old})) return H2O_ERR_ALIGN;
   if (step_mass && c->cfg.policy != H2O_POLICY_H2O) return H2O_ERR_UNSUPPORTED;
   if (s < 1 || s > c->cfg.max_chunk) return H2O_ERR_SHAPE;
   if (c->T + s > INT32_MAX) return H2O_ERR_STATE;
@@ -313,6 +325,7 @@ h2o_status h2o_chunk_step(h2o_cache* c, const void* q, const void* k_new, const 
 
 h2o_status h2o_get_scores(const h2o_cache* c, float* scores_out, int32_t* positions_out, void* stream) {
   if (!c || !scores_out) return H2O_ERR_NULL;
+  if (misaligned({scores_out, positions_out})) return H2O_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const size_t n = static_cast<size_t>(c->cfg.batch) * c->cfg.n_kv_heads * c->cfg.cache_slots;
   hipError_t e = hipMemcpyAsync(scores_out, c->scores, n * sizeof(float), hipMemcpyDeviceToDevice, st);
@@ -402,6 +415,9 @@ h2o_status h2o_chunk_backward(const h2o_config* cfg, const void* q, const void* 
   if (!cfg || !q || !k_cache || !v_cache || !positions || !k_new || !v_new || !out || !lse ||
       !d_out || !dq || !dk_cache || !dv_cache || !dk_new || !dv_new || !workspace)
     return H2O_ERR_NULL;
+  if (misaligned({q, k_cache, v_cache, positions, k_new, v_new, out, lse, d_out, dq, dk_cache, dv_cache,
+                  dk_new, dv_new, workspace}))
+    return H2O_ERR_ALIGN;
   h2o_status r = h2o_validate_config(cfg);
   if (r != H2O_OK) return r;
   if (cfg->dtype != H2O_BF16) return H2O_ERR_UNSUPPORTED;
@@ -430,6 +446,9 @@ h2o_status h2o_recurrence_backward_step(const h2o_config* cfg, void* k_cache, vo
   if (!cfg || !k_cache || !v_cache || !positions || !slots || !k_old || !v_old || !pos_old || !q ||
       !k_new || !v_new || !out || !lse || !d_out || !acc_k || !acc_v || !dq || !gk || !gv || !workspace)
     return H2O_ERR_NULL;
+  if (misaligned({k_cache, v_cache, positions, slots, k_old, v_old, pos_old, q, k_new, v_new, out, lse, d_out,
+                  acc_k, acc_v, dq, gk, gv, workspace}))
+    return H2O_ERR_ALIGN;
   h2o_status r = h2o_validate_config(cfg);
   if (r != H2O_OK) return r;
   if (cfg->dtype != H2O_BF16) return H2O_ERR_UNSUPPORTED;

@@ -22,7 +22,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libh2o.so")
 
 H2O_OK, H2O_ERR_NULL, H2O_ERR_CONFIG, H2O_ERR_SHAPE, H2O_ERR_STATE = 0, 1, 2, 3, 4
-H2O_ERR_WORKSPACE, H2O_ERR_HIP, H2O_ERR_UNSUPPORTED = 5, 6, 7
+H2O_ERR_WORKSPACE, H2O_ERR_HIP, H2O_ERR_UNSUPPORTED, H2O_ERR_ALIGN = 5, 6, 7, 8
 H2O_BF16, H2O_FP32 = 0, 1
 POLICIES = {"h2o": 0, "recent": 1, "sink_recent": 2}
 KERNEL_IDS = {"attn_fwd": 0, "score": 1, "select": 2, "reset": 3, "scatter": 4}
@@ -150,6 +150,8 @@ def _expect(t, name, shape, dtype, allow_none=False):
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if t.data_ptr() % 16:
+        raise ValueError(f"{name} must start at a 16-byte aligned address")
 
 
 def h2o_validate_config(cfg: H2OConfig) -> int:
@@ -174,8 +176,9 @@ def h2o_cache_init(cfg: H2OConfig, k_cache, v_cache, scores, positions, workspac
     _expect(v_cache, "v_cache", (B, Hkv, M, d), cfg.torch_dtype)
     _expect(scores, "scores", (B, Hkv, M), torch.float32)
     _expect(positions, "positions", (B, Hkv, M), torch.int32)
-    if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous uint8 device tensor")
+    if (workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous()
+            or workspace.data_ptr() % 16):
+        raise ValueError("workspace must be a contiguous, 16-byte aligned uint8 device tensor")
     c = cfg.c()
     handle = ctypes.c_void_p()
     _check(_lib.h2o_cache_init(ctypes.byref(c), _ptr(k_cache), _ptr(v_cache), _ptr(scores),

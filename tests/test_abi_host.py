@@ -83,7 +83,7 @@ def test_invalid_configs_are_rejected(kw):
 def test_null_config_and_status_strings():
     h2o = _lib_module()
     assert h2o._lib.h2o_validate_config(None) == h2o.H2O_ERR_NULL
-    for s in range(8):
+    for s in range(9):
         assert h2o.status_str(s) and h2o.status_str(s) != "unknown status"
     assert h2o.status_str(99) == "unknown status"
 
@@ -96,6 +96,34 @@ def test_null_handle_calls_fail_cleanly():
     assert h2o._lib.h2o_recurrence_backward_step(*([None] * 11), 4, *([None] * 9), 0, None) == h2o.H2O_ERR_NULL
     assert h2o._lib.h2o_tokens_seen(None) == -1
     assert h2o._lib.h2o_last_hip_error(None) == 0
+
+
+def test_misaligned_buffer_pointers_are_refused():
+    """A buffer pointer off a 16-byte boundary is refused on the host before
+    anything is enqueued (the fake addresses below are never dereferenced)."""
+    import ctypes
+    h2o = _lib_module()
+    c = _cfg().c()
+    good, bad = 0x10000, 0x10008
+    ws = h2o._lib.h2o_workspace_bytes(ctypes.byref(c))
+    for i in range(5):      # k_cache, v_cache, scores, positions, workspace
+        p = [good] * 5
+        p[i] = bad
+        out = ctypes.c_void_p(0x20000)
+        assert h2o._lib.h2o_cache_init(ctypes.byref(c), *p, ws, 0, 0, None,
+                                       ctypes.byref(out)) == h2o.H2O_ERR_ALIGN
+        assert out.value is None
+    for i in range(15):     # q .. v_new, then out .. workspace
+        p = [good] * 15
+        p[i] = bad
+        assert h2o._lib.h2o_chunk_backward(ctypes.byref(c), *p[:6], 64, *p[6:], 1 << 40,
+                                           None) == h2o.H2O_ERR_ALIGN
+    for i in range(19):     # k_cache .. v_new, then out .. workspace
+        p = [good] * 19
+        p[i] = bad
+        assert h2o._lib.h2o_recurrence_backward_step(ctypes.byref(c), *p[:10], 64, *p[10:], 1 << 40,
+                                                     None) == h2o.H2O_ERR_ALIGN
+    assert "aligned" in h2o.status_str(h2o.H2O_ERR_ALIGN)
 
 
 def test_position_policy_configs_validate():

@@ -271,6 +271,16 @@ def test_error_paths_leave_state_unchanged():
     rc = h2o._lib.h2o_chunk_step(cache.handle, None, None, None, 4, None, None, None, None, None, None, None,
                                  None)
     assert rc == h2o.H2O_ERR_NULL
+    # a query buffer 8 bytes off a 16-byte boundary: refused before any launch
+    flat = torch.empty(q1.numel() + 8, dtype=torch.bfloat16, device="cuda")
+    q_off = flat[4:4 + q1.numel()].view(q1.shape)
+    q_off.copy_(q1)
+    with pytest.raises(ValueError):
+        cache.chunk_step(q_off, k1, v1)
+    out = torch.empty_like(q1)
+    rc = h2o._lib.h2o_chunk_step(cache.handle, q_off.data_ptr(), k1.data_ptr(), v1.data_ptr(), w.chunk,
+                                 out.data_ptr(), None, None, None, None, None, None, None)
+    assert rc == h2o.H2O_ERR_ALIGN
     assert cache.tokens_seen == w.prefill
     cache.chunk_step(q1, k1, v1)
     assert cache.tokens_seen == w.prefill + w.chunk
