@@ -522,7 +522,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   wait_vmem_all();
   barrier_lds();
   constexpr int NX = kRowBlocks * 64;                     // exchange slots
-  float* xo = reinterpret_cast<float*>(k00);              // 16 x NX floats
+  constexpr int XR = TB / (NX * 4) < 16 ? TB / (NX * 4) : 16;   // O registers per round
+  static_assert(XR >= 1 && 16 % XR == 0 && 2 * NX * 4 <= TB, "exchange fits a K slot");
+  float* xo = reinterpret_cast<float*>(k00);              // XR x NX floats (one K slot)
   float* xm = reinterpret_cast<float*>(k01);              // m, l
   auto fold = [&](bool writer, bool reader, int slot) __attribute__((always_inline)) {
     if (writer) {
@@ -542,16 +544,19 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      if (writer) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) xo[r * NX + slot] = o[db][r];
-      }
-      barrier_lds();
-      if (reader) {
+      for (int r0 = 0; r0 < 16; r0 += XR) {
+        if (writer) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + xo[r * NX + slot] * a1;
+          for (int r = 0; r < XR; ++r) xo[r * NX + slot] = o[db][r0 + r];
+        }
+        barrier_lds();
+        if (reader) {
+#pragma unroll
+          for (int r = 0; r < XR; ++r) o[db][r0 + r] = o[db][r0 + r] * a0 + xo[r * NX + slot] * a1;
+        }
+        barrier_lds();
       }
-      barrier_lds();
     }
   };
   if constexpr (DEC) {
