@@ -31,6 +31,7 @@
 //     column adds of the current one, with one barrier per block.
 //   * Blocks where some query of the block precedes some key of the wave
 //     take a masked variant; all others no per-element test.
+#include <cstdint>
 #include <type_traits>
 
 #include "h2o_device.h"
@@ -512,17 +513,29 @@ int score_tiles(const StepShape& sh, int dtype) {
   return (sh.n_cache + ct - 1) / ct + (sh.S + ct - 1) / ct;
 }
 
+// Row splits R: a workgroup costs a start-up of about kStartBlocks block
+// times (K fragments, first copies) plus one block time per 64-row block
+// when it has its CU to itself, two per block beside a second resident
+// workgroup.  R minimises the start-ups of the rounds of 2 * kCUs workgroups
+// plus the blocks queued on the busiest CU (measured: the 64k shape's best
+// R is 5, 128-token chunks' 3).
 int score_row_splits(const StepShape& sh, int dtype) {
   if (dtype != kBF16) return 1;
-  const int n_heads = sh.B * sh.Hkv;
-  const int n_tiles = score_tiles(sh, dtype);
+  constexpr int kCUs = 256, kStartBlocks = 4;
+  const int64_t ht = static_cast<int64_t>(sh.B) * sh.Hkv * score_tiles(sh, dtype);
   const int n_blk = (sh.Hq / sh.Hkv * sh.S + kRB - 1) / kRB;
-  const int target = 512;   // two resident workgroups per CU
-  int R = target / (n_heads * n_tiles);
-  R = R < 1 ? 1 : R;
-  R = R > kRowSplitsMax ? kRowSplitsMax : R;
-  R = R > n_blk ? n_blk : R;
-  return R;
+  int best = 1;
+  int64_t best_cost = INT64_MAX;
+  for (int R = 1; R <= kRowSplitsMax && R <= n_blk; ++R) {
+    const int64_t n_wg = ht * R;
+    const int64_t cost = kStartBlocks * ((n_wg + 2 * kCUs - 1) / (2 * kCUs)) +
+                         static_cast<int64_t>((n_blk + R - 1) / R) * ((n_wg + kCUs - 1) / kCUs);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = R;
+    }
+  }
+  return best;
 }
 
 hipError_t launch_score(const StepShape& sh, const ScoreArgs& a, int dtype, hipStream_t st) {
