@@ -37,9 +37,8 @@ namespace {
 constexpr int kBKT = 64;     // keys per LDS tile (dq kernel)
 constexpr int kBWaves = 8;     // row blocks (waves) per dQ workgroup
 
-__device__ __forceinline__ int bkrow_of_key(int k) {
-  return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3);
-}
+// LDS row r of a 32-key block holds key key_of_bkrow(r) (MFMA A-operand row
+// order: row 8q + 4h + r' holds key 16h + 4q + r').
 __device__ __forceinline__ int key_of_bkrow(int r) {
   return ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3);
 }

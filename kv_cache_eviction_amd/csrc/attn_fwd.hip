@@ -59,15 +59,10 @@ constexpr int kFwdThreads = 512;
 constexpr float kRescaleSlack = 8.f;   // log2 headroom before the running maximum must move
 constexpr float kNoMax = -1e30f;       // running maximum of a query that has seen no key yet
 
-// Key k (0..31) of a 32-key block -> LDS row = MFMA A-operand row that reads
-// it.  Row 8q + 4h + r holds key 16h + 4q + r, so that accumulator register
-// r' of lane l corresponds to key 16(l/32) + r'.
-__device__ __forceinline__ int krow_of_key(int k) {
-  return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3);
-}
-__device__ __forceinline__ int key_of_krow(int r) {
-  return ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3);
-}
+// K rows of a 32-key block sit in LDS in MFMA A-operand row order: row
+// 8q + 4h + r holds key 16h + 4q + r, so that accumulator register r' of
+// lane l corresponds to key 16(l/32) + r'.  The tile copies below apply this
+// permutation on the source side (their per-lane and scalar offsets).
 
 // Swizzled 16-byte chunk of a K row / V row (CPR chunks per row); both maps
 // are involutions in the chunk index.

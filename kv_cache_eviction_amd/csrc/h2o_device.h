@@ -95,8 +95,4 @@ __device__ __forceinline__ f32x16 zero16() {
 // Value of lane (l ^ 32): the other half of a 32x32 MFMA accumulator column.
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32); }
 
-__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
-  return __uint_as_float(static_cast<uint32_t>(b) << 16);
-}
-
 }  // namespace h2o
