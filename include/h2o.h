@@ -261,8 +261,9 @@ H2O_API h2o_status h2o_device_status(h2o_cache* c, void* stream, int32_t* flags)
  * accumulation, 2 eviction select, 3 state reset, 4 K/V scatter.  Each
  * bracketed launch adds two event records to the stream, so select only
  * the kernels of interest when the step time matters.  h2o_get_timing
- * synchronises on the last recorded event and returns the summed
- * milliseconds and launch count since timing was enabled. */
+ * synchronises on the recorded events and returns the milliseconds and the
+ * launch count of kernel_id summed over every bracketed launch since the
+ * handle was created (H2O_ERR_SHAPE for an id outside 0..4). */
 H2O_API h2o_status h2o_set_timing(h2o_cache* c, int32_t kernel_mask);
 H2O_API h2o_status h2o_get_timing(h2o_cache* c, int32_t kernel_id, double* total_ms,
                           int64_t* launches);

@@ -286,6 +286,32 @@ def test_error_paths_leave_state_unchanged():
     assert cache.tokens_seen == w.prefill + w.chunk
 
 
+def test_scores_snapshot_and_timing_counters():
+    """h2o_get_scores copies the live scores and positions; the event timing
+    counts exactly the launches of the selected kernels."""
+    h2o = h2o_mod()
+    w = wl.workload("llama8b_64k", **SMALL_BF16["g4_d128_ragged"])
+    cache = h2o.H2OCache(cfg_of(w))
+    h2o.h2o_set_timing(cache.handle, ["attn_fwd", "select"])
+    steps = 4
+    for c in range(steps):
+        q, k, v = (to_device(x) for x in wl.chunk_inputs(w, 2, c))
+        if c == 0:
+            cache.prefill(q, k, v)
+        else:
+            cache.chunk_step(q, k, v)
+    sc, ps = cache.get_scores()
+    torch.cuda.synchronize()
+    assert torch.equal(sc, cache.scores) and torch.equal(ps, cache.positions)
+    for name in ("attn_fwd", "select"):
+        ms, n = h2o.h2o_get_timing(cache.handle, name)
+        assert n == steps and ms > 0, (name, ms, n)
+    assert h2o.h2o_get_timing(cache.handle, "score") == (0.0, 0)
+    with pytest.raises(h2o.H2OError) as e:
+        h2o.h2o_get_timing(cache.handle, 7)
+    assert e.value.status == h2o.H2O_ERR_SHAPE
+
+
 def test_infeasible_adopted_state_sets_device_status():
     h2o = h2o_mod()
     B, Hq, Hkv, d, M, S, W = 1, 2, 1, 64, 64, 16, 8
