@@ -136,8 +136,12 @@ H2O_API size_t h2o_workspace_bytes(const h2o_config* cfg);
  *   patterns in unused memory from reaching any output only if the values
  *   themselves are finite.
  * The workspace counters are cleared on `stream` in both cases.
- * Errors: H2O_ERR_NULL, H2O_ERR_CONFIG, H2O_ERR_WORKSPACE, H2O_ERR_STATE
- * (adopt = 0 with tokens_seen != 0, or tokens_seen < 0), H2O_ERR_HIP. */
+ * The handle belongs to the device current at this call: its compute-unit
+ * count sizes the grids of small steps, and every later call on the handle
+ * must run with that device current.
+ * Errors: H2O_ERR_NULL, H2O_ERR_ALIGN, H2O_ERR_CONFIG, H2O_ERR_WORKSPACE,
+ * H2O_ERR_STATE (adopt = 0 with tokens_seen != 0, or tokens_seen < 0),
+ * H2O_ERR_HIP (also when the device cannot be queried). */
 H2O_API h2o_status h2o_cache_init(const h2o_config* cfg, void* k_cache, void* v_cache,
                           float* scores, int32_t* positions, void* workspace,
                           size_t workspace_bytes, int32_t adopt,

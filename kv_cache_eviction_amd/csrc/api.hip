@@ -74,6 +74,7 @@ struct h2o_cache {
   Layout lay;
   int64_t T;
   int filled;          // slots [0, filled) hold tokens, the rest are free; -1: unknown (adopted)
+  int n_cu;            // compute units of the device current at h2o_cache_init
   int32_t last_hip_error;
   uint32_t timing_mask;      // bit k: bracket kernel id k with events
   std::vector<TimedLaunch> pending;
@@ -138,6 +139,7 @@ h2o::StepShape shape_of(const h2o_cache* c, int s) {
   sh.scale = g.softmax_scale > 0.f ? g.softmax_scale : 1.0f / sqrtf(static_cast<float>(g.head_dim));
   sh.policy = g.policy;
   sh.n_sink = g.n_sink;
+  sh.n_cu = c->n_cu;
   return sh;
 }
 
@@ -268,7 +270,12 @@ h2o_status h2o_cache_init(const h2o_config* cfg, void* k_cache, void* v_cache, f
   if (tokens_seen < 0 || (!adopt && tokens_seen != 0) || tokens_seen > INT32_MAX) return H2O_ERR_STATE;
   const Layout lay = layout_of(cfg);
   if (workspace_bytes < lay.total) return H2O_ERR_WORKSPACE;
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
+    return H2O_ERR_HIP;
   h2o_cache* c = new h2o_cache();
+  c->n_cu = n_cu;
   c->cfg = *cfg;
   c->k_cache = k_cache;
   c->v_cache = v_cache;

@@ -712,12 +712,13 @@ hipError_t launch_attn_fwd(const StepShape& sh, const AttnArgs& a, int dtype, hi
     const int n_rb = dec ? (G * sh.S + 31) / 32 : G * ((sh.S + 31) / 32);
     const int rbw = dec ? 2 : kRowBlocks;
     const int wgp = (n_rb + rbw - 1) / rbw;
-    // small grids split the keys of each row group over several workgroups
-    // (about one round of the CUs, at least 4 tiles each) and merge after
+    // small grids (under half the CUs) split the keys of each row group over
+    // several workgroups (about one round of the CUs, at least 4 tiles each)
+    // and merge after
     int n_split = 1;
-    if (!dec && a.part != nullptr && n_heads * wgp < 128) {
+    if (!dec && a.part != nullptr && 2 * n_heads * wgp < sh.n_cu) {
       const int n_tiles_min = (sh.n_cache + 63) / 64 + 1;
-      n_split = std::min(kMaxKeySplits, std::min(256 / (n_heads * wgp), std::max(1, n_tiles_min / 4)));
+      n_split = std::min(kMaxKeySplits, std::min(sh.n_cu / (n_heads * wgp), std::max(1, n_tiles_min / 4)));
       while (n_split > 1 && static_cast<int64_t>(sh.B) * sh.Hq * sh.S * n_split > kSplitRows) --n_split;
     }
     const dim3 grid(n_heads * wgp * n_split), block(kFwdThreads);

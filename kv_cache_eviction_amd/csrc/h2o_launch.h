@@ -14,6 +14,7 @@ struct StepShape {
   float scale;      // softmax scale applied to q.k
   int policy = 0;   // 0 H2O (score key), 1 recent, 2 sink_recent (position key)
   int n_sink = 0;   // sink_recent: positions below n_sink are never evicted
+  int n_cu = 256;   // compute units of the device (sizes the grids of small steps)
 };
 
 struct AttnArgs {

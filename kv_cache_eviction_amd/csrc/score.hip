@@ -516,20 +516,21 @@ int score_tiles(const StepShape& sh, int dtype) {
 // Row splits R: a workgroup costs a start-up of about kStartBlocks block
 // times (K fragments, first copies) plus one block time per 64-row block
 // when it has its CU to itself, two per block beside a second resident
-// workgroup.  R minimises the start-ups of the rounds of 2 * kCUs workgroups
-// plus the blocks queued on the busiest CU (measured: the 64k shape's best
-// R is 5, 128-token chunks' 3).
+// workgroup.  R minimises the start-ups of the rounds of two workgroups per
+// CU plus the blocks queued on the busiest CU (measured on 256 CUs: the 64k
+// shape's best R is 5, 128-token chunks' 3).
 int score_row_splits(const StepShape& sh, int dtype) {
   if (dtype != kBF16) return 1;
-  constexpr int kCUs = 256, kStartBlocks = 4;
+  constexpr int kStartBlocks = 4;
+  const int64_t n_cu = sh.n_cu;
   const int64_t ht = static_cast<int64_t>(sh.B) * sh.Hkv * score_tiles(sh, dtype);
   const int n_blk = (sh.Hq / sh.Hkv * sh.S + kRB - 1) / kRB;
   int best = 1;
   int64_t best_cost = INT64_MAX;
   for (int R = 1; R <= kRowSplitsMax && R <= n_blk; ++R) {
     const int64_t n_wg = ht * R;
-    const int64_t cost = kStartBlocks * ((n_wg + 2 * kCUs - 1) / (2 * kCUs)) +
-                         static_cast<int64_t>((n_blk + R - 1) / R) * ((n_wg + kCUs - 1) / kCUs);
+    const int64_t cost = kStartBlocks * ((n_wg + 2 * n_cu - 1) / (2 * n_cu)) +
+                         static_cast<int64_t>((n_blk + R - 1) / R) * ((n_wg + n_cu - 1) / n_cu);
     if (cost < best_cost) {
       best_cost = cost;
       best = R;
