@@ -150,7 +150,7 @@ H2O_API h2o_status h2o_cache_init(const h2o_config* cfg, void* k_cache, void* v_
 /* The prefill chunk of length n = N_C (LHF Fig. 1(a)): causal attention over
  * the chunk, then its K/V written to slots 0..n-1 with their masses as scores.
  * q [B,Hq,n,d]; k, v [B,Hkv,n,d]; out [B,Hq,n,d]; lse [B,Hq,n] or NULL.
- * Errors: H2O_ERR_NULL; H2O_ERR_SHAPE unless 1 <= n <= max_prefill;
+ * Errors: H2O_ERR_NULL, H2O_ERR_ALIGN; H2O_ERR_SHAPE unless 1 <= n <= max_prefill;
  * H2O_ERR_STATE unless the handle has seen no token yet. */
 H2O_API h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k,
                        const void* v, int32_t n, void* out, float* lse,
@@ -168,7 +168,7 @@ H2O_API h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k,
  *   pos_old [B,Hkv,s] int32: the position slot R_j held before the step (-1
  *     where a free slot was filled).  slots_out, k_old/v_old and pos_old
  *     together let h2o_recurrence_backward_step undo the step.
- * Errors: H2O_ERR_NULL; H2O_ERR_SHAPE unless 1 <= s <= max_chunk.
+ * Errors: H2O_ERR_NULL, H2O_ERR_ALIGN; H2O_ERR_SHAPE unless 1 <= s <= max_chunk.
  * If a state adopted through h2o_cache_init has fewer evictable slots than
  * the step needs, no slot of that (b, head) is written (K/V and positions
  * unchanged; its scores have received the step's mass) and bit 0 of the
@@ -180,7 +180,7 @@ H2O_API h2o_status h2o_chunk_step(h2o_cache* c, const void* q, const void* k_new
 
 /* Enqueues device-to-device copies of the scores [B,Hkv,M] into scores_out
  * and, if positions_out != NULL, of the positions.  Errors: H2O_ERR_NULL,
- * H2O_ERR_HIP. */
+ * H2O_ERR_ALIGN, H2O_ERR_HIP. */
 H2O_API h2o_status h2o_get_scores(const h2o_cache* c, float* scores_out,
                           int32_t* positions_out, void* stream);
 
@@ -196,7 +196,7 @@ H2O_API h2o_status h2o_get_scores(const h2o_cache* c, float* scores_out,
  * dK/dV of a KV head sum over the G query heads of its group.
  * workspace >= h2o_backward_workspace_bytes(cfg, s) (holds dO . O per row and
  * the fp32 partial dK/dV of the chunk keys; contents need no initialisation).
- * Deterministic (no atomics).  Errors: H2O_ERR_NULL, H2O_ERR_CONFIG,
+ * Deterministic (no atomics).  Errors: H2O_ERR_NULL, H2O_ERR_ALIGN, H2O_ERR_CONFIG,
  * H2O_ERR_UNSUPPORTED (fp32 configs), H2O_ERR_SHAPE (s < 1 or s larger than
  * max(max_chunk, max_prefill)), H2O_ERR_WORKSPACE, H2O_ERR_HIP. */
 H2O_API h2o_status h2o_chunk_backward(const h2o_config* cfg, const void* q,
@@ -238,9 +238,9 @@ H2O_API size_t h2o_backward_workspace_bytes(const h2o_config* cfg, int32_t s);
  * A slot index outside [0, M) (a step that wrote nothing for that head) is
  *   skipped by the undo and the routing.
  * workspace >= h2o_recurrence_workspace_bytes(cfg, s).  Deterministic.
- * Errors: H2O_ERR_NULL, H2O_ERR_CONFIG, H2O_ERR_UNSUPPORTED (fp32 configs),
- * H2O_ERR_SHAPE (s < 1 or s larger than max(max_chunk, max_prefill)),
- * H2O_ERR_WORKSPACE, H2O_ERR_HIP. */
+ * Errors: H2O_ERR_NULL, H2O_ERR_ALIGN, H2O_ERR_CONFIG, H2O_ERR_UNSUPPORTED
+ * (fp32 configs), H2O_ERR_SHAPE (s < 1 or s larger than max(max_chunk,
+ * max_prefill)), H2O_ERR_WORKSPACE, H2O_ERR_HIP. */
 H2O_API h2o_status h2o_recurrence_backward_step(
     const h2o_config* cfg, void* k_cache, void* v_cache, int32_t* positions,
     const int32_t* slots, const void* k_old, const void* v_old, const int32_t* pos_old,
