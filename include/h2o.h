@@ -151,7 +151,7 @@ H2O_API h2o_status h2o_cache_init(const h2o_config* cfg, void* k_cache, void* v_
  * the chunk, then its K/V written to slots 0..n-1 with their masses as scores.
  * q [B,Hq,n,d]; k, v [B,Hkv,n,d]; out [B,Hq,n,d]; lse [B,Hq,n] or NULL.
  * Errors: H2O_ERR_NULL, H2O_ERR_ALIGN; H2O_ERR_SHAPE unless 1 <= n <= max_prefill;
- * H2O_ERR_STATE unless the handle has seen no token yet. */
+ * H2O_ERR_STATE unless the handle has seen no token yet; H2O_ERR_HIP. */
 H2O_API h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k,
                        const void* v, int32_t n, void* out, float* lse,
                        void* stream);
@@ -168,7 +168,10 @@ H2O_API h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k,
  *   pos_old [B,Hkv,s] int32: the position slot R_j held before the step (-1
  *     where a free slot was filled).  slots_out, k_old/v_old and pos_old
  *     together let h2o_recurrence_backward_step undo the step.
- * Errors: H2O_ERR_NULL, H2O_ERR_ALIGN; H2O_ERR_SHAPE unless 1 <= s <= max_chunk.
+ * Errors: H2O_ERR_NULL (also one of k_old, v_old without the other),
+ * H2O_ERR_ALIGN, H2O_ERR_UNSUPPORTED (step_mass with a position policy),
+ * H2O_ERR_SHAPE unless 1 <= s <= max_chunk, H2O_ERR_STATE (tokens seen would
+ * pass 2^31 - 1), H2O_ERR_HIP.
  * If a state adopted through h2o_cache_init has fewer evictable slots than
  * the step needs, no slot of that (b, head) is written (K/V and positions
  * unchanged; its scores have received the step's mass) and bit 0 of the
