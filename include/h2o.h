@@ -55,7 +55,10 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
  *     enqueued; no call synchronises the device except where stated.
  *   - Arguments are validated on the host before anything is enqueued; on
- *     any error nothing is enqueued and the cache state is unchanged.
+ *     every error but H2O_ERR_HIP nothing is enqueued and the cache state is
+ *     unchanged.  H2O_ERR_HIP means a launch failed part-way through a call:
+ *     kernels enqueued before it may have updated the state, so the handle
+ *     should be destroyed (a snapshot taken earlier can be adopted again).
  *   - A handle is not thread-safe; calls on one handle must be issued in
  *     order on one stream.
  */
