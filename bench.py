@@ -24,7 +24,7 @@ With --policy recent | sink_recent (--n-sink N): the same step under a
 position eviction policy (no score pass; the oldest unprotected tokens go).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--recurrence]
-                       [--policy h2o|recent|sink_recent] [--n-sink N]
+                       [--policy h2o|recent|sink_recent] [--n-sink N] [--no-cpu-baseline]
        python bench.py --copy-probe MB    (plain copy of known size, for
                                            scaling the HBM byte counters)
 """
