@@ -178,7 +178,10 @@ H2O_API h2o_status h2o_prefill(h2o_cache* c, const void* q, const void* k,
  * If a state adopted through h2o_cache_init has fewer evictable slots than
  * the step needs, no slot of that (b, head) is written (K/V and positions
  * unchanged; its scores have received the step's mass) and bit 0 of the
- * device status word is set (see h2o_device_status). */
+ * device status word is set (see h2o_device_status).  The optional outputs
+ * of that head are still all written: slots_out and pos_old -1 (a slot
+ * outside [0, M), which h2o_recurrence_backward_step skips), k_old/v_old
+ * zero, step_mass the masses the step computed. */
 H2O_API h2o_status h2o_chunk_step(h2o_cache* c, const void* q, const void* k_new,
                           const void* v_new, int32_t s, void* out, float* lse,
                           int32_t* slots_out, float* step_mass, void* k_old,
@@ -228,13 +231,16 @@ H2O_API size_t h2o_backward_workspace_bytes(const h2o_config* cfg, int32_t s);
  *   1. undoes the step on the cache: rows slots[b,h,j] of k_cache/v_cache get
  *      k_old/v_old[b,h,j] and their positions pos_old[b,h,j] (the delta that
  *      h2o_chunk_step exported), leaving the cache as step c saw it;
- *   2. runs the frozen-eviction backward of the step on that cache (as
- *      h2o_chunk_backward): dq [B,Hq,s,d] (dtype) is the step's query
- *      gradient, and the cache gradient dK_c, dV_c is kept in the workspace;
- *   3. routes: for token j written to slot m = slots[b,h,j],
- *      gk[b,h,j] = dk_new[b,h,j] + acc_k[b,h,m] (fp32 [B,Hkv,s,d]: the
- *      token key's total gradient), then acc_k[b,h,m] = 0, and for every
- *      slot acc_k += dK_c; the same for v.
+ *   2. routes what later steps owe the step's tokens: for token j written
+ *      to slot m = slots[b,h,j], gk[b,h,j] = acc_k[b,h,m], then
+ *      acc_k[b,h,m] = 0 (the same for v);
+ *   3. runs the frozen-eviction backward of the step on that cache (as
+ *      h2o_chunk_backward) in fp32 accumulating form: dq [B,Hq,s,d] (dtype)
+ *      is the step's query gradient, the cache gradient is added to every
+ *      filled slot (acc_k += dK_c, acc_v += dV_c) and the chunk keys' own
+ *      gradient to gk, gv (fp32 [B,Hkv,s,d]), which end as each token's
+ *      total key/value gradient.  No gradient is rounded on its way
+ *      through the walk.
  * acc_k, acc_v: fp32 [B,Hkv,M,d], zero before the last step's call, carried
  *   between the calls (each slot holds the gradient owed to its occupant).
  * The prefill is undone as a step whose slots are 0..n-1 of every head,
@@ -243,7 +249,8 @@ H2O_API size_t h2o_backward_workspace_bytes(const h2o_config* cfg, int32_t s);
  *   outputs and the output gradient, as for h2o_chunk_backward.
  * A slot index outside [0, M) (a step that wrote nothing for that head) is
  *   skipped by the undo and the routing.
- * workspace >= h2o_recurrence_workspace_bytes(cfg, s).  Deterministic.
+ * workspace >= h2o_recurrence_workspace_bytes(cfg, s) (the backward's:
+ *   h2o_backward_workspace_bytes).  Deterministic.
  * Errors: H2O_ERR_NULL, H2O_ERR_ALIGN, H2O_ERR_CONFIG, H2O_ERR_UNSUPPORTED
  * (fp32 configs), H2O_ERR_SHAPE (s < 1 or s larger than max(max_chunk,
  * max_prefill)), H2O_ERR_WORKSPACE, H2O_ERR_HIP. */

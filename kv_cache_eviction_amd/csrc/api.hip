@@ -191,22 +191,10 @@ h2o::StepShape backward_shape(const h2o_config* cfg, int32_t s) {
   return sh;
 }
 
-// recurrence step workspace: the backward's, then its bf16 outputs dK/dV of
-// the cache and dk/dv of the chunk
-struct RecLayout {
-  size_t bwd, dkc, dvc, dkn, dvn, total;
-};
-RecLayout rec_layout(const h2o_config* cfg, int32_t s) {
-  const size_t cache_rows = static_cast<size_t>(cfg->batch) * cfg->n_kv_heads * cfg->cache_slots * cfg->head_dim * 2;
-  const size_t new_rows = static_cast<size_t>(cfg->batch) * cfg->n_kv_heads * s * cfg->head_dim * 2;
-  RecLayout l;
-  l.bwd = 0;
-  l.dkc = align_up(h2o::backward_workspace_bytes(cfg->batch, cfg->n_q_heads, cfg->n_kv_heads, s, cfg->head_dim));
-  l.dvc = l.dkc + align_up(cache_rows);
-  l.dkn = l.dvc + align_up(cache_rows);
-  l.dvn = l.dkn + align_up(new_rows);
-  l.total = l.dvn + align_up(new_rows);
-  return l;
+// recurrence step workspace: the backward's (the walk's gradients go
+// straight into the caller's fp32 accumulators)
+size_t rec_workspace_bytes(const h2o_config* cfg, int32_t s) {
+  return h2o::backward_workspace_bytes(cfg->batch, cfg->n_q_heads, cfg->n_kv_heads, s, cfg->head_dim);
 }
 
 }  // namespace
@@ -440,7 +428,7 @@ h2o_status h2o_chunk_backward(const h2o_config* cfg, const void* q, const void* 
 
 size_t h2o_recurrence_workspace_bytes(const h2o_config* cfg, int32_t s) {
   if (h2o_validate_config(cfg) != H2O_OK || s < 1) return 0;
-  return rec_layout(cfg, s).total;
+  return rec_workspace_bytes(cfg, s);
 }
 
 h2o_status h2o_recurrence_backward_step(const h2o_config* cfg, void* k_cache, void* v_cache,
@@ -460,20 +448,15 @@ h2o_status h2o_recurrence_backward_step(const h2o_config* cfg, void* k_cache, vo
   if (r != H2O_OK) return r;
   if (cfg->dtype != H2O_BF16) return H2O_ERR_UNSUPPORTED;
   if (s < 1 || s > max_len(cfg)) return H2O_ERR_SHAPE;
-  const RecLayout l = rec_layout(cfg, s);
-  if (workspace_bytes < l.total) return H2O_ERR_WORKSPACE;
+  if (workspace_bytes < rec_workspace_bytes(cfg, s)) return H2O_ERR_WORKSPACE;
   const h2o::StepShape sh = backward_shape(cfg, s);
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  h2o::RecurrenceArgs ra{k_cache, v_cache, positions, slots, k_old, v_old, pos_old,
-                         ws + l.dkc, ws + l.dvc, ws + l.dkn, ws + l.dvn, acc_k, acc_v, gk, gv};
-  hipError_t e = h2o::launch_undo_step(sh, ra, cfg->dtype, st);
+  h2o::RecurrenceArgs ra{k_cache, v_cache, positions, slots, k_old, v_old, pos_old, acc_k, acc_v, gk, gv};
+  hipError_t e = h2o::launch_undo_gather(sh, ra, cfg->dtype, st);
   if (e != hipSuccess) return H2O_ERR_HIP;
   h2o::BackwardArgs a{q, k_cache, v_cache, positions, k_new, v_new, out, lse, d_out,
-                      dq, ws + l.dkc, ws + l.dvc, ws + l.dkn, ws + l.dvn, ws + l.bwd};
+                      dq, acc_k, acc_v, gk, gv, workspace, true};
   e = h2o::launch_backward(sh, a, st);
-  if (e != hipSuccess) return H2O_ERR_HIP;
-  e = h2o::launch_route(sh, ra, st);
   return e == hipSuccess ? H2O_OK : H2O_ERR_HIP;
 }
 

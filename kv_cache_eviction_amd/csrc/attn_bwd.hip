@@ -277,12 +277,14 @@ constexpr int kPieces = 4;
 // fold their dK/dV at the end.  The workgroup's K and V rows sit in LDS and
 // are read as the B operands of every block, so a wave holds only its dK/dV
 // accumulators and the block in flight: two waves fit on each SIMD.
-template <int D>
+// ACC: the cache tiles add their (scaled) dK/dV into fp32 accumulators
+// [B*Hkv][M][d] instead of writing bf16 rows; a free slot adds nothing.
+template <int D, bool ACC>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
     const int32_t* __restrict__ pos, const bf16_t* __restrict__ Kn, const bf16_t* __restrict__ Vn,
     const bf16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dws,
-    bf16_t* __restrict__ dKc, bf16_t* __restrict__ dVc, float* __restrict__ part, int Hq,
+    void* __restrict__ dKc, void* __restrict__ dVc, float* __restrict__ part, int Hq,
     int Hkv, int S, int M, float c2, float scale, int n_heads, int n_ct, int n_cht) {
   constexpr int DS = D / 16, DB = D / 32, CPR = D / 8;
   constexpr int RB = 2 * D;                        // bytes per row
@@ -547,6 +549,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     }
   }
   if (rs == 1 || key >= lim) return;
+  if (ACC && is_cache && !key_ok) return;          // a free slot's accumulator is left as it is
   if (!key_ok) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -555,9 +558,25 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     }
   }
   // accumulator register r of lane l: d = 32 db + 8(r/4) + 4(l/32) + r%4, key column l%32
-  if (is_cache) {
-    bf16_t* ko = dKc + (static_cast<size_t>(bh) * M + key) * D;
-    bf16_t* vo = dVc + (static_cast<size_t>(bh) * M + key) * D;
+  if (ACC && is_cache) {
+    // each slot belongs to one workgroup: a plain read-modify-write
+    float* ko = static_cast<float*>(dKc) + (static_cast<size_t>(bh) * M + key) * D;
+    float* vo = static_cast<float*>(dVc) + (static_cast<size_t>(bh) * M + key) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        f32x4* kp = reinterpret_cast<f32x4*>(ko + db * 32 + 8 * a + 4 * hf);
+        f32x4* vp = reinterpret_cast<f32x4*>(vo + db * 32 + 8 * a + 4 * hf);
+        const f32x4 kold = *kp, vold = *vp;
+        *kp = kold + f32x4{dk[db][4 * a] * scale, dk[db][4 * a + 1] * scale, dk[db][4 * a + 2] * scale,
+                           dk[db][4 * a + 3] * scale};
+        *vp = vold + f32x4{dv[db][4 * a], dv[db][4 * a + 1], dv[db][4 * a + 2], dv[db][4 * a + 3]};
+      }
+    }
+  } else if (is_cache) {
+    bf16_t* ko = static_cast<bf16_t*>(dKc) + (static_cast<size_t>(bh) * M + key) * D;
+    bf16_t* vo = static_cast<bf16_t*>(dVc) + (static_cast<size_t>(bh) * M + key) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -588,11 +607,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 }
 
 // dK/dV of the chunk keys: sum of the kPieces partials in piece order
-// (deterministic), dK scaled, written in bf16.  One thread per 4 elements.
-template <int D>
+// (deterministic), dK scaled, written in bf16 -- or, with ACC, added to the
+// fp32 rows already in dKn/dVn.  One thread per 4 elements.
+template <int D, bool ACC>
 __global__ __launch_bounds__(256) void bwd_chunk_reduce_kernel(const float* __restrict__ part,
-                                                               bf16_t* __restrict__ dKn,
-                                                               bf16_t* __restrict__ dVn, int S,
+                                                               void* __restrict__ dKn,
+                                                               void* __restrict__ dVn, int S,
                                                                int n_heads, int n_cht, float scale) {
   constexpr int C4 = D / 4;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -610,8 +630,15 @@ __global__ __launch_bounds__(256) void bwd_chunk_reduce_kernel(const float* __re
     sk += *reinterpret_cast<const f32x4*>(src + p * ps);
     sv += *reinterpret_cast<const f32x4*>(src + kPieces * ps + p * ps);
   }
-  *reinterpret_cast<bf16x4*>(dKn + kr * D + 4 * c4) = to_bf16x4(sk * scale);
-  *reinterpret_cast<bf16x4*>(dVn + kr * D + 4 * c4) = to_bf16x4(sv);
+  if constexpr (ACC) {
+    f32x4* kp = reinterpret_cast<f32x4*>(static_cast<float*>(dKn) + kr * D + 4 * c4);
+    f32x4* vp = reinterpret_cast<f32x4*>(static_cast<float*>(dVn) + kr * D + 4 * c4);
+    *kp = *kp + sk * scale;
+    *vp = *vp + sv;
+  } else {
+    *reinterpret_cast<bf16x4*>(static_cast<bf16_t*>(dKn) + kr * D + 4 * c4) = to_bf16x4(sk * scale);
+    *reinterpret_cast<bf16x4*>(static_cast<bf16_t*>(dVn) + kr * D + 4 * c4) = to_bf16x4(sv);
+  }
 }
 
 }  // namespace
@@ -648,28 +675,36 @@ hipError_t launch_backward(const StepShape& sh, const BackwardArgs& a, hipStream
   if (e != hipSuccess) return e;
   const int n_ct = (sh.M + kKeysPerWG - 1) / kKeysPerWG;
   const int n_cht = (sh.S + kKeysPerWG - 1) / kKeysPerWG;
-#define H2O_LAUNCH_DKDV(DD)                                                                            \
-  hipLaunchKernelGGL(bwd_dkdv_kernel<DD>, dim3(n_heads * (n_ct + n_cht * kPieces)), dim3(512), 0, st,  \
-                     static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k_cache),          \
-                     static_cast<const bf16_t*>(a.v_cache), a.pos, static_cast<const bf16_t*>(a.k_new), \
-                     static_cast<const bf16_t*>(a.v_new), static_cast<const bf16_t*>(a.d_out), a.lse, \
-                     Dws, static_cast<bf16_t*>(a.dk_cache), static_cast<bf16_t*>(a.dv_cache), part,   \
+#define H2O_LAUNCH_DKDV(DD, AC)                                                                        \
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(bwd_dkdv_kernel<DD, AC>), dim3(n_heads * (n_ct + n_cht * kPieces)),  \
+                     dim3(512), 0, st, static_cast<const bf16_t*>(a.q),                                \
+                     static_cast<const bf16_t*>(a.k_cache), static_cast<const bf16_t*>(a.v_cache), a.pos, \
+                     static_cast<const bf16_t*>(a.k_new), static_cast<const bf16_t*>(a.v_new),         \
+                     static_cast<const bf16_t*>(a.d_out), a.lse, Dws, a.dk_cache, a.dv_cache, part,    \
                      sh.Hq, sh.Hkv, sh.S, sh.M, c2, sh.scale, n_heads, n_ct, n_cht)
-  if (sh.D == 128) H2O_LAUNCH_DKDV(128);
-  else H2O_LAUNCH_DKDV(64);
+  if (sh.D == 128) {
+    if (a.accumulate) H2O_LAUNCH_DKDV(128, true);
+    else H2O_LAUNCH_DKDV(128, false);
+  } else {
+    if (a.accumulate) H2O_LAUNCH_DKDV(64, true);
+    else H2O_LAUNCH_DKDV(64, false);
+  }
 #undef H2O_LAUNCH_DKDV
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n_red = static_cast<int64_t>(n_heads) * sh.S * (sh.D / 4);
   const unsigned red_blocks = static_cast<unsigned>((n_red + 255) / 256);
-  if (sh.D == 128)
-    hipLaunchKernelGGL(bwd_chunk_reduce_kernel<128>, dim3(red_blocks), dim3(256), 0, st, part,
-                       static_cast<bf16_t*>(a.dk_new), static_cast<bf16_t*>(a.dv_new), sh.S, n_heads, n_cht,
-                       sh.scale);
-  else
-    hipLaunchKernelGGL(bwd_chunk_reduce_kernel<64>, dim3(red_blocks), dim3(256), 0, st, part,
-                       static_cast<bf16_t*>(a.dk_new), static_cast<bf16_t*>(a.dv_new), sh.S, n_heads, n_cht,
-                       sh.scale);
+#define H2O_LAUNCH_RED(DD, AC)                                                                           \
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(bwd_chunk_reduce_kernel<DD, AC>), dim3(red_blocks), dim3(256), 0, st, \
+                     part, a.dk_new, a.dv_new, sh.S, n_heads, n_cht, sh.scale)
+  if (sh.D == 128) {
+    if (a.accumulate) H2O_LAUNCH_RED(128, true);
+    else H2O_LAUNCH_RED(128, false);
+  } else {
+    if (a.accumulate) H2O_LAUNCH_RED(64, true);
+    else H2O_LAUNCH_RED(64, false);
+  }
+#undef H2O_LAUNCH_RED
   return hipGetLastError();
 }
 

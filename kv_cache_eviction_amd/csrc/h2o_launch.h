@@ -77,6 +77,9 @@ struct BackwardArgs {
   void* dk_new;
   void* dv_new;
   void* workspace;         // >= backward_workspace_bytes: D_i = dO_i . O_i, partial dK/dV
+  // false: dk/dv outputs are bf16 and overwritten.  true: they are fp32 and
+  // the step's (scaled) gradients are added to them; free slots add nothing
+  bool accumulate = false;
 };
 
 // One step of the backward walk through the buffer (recurrence.hip).
@@ -88,10 +91,6 @@ struct RecurrenceArgs {
   const void* k_old;
   const void* v_old;
   const int32_t* pos_old;
-  const void* dk_cache;   // the step's backward outputs (bf16)
-  const void* dv_cache;
-  const void* dk_new;
-  const void* dv_new;
   float* acc_k;           // [B*Hkv][M][d] carried across the walk
   float* acc_v;
   float* gk;              // [B*Hkv][S][d] total gradients of the step's tokens
@@ -107,8 +106,9 @@ bool select_copies_rows(const StepShape& sh);   // the select kernel also writes
 hipError_t launch_scatter(const StepShape& sh, const SelectArgs& a, int dtype, hipStream_t st);
 hipError_t launch_backward(const StepShape& sh, const BackwardArgs& a, hipStream_t st);
 size_t backward_workspace_bytes(int B, int Hq, int Hkv, int S, int D);
-hipError_t launch_undo_step(const StepShape& sh, const RecurrenceArgs& a, int dtype, hipStream_t st);
-hipError_t launch_route(const StepShape& sh, const RecurrenceArgs& a, hipStream_t st);
+// undo the step on the cache and move each written slot's accumulator into
+// its token's gradient (before the step's backward adds into both)
+hipError_t launch_undo_gather(const StepShape& sh, const RecurrenceArgs& a, int dtype, hipStream_t st);
 hipError_t launch_reset(float* scores, int32_t* pos, int64_t n_slots, int32_t* counters,
                         int64_t n_counters, hipStream_t st);
 

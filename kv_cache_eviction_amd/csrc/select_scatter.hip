@@ -252,13 +252,36 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   const int n_free = tot & 0xffff, n_cand = tot >> 16;
   const int n_f = min(S, n_free);
   const int n_e = S - n_f;
-  if (n_cand < n_e) {                      // infeasible adopted state: no slot is written
+  if (n_cand < n_e) {
+    // infeasible adopted state: no slot is written.  Every optional output
+    // is still defined: slot and old position -1 (outside [0, M), so the
+    // backward walk skips the token), the chunk keys' masses as computed,
+    // zero old rows (the scatter kernel zeroes them for longer chunks)
     if constexpr (!POS) {
 #pragma unroll
       for (int i = 0; i < SPT; ++i)
         if (m0 + i < M && !((fmask >> i) & 1u)) sc_h[m0 + i] = key_value(key[i]);
     }
-    for (int jj = tid; jj < S; jj += kThreads) targets[static_cast<size_t>(bh) * S + jj] = -1;
+    for (int jj = tid; jj < S; jj += kThreads) {
+      const size_t r = static_cast<size_t>(bh) * S + jj;
+      targets[r] = -1;
+      if (slots_out) slots_out[r] = -1;
+      if (pos_old) pos_old[r] = -1;
+      if (step_mass) {
+        float mu = 0.f;
+        for (int sp = 0; sp < R; ++sp) mu += POS ? 0.f : ph[static_cast<size_t>(sp) * PS + M + jj];
+        step_mass[static_cast<size_t>(bh) * PS + M + jj] = mu;
+      }
+    }
+    if (row_bytes > 0 && k_old) {
+      const int cpr = row_bytes >> 4;
+      const u32x4 z = {0, 0, 0, 0};
+      for (int idx = tid; idx < S * cpr; idx += kThreads) {
+        const size_t off = static_cast<size_t>(bh) * S * row_bytes + static_cast<size_t>(idx) * 16;
+        store_u32x4(k_old + off, z);
+        store_u32x4(v_old + off, z);
+      }
+    }
     if (tid == 0) atomicOr(status, 1);
     return;
   }
@@ -440,9 +463,16 @@ __global__ __launch_bounds__(256) void scatter_kernel(
   for (int idx = threadIdx.x; idx < n; idx += blockDim.x) {
     const int jj = j0 + idx / cpr, c = idx % cpr;
     const int t = targets[static_cast<size_t>(bh) * S + jj];
-    if (t < 0) continue;                          // infeasible head: nothing is written
-    const int slot = t & ~kWasFree;
     const size_t src = (static_cast<size_t>(bh) * S + jj) * row_bytes + 16 * c;
+    if (t < 0) {                                  // infeasible head: nothing is overwritten
+      if (k_old) {
+        const u32x4 z = {0, 0, 0, 0};
+        store_u32x4(k_old + src, z);
+        store_u32x4(v_old + src, z);
+      }
+      continue;
+    }
+    const int slot = t & ~kWasFree;
     const size_t dst = (static_cast<size_t>(bh) * M + slot) * row_bytes + 16 * c;
     const u32x4 kv = load_u32x4(kn + src);
     const u32x4 vv = load_u32x4(vn + src);

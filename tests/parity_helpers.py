@@ -130,7 +130,7 @@ def run_and_check_step(cache, cfg, q_np, k_np, v_np, heads, W, scale=None, prefi
         kold_g, vold_g = to_f64(k_old), to_f64(v_old)
     qf, kf, vf = wl.stored_to_f64(q_np), wl.stored_to_f64(k_np), wl.stored_to_f64(v_np)
     errs = dict(o_max_abs=0.0, o_rel_rms=0.0, lse_max_abs=0.0, score_rel=0.0, mass_rel=0.0,
-                tie_exempt=0, min_gap=math.inf)
+                tie_exempt=0, min_gap=math.inf, evicting=0, exact_cuts=0)
     o_got, o_ref = [], []
     for (b, h) in heads:
         hs = slice(h * G, (h + 1) * G)
@@ -146,6 +146,9 @@ def run_and_check_step(cache, cfg, q_np, k_np, v_np, heads, W, scale=None, prefi
         R_ref = ref["targets"][0, 0]
         gap = ref["cut_gap"][0, 0]
         errs["min_gap"] = min(errs["min_gap"], gap)
+        if len(ref["evicted"][0][0]):
+            errs["evicting"] += 1                 # an eviction cut was checked ...
+            errs["exact_cuts"] += gap >= TIE_GAP  # ... bit-exactly (no near-tie exemption possible)
         if prefill:
             R_gpu = np.sort(np.flatnonzero(now["pos"][0, 0] >= before.T))
             diff = compare_targets(R_gpu, R_ref, sig_acc, ref["evicted"][0][0], gap)
@@ -168,6 +171,8 @@ def run_and_check_step(cache, cfg, q_np, k_np, v_np, heads, W, scale=None, prefi
                 exp_v = 0.0 if was_free else st["V"][0, 0, m]
                 assert np.array_equal(kold_g[b, h, j], np.broadcast_to(exp_k, (d,)))
                 assert np.array_equal(vold_g[b, h, j], np.broadcast_to(exp_v, (d,)))
+        if gap >= TIE_GAP:
+            assert not diff
         errs["tie_exempt"] += len(diff)
         keep = np.ones(M, dtype=bool)
         for m in diff:
@@ -181,6 +186,28 @@ def run_and_check_step(cache, cfg, q_np, k_np, v_np, heads, W, scale=None, prefi
         errs["score_rel"] = max(errs["score_rel"], float(srel.max(initial=0.0)))
     errs["o_max_abs"], errs["o_rel_rms"] = out_errors(np.stack(o_got), np.stack(o_ref))
     return errs
+
+
+def merge_errors(worst: dict, errs: dict) -> dict:
+    """Worst figures over several checked steps (counts are summed)."""
+    for key, val in errs.items():
+        if key == "min_gap":
+            worst[key] = min(worst.get(key, math.inf), val)
+        elif key in ("tie_exempt", "evicting", "exact_cuts"):
+            worst[key] = worst.get(key, 0) + val
+        else:
+            worst[key] = max(worst.get(key, 0), val)
+    return worst
+
+
+def assert_cuts_checked(worst: dict, what=""):
+    """Every checked eviction cut whose oracle gap allows it was compared
+    bit-exactly: no slot was exempted unless a near-tie was seen, and at least
+    one evicting step was checked without the exemption."""
+    if worst.get("min_gap", math.inf) >= TIE_GAP:
+        assert worst.get("tie_exempt", 0) == 0, (what, worst)
+    if worst.get("evicting", 0):
+        assert worst.get("exact_cuts", 0) >= 1, (what, worst)
 
 
 def assert_within(errs, what=""):

@@ -17,8 +17,8 @@ import torch.nn.functional as F
 
 from kv_cache_eviction_amd import workloads as wl
 from oracle import h2o_oracle as orc
-from tests.parity_helpers import (assert_within, cfg_of, run_and_check_step, snapshot, to_device,
-                                  to_f64, h2o_mod)
+from tests.parity_helpers import (assert_cuts_checked, assert_within, cfg_of, merge_errors,
+                                  run_and_check_step, snapshot, to_device, to_f64, h2o_mod)
 
 pytestmark = pytest.mark.gpu
 
@@ -42,8 +42,7 @@ def _run(w: wl.Workload, seed: int, check_steps, heads, cfg_kw=None, max_steps=N
             _say(f"[{w.name}] check chunk {c}")
             errs = run_and_check_step(cache, cfg, q, k, v, heads, w.recent_window, prefill=(c == 0))
             assert_within(errs, f"{w.name} chunk {c}")
-            for key, val in errs.items():
-                worst[key] = max(worst.get(key, 0), val) if key != "min_gap" else min(worst.get(key, math.inf), val)
+            merge_errors(worst, errs)
         else:
             qt, kt, vt = to_device(q), to_device(k), to_device(v)
             if c == 0:
@@ -53,6 +52,7 @@ def _run(w: wl.Workload, seed: int, check_steps, heads, cfg_kw=None, max_steps=N
     torch.cuda.synchronize()
     assert h2o.h2o_device_status(cache.handle) == 0
     _say(f"[{w.name}] worst errors {worst}")
+    assert_cuts_checked(worst, w.name)
     return cache, worst
 
 
@@ -312,11 +312,15 @@ def test_scores_snapshot_and_timing_counters():
     assert e.value.status == h2o.H2O_ERR_SHAPE
 
 
-def test_infeasible_adopted_state_sets_device_status():
+@pytest.mark.parametrize("S,M", [(16, 64), (300, 640)])
+def test_infeasible_adopted_state_sets_device_status(S, M):
+    """An adopted state with nothing evictable: no slot is written, the status
+    bit is set, and every optional output is still defined (S = 16: rows
+    handled by the select kernel; S = 300: by the scatter kernel)."""
     h2o = h2o_mod()
-    B, Hq, Hkv, d, M, S, W = 1, 2, 1, 64, 64, 16, 8
+    B, Hq, Hkv, d, W = 1, 2, 1, 64, 8
     cfg = h2o.H2OConfig(B, Hq, Hkv, d, M, W, S, M, "bf16")
-    T = 100
+    T = 1000
     # every slot inside the recent window: nothing is evictable
     pos = torch.full((B, Hkv, M), T - 1, dtype=torch.int32)
     state = (torch.zeros((B, Hkv, M, d), dtype=torch.bfloat16).cuda(),
@@ -326,10 +330,23 @@ def test_infeasible_adopted_state_sets_device_status():
     cache = h2o.H2OCache(cfg, adopt_state=state, tokens_seen=T)
     q = torch.randn((B, Hq, S, d), device="cuda").to(torch.bfloat16)
     k = torch.randn((B, Hkv, S, d), device="cuda").to(torch.bfloat16)
-    cache.chunk_step(q, k, k.clone())
+    # optional outputs pre-filled with garbage: all must be overwritten
+    slots = torch.full((B, Hkv, S), 7, dtype=torch.int32, device="cuda")
+    pos_old = torch.full((B, Hkv, S), 7, dtype=torch.int32, device="cuda")
+    mass = torch.full((B, Hkv, M + S), -5.0, dtype=torch.float32, device="cuda")
+    k_old = torch.full((B, Hkv, S, d), 3.0, dtype=torch.bfloat16, device="cuda")
+    v_old = torch.full_like(k_old, 3.0)
+    cache.chunk_step(q, k, k.clone(), slots_out=slots, step_mass=mass, k_old=k_old, v_old=v_old,
+                     pos_old=pos_old)
     assert h2o.h2o_device_status(cache.handle) == 1
     assert h2o.h2o_device_status(cache.handle) == 0         # cleared by the read
     # no slot written; the scores received the step's (positive) mass
     for i in (0, 1, 3):
         assert torch.equal(before[i], state[i])
     assert (state[2] > before[2]).all()
+    assert (slots == -1).all() and (pos_old == -1).all()
+    assert (k_old.float() == 0).all() and (v_old.float() == 0).all()
+    m = mass.double().cpu()
+    assert (m > 0).all()
+    assert torch.allclose(m.sum(-1), torch.full((B, Hkv), float(S * Hq // Hkv), dtype=torch.float64), rtol=1e-5)
+    assert torch.allclose(m[..., :M], (state[2] - before[2]).double().cpu(), rtol=1e-6, atol=0)

@@ -9,7 +9,8 @@ gradient and the total key/value gradients (own step plus every later step
 that read the token's slot) are compared with rel-RMS <= 5e-3 and
 max |err| <= 2e-2 * max |ref|, the bounds of the single-step backward.
 Undoing every step, the prefill last, must give back the empty cache
-exactly."""
+exactly.  The walk carries every gradient in fp32 (no per-step rounding), so
+the bound holds on rows of 20 and 30 steps as on short ones."""
 from __future__ import annotations
 
 import math
@@ -33,6 +34,13 @@ CASES = {
                     total_len=96 + 48 * 5, cache_slots=160, recent_window=16, qk_std=1.0),
     "g4_d64_b2": dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=64, prefill=64, chunk=40,
                       total_len=64 + 40 * 5, cache_slots=128, recent_window=8, qk_std=1.0),
+    # a long row: 20 chunk steps (4 fill steps, then 16 evicting), M = 1024
+    "g4_d128_m1024_20steps": dict(batch=1, n_q_heads=8, n_kv_heads=2, head_dim=128, prefill=512,
+                                  chunk=128, total_len=512 + 128 * 20, cache_slots=1024,
+                                  recent_window=128, qk_std=1.0),
+    # 30 chunk steps at G = 8, d = 64, two sequences
+    "g8_d64_b2_30steps": dict(batch=2, n_q_heads=16, n_kv_heads=2, head_dim=64, prefill=256, chunk=64,
+                              total_len=256 + 64 * 30, cache_slots=512, recent_window=64, qk_std=1.0),
 }
 
 
