@@ -87,7 +87,8 @@ typedef enum {
   H2O_ERR_WORKSPACE = 5,   /* workspace smaller than h2o_workspace_bytes()       */
   H2O_ERR_HIP = 6,         /* a HIP call failed; see h2o_last_hip_error()        */
   H2O_ERR_UNSUPPORTED = 7, /* valid request the library does not implement       */
-  H2O_ERR_ALIGN = 8        /* a buffer pointer is not 16-byte aligned            */
+  H2O_ERR_ALIGN = 8,       /* a buffer pointer is not 16-byte aligned            */
+  H2O_ERR_TOO_LARGE = 9    /* request exceeds h2o_chunk_backward_static's scratch */
 } h2o_status;
 
 typedef enum { H2O_BF16 = 0, H2O_FP32 = 1 } h2o_dtype;
@@ -220,6 +221,28 @@ H2O_API h2o_status h2o_chunk_backward(const h2o_config* cfg, const void* q,
 /* Host only: workspace bytes h2o_chunk_backward needs for chunk length s
  * (0 if the config is invalid or s < 1). */
 H2O_API size_t h2o_backward_workspace_bytes(const h2o_config* cfg, int32_t s);
+
+/* h2o_chunk_backward without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, serving loops, harnesses
+ * that forbid allocation).  Same arguments (minus workspace), outputs,
+ * determinism and errors as h2o_chunk_backward; the kernels are the same.
+ * Its scratch is a static device array of 72 MiB that the library holds on
+ * every GPU it runs on until the process ends, found once per device with
+ * hipGetSymbolAddress on the first call there; the call itself allocates
+ * nothing.  Requests whose h2o_backward_workspace_bytes(cfg, s) exceeds
+ * 72 MiB are refused with H2O_ERR_TOO_LARGE before anything is enqueued
+ * (at d = 128 that allows B * Hkv * ceil(s / 128) * 128 up to 16384 chunk
+ * keys, e.g. 8 KV heads of a 2048-token chunk).  Nothing in the scratch
+ * needs to start at zero.  Every call on one GPU shares that GPU's scratch:
+ * calls that overlap on one GPU (other streams, other threads) race and
+ * must be ordered by the caller. */
+H2O_API h2o_status h2o_chunk_backward_static(const h2o_config* cfg, const void* q,
+                                     const void* k_cache, const void* v_cache,
+                                     const int32_t* positions, const void* k_new,
+                                     const void* v_new, int32_t s, const void* out,
+                                     const float* lse, const void* d_out, void* dq,
+                                     void* dk_cache, void* dv_cache, void* dk_new,
+                                     void* dv_new, void* stream);
 
 /* One step of the backward walk through the KV buffer over a row of chunks
  * (LHF Fig. 1(b), with the buffer kept as the deltas of Fig. 1(c)): the

@@ -7,10 +7,15 @@
 #include <string.h>
 
 #include <initializer_list>
+#include <mutex>
 #include <vector>
 
 #include "h2o.h"
 #include "h2o_launch.h"
+
+// Scratch of h2o_chunk_backward_static (see below).
+constexpr size_t kStaticScratchBytes = size_t{72} << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -197,6 +202,35 @@ size_t rec_workspace_bytes(const h2o_config* cfg, int32_t s) {
   return h2o::backward_workspace_bytes(cfg->batch, cfg->n_q_heads, cfg->n_kv_heads, s, cfg->head_dim);
 }
 
+// Scratch of h2o_chunk_backward_static, for callers that cannot allocate:
+// the backward's workspace (D_i per query row, fp32 partial dK/dV of the
+// chunk keys) in a device array of fixed size that every GPU the library
+// runs on holds until the process ends.  Host code never passes `scratch`
+// itself to a kernel (on the host that name is only a stand-in): each
+// device's address comes from hipGetSymbolAddress, taken once per device
+// with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch (looked up on first use).
+hipError_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -212,6 +246,7 @@ const char* h2o_status_str(h2o_status s) {
     case H2O_ERR_HIP: return "HIP error";
     case H2O_ERR_UNSUPPORTED: return "unsupported request";
     case H2O_ERR_ALIGN: return "buffer pointer not 16-byte aligned";
+    case H2O_ERR_TOO_LARGE: return "request needs more than the library's static scratch (72 MiB)";
   }
   return "unknown status";
 }
@@ -422,6 +457,33 @@ h2o_status h2o_chunk_backward(const h2o_config* cfg, const void* q, const void* 
   const h2o::StepShape sh = backward_shape(cfg, s);
   h2o::BackwardArgs a{q, k_cache, v_cache, positions, k_new, v_new, out, lse, d_out,
                       dq, dk_cache, dv_cache, dk_new, dv_new, workspace};
+  const hipError_t e = h2o::launch_backward(sh, a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? H2O_OK : H2O_ERR_HIP;
+}
+
+h2o_status h2o_chunk_backward_static(const h2o_config* cfg, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* positions, const void* k_new,
+                                     const void* v_new, int32_t s, const void* out, const float* lse,
+                                     const void* d_out, void* dq, void* dk_cache, void* dv_cache,
+                                     void* dk_new, void* dv_new, void* stream) {
+  if (!cfg || !q || !k_cache || !v_cache || !positions || !k_new || !v_new || !out || !lse || !d_out ||
+      !dq || !dk_cache || !dv_cache || !dk_new || !dv_new)
+    return H2O_ERR_NULL;
+  if (misaligned({q, k_cache, v_cache, positions, k_new, v_new, out, lse, d_out, dq, dk_cache, dv_cache,
+                  dk_new, dv_new}))
+    return H2O_ERR_ALIGN;
+  h2o_status r = h2o_validate_config(cfg);
+  if (r != H2O_OK) return r;
+  if (cfg->dtype != H2O_BF16) return H2O_ERR_UNSUPPORTED;
+  if (s < 1 || s > max_len(cfg)) return H2O_ERR_SHAPE;
+  if (h2o::backward_workspace_bytes(cfg->batch, cfg->n_q_heads, cfg->n_kv_heads, s, cfg->head_dim) >
+      kStaticScratchBytes)
+    return H2O_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  if (scratch_of_current_device(&ws) != hipSuccess) return H2O_ERR_HIP;
+  const h2o::StepShape sh = backward_shape(cfg, s);
+  h2o::BackwardArgs a{q, k_cache, v_cache, positions, k_new, v_new, out, lse, d_out,
+                      dq, dk_cache, dv_cache, dk_new, dv_new, ws};
   const hipError_t e = h2o::launch_backward(sh, a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? H2O_OK : H2O_ERR_HIP;
 }

@@ -22,7 +22,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libh2o.so")
 
 H2O_OK, H2O_ERR_NULL, H2O_ERR_CONFIG, H2O_ERR_SHAPE, H2O_ERR_STATE = 0, 1, 2, 3, 4
-H2O_ERR_WORKSPACE, H2O_ERR_HIP, H2O_ERR_UNSUPPORTED, H2O_ERR_ALIGN = 5, 6, 7, 8
+H2O_ERR_WORKSPACE, H2O_ERR_HIP, H2O_ERR_UNSUPPORTED, H2O_ERR_ALIGN, H2O_ERR_TOO_LARGE = 5, 6, 7, 8, 9
 H2O_BF16, H2O_FP32 = 0, 1
 POLICIES = {"h2o": 0, "recent": 1, "sink_recent": 2}
 KERNEL_IDS = {"attn_fwd": 0, "score": 1, "select": 2, "reset": 3, "scatter": 4}
@@ -30,6 +30,7 @@ KERNEL_IDS = {"attn_fwd": 0, "score": 1, "select": 2, "reset": 3, "scatter": 4}
 EXPORTED = [
     "h2o_validate_config", "h2o_workspace_bytes", "h2o_cache_init", "h2o_prefill",
     "h2o_chunk_step", "h2o_get_scores", "h2o_chunk_backward", "h2o_backward_workspace_bytes",
+    "h2o_chunk_backward_static",
     "h2o_recurrence_backward_step", "h2o_recurrence_workspace_bytes",
     "h2o_tokens_seen", "h2o_device_status", "h2o_set_timing", "h2o_get_timing",
     "h2o_cache_destroy", "h2o_status_str", "h2o_last_hip_error",
@@ -67,6 +68,7 @@ def _load():
         "h2o_get_scores": (I32, [P, P, P, P]),
         "h2o_chunk_backward": (I32, [cfgp, P, P, P, P, P, P, I32, P, P, P, P, P, P, P, P, P, SZ, P]),
         "h2o_backward_workspace_bytes": (SZ, [cfgp, I32]),
+        "h2o_chunk_backward_static": (I32, [cfgp, P, P, P, P, P, P, I32, P, P, P, P, P, P, P, P, P]),
         "h2o_recurrence_backward_step": (I32, [cfgp, P, P, P, P, P, P, P, P, P, P, I32, P, P, P, P, P, P, P,
                                                P, P, SZ, P]),
         "h2o_recurrence_workspace_bytes": (SZ, [cfgp, I32]),
@@ -224,8 +226,8 @@ def h2o_get_scores(handle, scores_out, positions_out=None, stream=None):
            "h2o_get_scores")
 
 
-def h2o_chunk_backward(cfg: H2OConfig, q, k_cache, v_cache, positions, k_new, v_new, out, lse, d_out,
-                       dq, dk_cache, dv_cache, dk_new, dv_new, workspace, stream=None):
+def _check_backward_args(cfg, q, k_cache, v_cache, positions, k_new, v_new, out, lse, d_out, dq, dk_cache,
+                         dv_cache, dk_new, dv_new):
     B, Hq, Hkv, d, M = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.cache_slots
     s = q.shape[2]
     dt = cfg.torch_dtype
@@ -238,12 +240,31 @@ def h2o_chunk_backward(cfg: H2OConfig, q, k_cache, v_cache, positions, k_new, v_
         (dk_cache, "dk_cache", (B, Hkv, M, d), dt), (dv_cache, "dv_cache", (B, Hkv, M, d), dt),
         (dk_new, "dk_new", (B, Hkv, s, d), dt), (dv_new, "dv_new", (B, Hkv, s, d), dt)]:
         _expect(t, name, shp, ty)
+    return s
+
+
+def h2o_chunk_backward(cfg: H2OConfig, q, k_cache, v_cache, positions, k_new, v_new, out, lse, d_out,
+                       dq, dk_cache, dv_cache, dk_new, dv_new, workspace, stream=None):
+    s = _check_backward_args(cfg, q, k_cache, v_cache, positions, k_new, v_new, out, lse, d_out, dq,
+                             dk_cache, dv_cache, dk_new, dv_new)
     c = cfg.c()
     ws_bytes = 0 if workspace is None else workspace.numel()
     _check(_lib.h2o_chunk_backward(ctypes.byref(c), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(positions),
                                    _ptr(k_new), _ptr(v_new), s, _ptr(out), _ptr(lse), _ptr(d_out), _ptr(dq),
                                    _ptr(dk_cache), _ptr(dv_cache), _ptr(dk_new), _ptr(dv_new),
                                    _ptr(workspace), ws_bytes, _stream(stream)), "h2o_chunk_backward")
+
+
+def h2o_chunk_backward_static(cfg: H2OConfig, q, k_cache, v_cache, positions, k_new, v_new, out, lse, d_out,
+                              dq, dk_cache, dv_cache, dk_new, dv_new, stream=None):
+    """h2o_chunk_backward with the library's static scratch: no workspace, no allocation."""
+    s = _check_backward_args(cfg, q, k_cache, v_cache, positions, k_new, v_new, out, lse, d_out, dq,
+                             dk_cache, dv_cache, dk_new, dv_new)
+    c = cfg.c()
+    _check(_lib.h2o_chunk_backward_static(ctypes.byref(c), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                          _ptr(positions), _ptr(k_new), _ptr(v_new), s, _ptr(out), _ptr(lse),
+                                          _ptr(d_out), _ptr(dq), _ptr(dk_cache), _ptr(dv_cache), _ptr(dk_new),
+                                          _ptr(dv_new), _stream(stream)), "h2o_chunk_backward_static")
 
 
 def h2o_recurrence_workspace_bytes(cfg: H2OConfig, s: int) -> int:
