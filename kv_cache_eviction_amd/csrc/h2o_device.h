@@ -47,13 +47,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 // buffer_load_dwordx4 ... lds: lane i copies the 16 bytes at voff + soff of
-// the resource to LDS address lds_base + 16 i (lds_base wave-uniform).  The
-// compiler does not track these writes: wait with vmcnt(0) and a barrier
-// before any wave reads the destination.
+// the resource to LDS address lds_base + 16 i (lds_base wave-uniform, in M0).
+// Issued from inline asm so that the compiler does not track the copy: its
+// own tracking cannot tell one LDS destination array from another across a
+// loop back-edge and would wait for copies just issued into other slots
+// before an LDS read, draining the prefetch.  Every caller orders the copies
+// itself: an explicit vmcnt wait and a barrier before any wave reads the
+// destination, and a barrier after the last reads before a copy overwrites
+// it.  The instruction has no register result, and copies issued here only
+// make the compiler's own vmcnt waits stricter (loads retire in order).
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds_base, uint32_t voff,
                                       uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      r, (__attribute__((address_space(3))) void*)(const_cast<void*>(lds_base)), 16, voff, soff, 0, 0);
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const void*)(lds_base)));
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(m0)
+               : "memory");
 }
 
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }

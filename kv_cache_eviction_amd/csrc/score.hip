@@ -137,6 +137,14 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
   auto issue_blk = [&](int bk, auto stg) __attribute__((always_inline)) {
     const char* dst = stage_buf(stg) + wave * NDMA * 1024;
     const int u0 = bk * kRB + r0;
+    if (is_cache) {                 // every query row of the group: row u is row u
+#pragma unroll
+      for (int j = 0; j < NDMA; ++j) {
+        const uint32_t chunk = CPR == 16 ? (chunk0 ^ (64u * j)) : chunk0;
+        dma16(rq, dst + j * 1024, static_cast<uint32_t>(min(u0 + j * RK, n_need - 1)) * RBY + chunk, 0);
+      }
+      return;
+    }
     int i0;
     const int row0 = row_of(min(u0, n_need - 1), i0);
     int rows[NDMA];
@@ -169,10 +177,15 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
     RowInfo ri{0.f, 1 << 30};
     if (tid < kRB) {
       const int u = bk * kRB + tid;
-      int i;
-      const int row = row_of(min(u, n_need - 1), i);
-      ri.lv = lhead[row];
-      ri.qi = u < n_need ? i : (1 << 30);
+      if (is_cache) {               // row u is row u; its query index is never tested
+        ri.lv = lhead[min(u, n_need - 1)];
+        ri.qi = u < n_need ? 0 : (1 << 30);
+      } else {
+        int i;
+        const int row = row_of(min(u, n_need - 1), i);
+        ri.lv = lhead[row];
+        ri.qi = u < n_need ? i : (1 << 30);
+      }
     }
     return ri;
   };

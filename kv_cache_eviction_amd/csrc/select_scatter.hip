@@ -24,9 +24,10 @@
 //      scores (fixed split order: deterministic);
 //   2. selects the targets: scores map to order-preserving 32-bit keys, the
 //      bits every candidate shares are found with an AND/OR reduction and
-//      skipped, and 8-bit LDS radix passes over the remaining bits (one
-//      barrier each) find the n_e-th smallest key; equal keys resolve to the
-//      lowest slot through one exclusive scan in slot order;
+//      skipped, and 11-bit LDS radix passes over the remaining bits (one
+//      barrier each, stopping as soon as the bin holding the cut is taken
+//      whole) find the n_e-th smallest key; equal keys resolve to the lowest
+//      slot through one exclusive scan in slot order;
 //   3. writes scores, positions and the target list R (with a flag for
 //      targets that were free).
 // The scatter kernel then copies the chunk's K/V rows into their slots with
@@ -43,7 +44,8 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kWavesSel = kThreads / 64;
 constexpr int kMaxSplits = 8;  // upper bound of the score kernel's row splits
-constexpr int kMuRegs = 2;     // chunk keys per thread whose masses are prefetched
+constexpr int kDigitBits = 11; // radix digit: 2048-bin histograms
+constexpr int kBins = 1 << kDigitBits;
 // chunks up to this length copy their K/V rows inside the select kernel (one
 // workgroup per head keeps up with that little data, and a launch is saved);
 // longer chunks use the many-workgroup scatter kernel
@@ -105,7 +107,7 @@ __device__ void block_excl_scan2(int a, int b, int* tmp, int& pa, int& pb) {
     tmp[wave] = ia;
     tmp[kWavesSel + wave] = ib;
   }
-  __syncthreads();
+  barrier_lds();
   int ba = 0, bb = 0;
 #pragma unroll
   for (int w = 0; w < kWavesSel; ++w) {
@@ -118,17 +120,25 @@ __device__ void block_excl_scan2(int a, int b, int* tmp, int& pa, int& pb) {
 
 // Thread t owns the SPT consecutive slots t*SPT .. t*SPT+SPT-1 (SPT*512 >= M)
 // and keeps their keys and classes in registers through every phase.
-template <int SPT, bool POS>
+// RMAX bounds the score pass's row splits R (1, 2, 4 or 8; R <= RMAX, splits
+// past R re-read split R-1 and are not added); RMAX = 0 selects a position
+// policy (no masses).  VEC: M and S are multiples of 4 and the buffers are
+// 16-byte aligned, so slot rows and chunk masses move in 16-byte pieces.
+template <int SPT, int RMAX, bool VEC>
 __global__ __launch_bounds__(kThreads) void select_kernel(
     float* __restrict__ scores, int32_t* __restrict__ pos, const float* __restrict__ partial,
     int R, int32_t* __restrict__ targets, int32_t* __restrict__ slots_out,
-    int32_t* __restrict__ pos_old, float* __restrict__ step_mass, int32_t* __restrict__ status, int T, int W, int S, int M,
-    int n_cache, int vec, int n_floor, char* __restrict__ kc, char* __restrict__ vc,
+    int32_t* __restrict__ pos_old, float* __restrict__ step_mass, int32_t* __restrict__ status, int T, int W,
+    int S, int M, int n_cache, int n_floor, char* __restrict__ kc, char* __restrict__ vc,
     const char* __restrict__ kn, const char* __restrict__ vn, char* __restrict__ k_old,
     char* __restrict__ v_old, int row_bytes) {
+  constexpr bool POS = RMAX == 0;
+  constexpr int NR = POS ? 1 : RMAX;
+  constexpr bool VSLOT = VEC && SPT % 4 == 0;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  int* s_R = reinterpret_cast<int*>(smem);                 // [S]: target of chunk row j (flagged)
-  __shared__ __attribute__((aligned(16))) uint32_t hist[3][kWavesSel / 2][256];   // per wave pair, 3 rotating
+  float* s_mu = reinterpret_cast<float*>(smem);                      // [S] chunk keys' masses (H2O)
+  int* s_R = reinterpret_cast<int*>(smem + (POS ? 0 : 4 * static_cast<size_t>(S)));   // [S] row copy
+  __shared__ __attribute__((aligned(16))) uint32_t hist[3][kBins];   // 3 rotating histograms
   __shared__ int s_red[3][kWavesSel];
   __shared__ int s_scan[2 * kWavesSel];
 
@@ -139,65 +149,91 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   float* sc_h = scores + static_cast<size_t>(bh) * M;
   int32_t* pos_h = pos + static_cast<size_t>(bh) * M;
   const int m0 = tid * SPT;
+  auto split_of = [&](int r) __attribute__((always_inline)) { return static_cast<size_t>(min(r, R - 1)) * PS; };
 
-  // 0. every load up front: the chunk keys' masses (first kMuRegs keys per
-  // thread, summed at the end), then the thread's slots (position, score
-  // and the R per-split masses; splits past R re-read split R-1)
-  float mup[kMuRegs][kMaxSplits];
-#pragma unroll
-  for (int k = 0; k < kMuRegs; ++k) {
-    const int jj = min(tid + k * kThreads, S - 1);
-#pragma unroll
-    for (int r = 0; r < kMaxSplits; ++r)
-      mup[k][r] = POS ? 0.f : ph[static_cast<size_t>(min(r, R - 1)) * PS + M + jj];
-  }
+  // 0. loads.  The thread's slots first (position, score, the per-split
+  // masses), then the chunk keys' masses, summed in split order into s_mu;
+  // every load is unconditional (out-of-range threads re-read a valid row
+  // that they do not use), so the two sets are in flight together and the
+  // wait for the second covers the first.
   int pv[SPT];
   float sv[SPT], dv[SPT];
-  if constexpr (POS) {
-    // positions only: no score is read or kept
-#pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-      pv[i] = pos_h[min(m0 + i, M - 1)];
-      sv[i] = 0.f;
-      dv[i] = 0.f;
-    }
-  } else if (SPT % 4 == 0 && vec && m0 + SPT <= M) {
-    // 16-byte loads of the thread's slots (rows aligned: M, S multiples of 4)
+  if constexpr (VSLOT) {
 #pragma unroll
     for (int i = 0; i < SPT; i += 4) {
-      const int4 p4 = *reinterpret_cast<const int4*>(pos_h + m0 + i);
-      const float4 s4 = *reinterpret_cast<const float4*>(sc_h + m0 + i);
+      const int g = min(m0 + i, M - 4);
+      const int4 p4 = *reinterpret_cast<const int4*>(pos_h + g);
       pv[i] = p4.x; pv[i + 1] = p4.y; pv[i + 2] = p4.z; pv[i + 3] = p4.w;
-      sv[i] = s4.x; sv[i + 1] = s4.y; sv[i + 2] = s4.z; sv[i + 3] = s4.w;
-      float4 part[kMaxSplits];
+      if constexpr (POS) {
+        sv[i] = sv[i + 1] = sv[i + 2] = sv[i + 3] = 0.f;
+        dv[i] = dv[i + 1] = dv[i + 2] = dv[i + 3] = 0.f;
+      } else {
+        const float4 s4 = *reinterpret_cast<const float4*>(sc_h + g);
+        sv[i] = s4.x; sv[i + 1] = s4.y; sv[i + 2] = s4.z; sv[i + 3] = s4.w;
+        float4 part[NR];
 #pragma unroll
-      for (int r = 0; r < kMaxSplits; ++r)
-        part[r] = *reinterpret_cast<const float4*>(ph + static_cast<size_t>(min(r, R - 1)) * PS + m0 + i);
-      float4 ds = {0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < NR; ++r) part[r] = *reinterpret_cast<const float4*>(ph + split_of(r) + g);
+        float4 ds = part[0];
 #pragma unroll
-      for (int r = 0; r < kMaxSplits; ++r) {
-        if (r < R) {
-          ds.x += part[r].x;
-          ds.y += part[r].y;
-          ds.z += part[r].z;
-          ds.w += part[r].w;
+        for (int r = 1; r < NR; ++r) {
+          if (r < R) {
+            ds.x += part[r].x;
+            ds.y += part[r].y;
+            ds.z += part[r].z;
+            ds.w += part[r].w;
+          }
         }
+        dv[i] = ds.x; dv[i + 1] = ds.y; dv[i + 2] = ds.z; dv[i + 3] = ds.w;
       }
-      dv[i] = ds.x; dv[i + 1] = ds.y; dv[i + 2] = ds.z; dv[i + 3] = ds.w;
     }
   } else {
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       const int m = min(m0 + i, M - 1);
       pv[i] = pos_h[m];
-      sv[i] = sc_h[m];
-      float part[kMaxSplits];
+      if constexpr (POS) {
+        sv[i] = 0.f;
+        dv[i] = 0.f;
+      } else {
+        sv[i] = sc_h[m];
+        float part[NR];
 #pragma unroll
-      for (int r = 0; r < kMaxSplits; ++r) part[r] = ph[static_cast<size_t>(min(r, R - 1)) * PS + m];
-      float ds = 0.f;
+        for (int r = 0; r < NR; ++r) part[r] = ph[split_of(r) + m];
+        float ds = part[0];
 #pragma unroll
-      for (int r = 0; r < kMaxSplits; ++r) ds += (r < R) ? part[r] : 0.f;
-      dv[i] = ds;
+        for (int r = 1; r < NR; ++r) ds += (r < R) ? part[r] : 0.f;
+        dv[i] = ds;
+      }
+    }
+  }
+  if constexpr (!POS) {
+    if constexpr (VEC) {
+      for (int j0 = 4 * tid; j0 < S; j0 += 4 * kThreads) {
+        float4 part[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) part[r] = *reinterpret_cast<const float4*>(ph + split_of(r) + M + j0);
+        float4 mu = part[0];
+#pragma unroll
+        for (int r = 1; r < NR; ++r) {
+          if (r < R) {
+            mu.x += part[r].x;
+            mu.y += part[r].y;
+            mu.z += part[r].z;
+            mu.w += part[r].w;
+          }
+        }
+        *reinterpret_cast<float4*>(s_mu + j0) = mu;
+      }
+    } else {
+      for (int jj = tid; jj < S; jj += kThreads) {
+        float part[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) part[r] = ph[split_of(r) + M + jj];
+        float mu = part[0];
+#pragma unroll
+        for (int r = 1; r < NR; ++r) mu += (r < R) ? part[r] : 0.f;
+        s_mu[jj] = mu;
+      }
     }
   }
 
@@ -227,7 +263,9 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       k_or |= key[i];
     }
   }
-  for (int i = tid; i < 2 * (kWavesSel / 2) * 256; i += kThreads) (&hist[0][0][0])[i] = 0;
+  // the first two passes' histograms start at zero (each pass clears the
+  // one two passes ahead)
+  for (int i = tid; i < 2 * kBins / 4; i += kThreads) reinterpret_cast<uint4*>(&hist[0][0])[i] = uint4{0, 0, 0, 0};
   // 2. counts (free | candidates << 16: each at most M <= 16384) and the
   // candidates' common bits, one barrier
   {
@@ -240,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       s_red[2][wave] = static_cast<int>(wo);
     }
   }
-  __syncthreads();
+  barrier_lds();
   int tot = 0;
   uint32_t all_and = 0xffffffffu, all_or = 0u;
 #pragma unroll
@@ -267,11 +305,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       targets[r] = -1;
       if (slots_out) slots_out[r] = -1;
       if (pos_old) pos_old[r] = -1;
-      if (step_mass) {
-        float mu = 0.f;
-        for (int sp = 0; sp < R; ++sp) mu += POS ? 0.f : ph[static_cast<size_t>(sp) * PS + M + jj];
-        step_mass[static_cast<size_t>(bh) * PS + M + jj] = mu;
-      }
+      if (step_mass) step_mass[static_cast<size_t>(bh) * PS + M + jj] = POS ? 0.f : s_mu[jj];
     }
     if (row_bytes > 0 && k_old) {
       const int cpr = row_bytes >> 4;
@@ -287,11 +321,13 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   }
 
   // 3. radix select of the n_e-th smallest candidate key over the bits the
-  // candidates do not all share, 8 bits per pass, one barrier per pass:
-  // histograms rotate through three buffers (a buffer is cleared two passes
-  // before its use, after every wave has read it) and every wave finds the
-  // digit itself
-  uint32_t thr = 0;
+  // candidates do not all share, kDigitBits bits per pass, one barrier per
+  // pass: histograms rotate through three buffers (a buffer is cleared two
+  // passes before its use, after every wave has read it) and every wave
+  // finds the digit itself.  The walk stops early once the bin holding the
+  // cut is taken whole: the bits seen so far then decide every candidate
+  // (cmp_mask below), and the order inside the bin no longer matters.
+  uint32_t thr = 0, cmp_mask = 0xffffffffu;
   int k_eq = 0;
   if (n_e > 0) {
     const uint32_t differ = all_and ^ all_or;
@@ -300,72 +336,88 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     int top = differ ? 31 - __builtin_clz(differ) : -1;  // highest differing bit
     int pass = 0;
     while (top >= 0) {
-      const int shift = top >= 7 ? top - 7 : 0;
-      const uint32_t dmask = (top >= 7 ? 0xffu : ((1u << (top + 1)) - 1u)) << shift;
-      uint32_t (*h)[256] = hist[pass % 3];
-      uint32_t* hw = h[wave >> 1];
+      const int nb = top + 1 < kDigitBits ? top + 1 : kDigitBits;
+      const int shift = top + 1 - nb;
+      const uint32_t dmask = ((1u << nb) - 1u) << shift;
+      uint32_t* h = hist[pass % 3];
+      // histogram: the lanes of a wave whose digit equals the first active
+      // lane's add together in one atomic (scores cluster, so many lanes of
+      // a wave often share a bin), the others one by one
 #pragma unroll
-      for (int i = 0; i < SPT; ++i)
-        if (((cmask >> i) & 1u) && (key[i] & pmask) == prefix) atomicAdd(&hw[(key[i] & dmask) >> shift], 1u);
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < (kWavesSel / 2) * 256 / kThreads; ++i) (&hist[(pass + 2) % 3][0][0])[tid + i * kThreads] = 0;
-      int c[4] = {0, 0, 0, 0}, sum = 0;
-#pragma unroll
-      for (int wp = 0; wp < kWavesSel / 2; ++wp) {
-        const uint4 v = *reinterpret_cast<const uint4*>(&h[wp][4 * lane]);
-        c[0] += static_cast<int>(v.x);
-        c[1] += static_cast<int>(v.y);
-        c[2] += static_cast<int>(v.z);
-        c[3] += static_cast<int>(v.w);
+      for (int i = 0; i < SPT; ++i) {
+        const bool c = ((cmask >> i) & 1u) && (key[i] & pmask) == prefix;
+        const uint32_t d = (key[i] & dmask) >> shift;
+        const uint64_t act = __ballot(c);
+        if (act) {
+          const int lead = static_cast<int>(__builtin_ctzll(act));
+          const uint32_t d0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(d), lead));
+          const uint64_t same = __ballot(c && d == d0);
+          if (lane == lead) atomicAdd(&h[d0], static_cast<uint32_t>(__builtin_popcountll(same)));
+          else if (c && d != d0) atomicAdd(&h[d], 1u);
+        }
       }
+      barrier_lds();
+      {
+        uint4* hc = reinterpret_cast<uint4*>(hist[(pass + 2) % 3]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) sum += c[q];
-      // the cumulative counts are monotone, so exactly one (lane, q) has
-      // kk in (cb, cb + c[q]]: no ordering between the q tests is needed
-      int cb = wave_incl_scan(sum) - sum;
-      int digit = 0, before = 0;
-      bool found = false;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bool hit = cb < kk && kk <= cb + c[q];
-        digit = hit ? 4 * lane + q : digit;
-        before = hit ? cb : before;
-        found = found || hit;
-        cb += c[q];
+        for (int i = 0; i < kBins / 4 / kThreads; ++i) hc[tid + i * kThreads] = uint4{0, 0, 0, 0};
       }
-      const uint64_t bal = __ballot(found);
-      const int src = bal ? static_cast<int>(__builtin_ctzll(bal)) : 0;   // exactly one lane finds it
-      digit = __builtin_amdgcn_readlane(digit, src);
-      before = __builtin_amdgcn_readlane(before, src);
+      // two levels: lane l sums bins kPer l .. kPer l + kPer - 1 and the
+      // lane holding the cut is found; then its bins, one per lane, give the
+      // digit (the cumulative counts are monotone: exactly one bin holds it)
+      constexpr int kPer = kBins / 64;
+      int sum = 0;
+#pragma unroll
+      for (int v = 0; v < kPer / 4; ++v) {
+        const uint4 x = *reinterpret_cast<const uint4*>(&h[kPer * lane + 4 * v]);
+        sum += static_cast<int>(x.x + x.y + x.z + x.w);
+      }
+      const int run = wave_incl_scan(sum) - sum;
+      const uint64_t bal = __ballot(run < kk && kk <= run + sum);
+      const int src = bal ? static_cast<int>(__builtin_ctzll(bal)) : 0;   // exactly one lane holds it
+      const int base = __builtin_amdgcn_readlane(run, src);
+      const int cq = lane < kPer ? static_cast<int>(h[kPer * src + lane]) : 0;
+      const int r2 = base + wave_incl_scan(cq) - cq;
+      const uint64_t bal2 = __ballot(lane < kPer && r2 < kk && kk <= r2 + cq);
+      const int q = bal2 ? static_cast<int>(__builtin_ctzll(bal2)) : 0;
+      const int digit = kPer * src + q;
+      const int before = __builtin_amdgcn_readlane(r2, q);
+      const int cnt = __builtin_amdgcn_readlane(cq, q);
       prefix |= static_cast<uint32_t>(digit) << shift;
       pmask |= dmask;
       kk -= before;
       top = shift - 1;
       ++pass;
+      if (kk == cnt) break;   // the whole bin is taken
     }
     thr = prefix;
-    k_eq = kk;      // how many candidates with key == thr are taken (lowest slots)
+    cmp_mask = pmask;
+    k_eq = kk;      // how many candidates whose masked key equals thr are taken (lowest slots)
   }
 
   // 4. targets in ascending slot order.  One scan of (free | equal << 16,
-  // below) gives each thread's first target index: the free targets are the
-  // first n_f free slots and the equal ones the first k_eq candidates with
-  // key == thr.
+  // below) gives each thread its first target index: the free targets are
+  // the first n_f free slots and the equal ones the first k_eq candidates
+  // whose masked key equals thr.  The owner of a target slot then writes
+  // everything about it -- the slot's new score (the chunk key's mass) and
+  // position, and the token's slot, old position, mass and list entry -- so
+  // every address has one writer and no ordering between threads is needed.
   int c_eq = 0, c_lt = 0;
   if (n_e > 0) {
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       const bool cand = (cmask >> i) & 1u;
-      c_lt += cand && key[i] < thr;
-      c_eq += cand && key[i] == thr;
+      c_lt += cand && (key[i] & cmp_mask) < thr;
+      c_eq += cand && (key[i] & cmp_mask) == thr;
     }
   }
   int p_fe, p_lt;
   block_excl_scan2(__builtin_popcount(fmask) | (c_eq << 16), c_lt, s_scan, p_fe, p_lt);
   int fr = p_fe & 0xffff, eq = p_fe >> 16;
   int j = min(fr, n_f) + p_lt + min(eq, k_eq);
-  float nsc[SPT];                      // new scores of kept slots (targets: rewritten below)
+  float nsc[SPT];
+  int npos[SPT];
+  uint32_t tmask = 0;
 #pragma unroll
   for (int i = 0; i < SPT; ++i) {
     const int m = m0 + i;
@@ -375,58 +427,56 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       t = fr < n_f;
       ++fr;
     } else if (((cmask >> i) & 1u) && n_e > 0) {
-      t = (key[i] < thr) || (key[i] == thr && eq < k_eq);
-      eq += key[i] == thr;
+      const uint32_t km = key[i] & cmp_mask;
+      t = (km < thr) || (km == thr && eq < k_eq);
+      eq += km == thr;
     }
-    if (t) s_R[j++] = fre ? (m | kWasFree) : m;
     nsc[i] = fre ? sv[i] : key_value(key[i]);
+    npos[i] = pv[i];
+    if (t) {
+      const int jj = j++;
+      const float mu = POS ? 0.f : s_mu[jj];
+      const size_t r = static_cast<size_t>(bh) * S + jj;
+      const int v = fre ? (m | kWasFree) : m;
+      nsc[i] = mu;
+      npos[i] = T + jj;
+      tmask |= 1u << i;
+      targets[r] = v;
+      if (slots_out) slots_out[r] = m;
+      if (pos_old) pos_old[r] = pv[i];
+      if (step_mass) step_mass[static_cast<size_t>(bh) * PS + M + jj] = mu;
+      if (row_bytes > 0) s_R[jj] = v;
+    }
   }
   if constexpr (POS) {
-    // scores are not kept
-  } else if (SPT % 4 == 0 && vec && m0 + SPT <= M) {
-#pragma unroll
-    for (int i = 0; i < SPT; i += 4)
-      *reinterpret_cast<float4*>(sc_h + m0 + i) = float4{nsc[i], nsc[i + 1], nsc[i + 2], nsc[i + 3]};
-  } else {
+    // scores are not kept: a written slot's score is 0, the rest untouched
 #pragma unroll
     for (int i = 0; i < SPT; ++i)
-      if (m0 + i < M && !((fmask >> i) & 1u)) sc_h[m0 + i] = nsc[i];
-  }
-  __syncthreads();                     // orders these stores before the target stores below
-
-  // 5. targets: score = mass from the chunk's own queries, position T + j
-  auto write_target = [&](int jj, float mu) __attribute__((always_inline)) {
-    const int v = s_R[jj];
-    const int slot = v & ~kWasFree;
-    sc_h[slot] = mu;
-    if (pos_old) pos_old[static_cast<size_t>(bh) * S + jj] = pos_h[slot];
-    pos_h[slot] = T + jj;
-    targets[static_cast<size_t>(bh) * S + jj] = v;
-    if (slots_out) slots_out[static_cast<size_t>(bh) * S + jj] = slot;
-    if (step_mass) step_mass[static_cast<size_t>(bh) * PS + M + jj] = mu;
-  };
+      if ((tmask >> i) & 1u) {
+        sc_h[m0 + i] = 0.f;
+        pos_h[m0 + i] = npos[i];
+      }
+  } else if constexpr (VSLOT) {
 #pragma unroll
-  for (int k = 0; k < kMuRegs; ++k) {
-    const int jj = tid + k * kThreads;
-    float mu = 0.f;
+    for (int i = 0; i < SPT; i += 4) {
+      if (m0 + i < M) {
+        *reinterpret_cast<float4*>(sc_h + m0 + i) = float4{nsc[i], nsc[i + 1], nsc[i + 2], nsc[i + 3]};
+        *reinterpret_cast<int4*>(pos_h + m0 + i) = int4{npos[i], npos[i + 1], npos[i + 2], npos[i + 3]};
+      }
+    }
+  } else {
 #pragma unroll
-    for (int r = 0; r < kMaxSplits; ++r) mu += (r < R) ? mup[k][r] : 0.f;
-    if (jj < S) write_target(jj, mu);
-  }
-  for (int jj = tid + kMuRegs * kThreads; jj < S; jj += kThreads) {
-    float part[kMaxSplits];
-#pragma unroll
-    for (int r = 0; r < kMaxSplits; ++r) part[r] = POS ? 0.f : ph[static_cast<size_t>(min(r, R - 1)) * PS + M + jj];
-    float mu = 0.f;
-#pragma unroll
-    for (int r = 0; r < kMaxSplits; ++r) mu += (r < R) ? part[r] : 0.f;
-    write_target(jj, mu);
+    for (int i = 0; i < SPT; ++i) {
+      if (m0 + i < M && !((fmask >> i) & 1u && !((tmask >> i) & 1u))) sc_h[m0 + i] = nsc[i];
+      if ((tmask >> i) & 1u) pos_h[m0 + i] = npos[i];
+    }
   }
 
   // short chunks (row_bytes > 0): the chunk's K/V rows go to their targets
-  // here, as scatter_kernel would copy them (the target list is complete in
-  // LDS since the barrier after step 4; each slot has one writer)
+  // here, as scatter_kernel would copy them (each slot has one writer; the
+  // target list is complete in LDS after the barrier)
   if (row_bytes > 0) {
+    barrier_lds();
     const int cpr = row_bytes >> 4;
     for (int idx = tid; idx < S * cpr; idx += kThreads) {
       const int jj = idx / cpr, c = idx - jj * cpr;
@@ -499,17 +549,19 @@ __global__ void reset_kernel(float* scores, int32_t* pos, int64_t n, int32_t* co
 
 }  // namespace
 
-size_t select_lds_bytes(int M, int S) {
-  (void)M;
-  return 4 * static_cast<size_t>(S) + 16;
-}
-
 bool select_copies_rows(const StepShape& sh) { return sh.S <= kSelectCopyRows; }
+
+// dynamic LDS of the select kernel: the chunk keys' masses (H2O), then the
+// target list of a chunk whose rows it copies
+size_t select_lds_bytes(const StepShape& sh) {
+  const size_t S = static_cast<size_t>(sh.S);
+  return (sh.policy == 0 ? 4 * S : 0) + (select_copies_rows(sh) ? 4 * S : 0) + 16;
+}
 
 hipError_t launch_select(const StepShape& sh, const SelectArgs& a, int dtype, hipStream_t st) {
   const int row_bytes = select_copies_rows(sh) ? sh.D * (dtype == kBF16 ? 2 : 4) : 0;
   const int n_heads = sh.B * sh.Hkv;
-  const size_t lds = select_lds_bytes(sh.M, sh.S);
+  const size_t lds = select_lds_bytes(sh);
   auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
   const bool vec = sh.M % 4 == 0 && sh.S % 4 == 0 && al16(a.scores) && al16(a.pos) && al16(a.partial);
   auto go = [&](auto kern) -> hipError_t {
@@ -520,23 +572,32 @@ hipError_t launch_select(const StepShape& sh, const SelectArgs& a, int dtype, hi
     }
     hipLaunchKernelGGL(kern, dim3(n_heads), dim3(kThreads), lds, st, a.scores, a.pos, a.partial, a.R,
                        a.targets, a.slots_out, a.pos_old, a.step_mass, a.status, a.T, sh.W, sh.S, sh.M, sh.n_cache,
-                       vec ? 1 : 0, sh.policy == 2 ? sh.n_sink : 0, static_cast<char*>(a.k_cache),
+                       sh.policy == 2 ? sh.n_sink : 0, static_cast<char*>(a.k_cache),
                        static_cast<char*>(a.v_cache), static_cast<const char*>(a.k_new),
                        static_cast<const char*>(a.v_new), static_cast<char*>(a.k_old),
                        static_cast<char*>(a.v_old), row_bytes);
     return hipGetLastError();
   };
-  // slots per thread: the smallest power of two with 512 * SPT >= M (M <= 16384)
-  auto pick = [&](auto pos_key) -> hipError_t {
-    constexpr bool P = decltype(pos_key)::value;
-    if (sh.M <= kThreads) return go(select_kernel<1, P>);
-    if (sh.M <= 2 * kThreads) return go(select_kernel<2, P>);
-    if (sh.M <= 4 * kThreads) return go(select_kernel<4, P>);
-    if (sh.M <= 8 * kThreads) return go(select_kernel<8, P>);
-    if (sh.M <= 16 * kThreads) return go(select_kernel<16, P>);
-    return go(select_kernel<32, P>);
+  // slots per thread: the smallest power of two with 512 * SPT >= M (M <= 16384);
+  // split bound: the smallest power of two >= R (0: position policy)
+  auto by_spt = [&](auto rmax, auto vv) -> hipError_t {
+    constexpr int RM = decltype(rmax)::value;
+    constexpr bool V = decltype(vv)::value;
+    if (sh.M <= kThreads) return go(select_kernel<1, RM, V>);
+    if (sh.M <= 2 * kThreads) return go(select_kernel<2, RM, V>);
+    if (sh.M <= 4 * kThreads) return go(select_kernel<4, RM, V>);
+    if (sh.M <= 8 * kThreads) return go(select_kernel<8, RM, V>);
+    if (sh.M <= 16 * kThreads) return go(select_kernel<16, RM, V>);
+    return go(select_kernel<32, RM, V>);
   };
-  return sh.policy == 0 ? pick(std::false_type{}) : pick(std::true_type{});
+  auto by_r = [&](auto vv) -> hipError_t {
+    if (sh.policy != 0) return by_spt(std::integral_constant<int, 0>{}, vv);
+    if (a.R <= 1) return by_spt(std::integral_constant<int, 1>{}, vv);
+    if (a.R <= 2) return by_spt(std::integral_constant<int, 2>{}, vv);
+    if (a.R <= 4) return by_spt(std::integral_constant<int, 4>{}, vv);
+    return by_spt(std::integral_constant<int, kMaxSplits>{}, vv);
+  };
+  return vec ? by_r(std::true_type{}) : by_r(std::false_type{});
 }
 
 hipError_t launch_scatter(const StepShape& sh, const SelectArgs& a, int dtype, hipStream_t st) {
