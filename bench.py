@@ -52,7 +52,8 @@ PEAK_HBM_GBS = 8000.0
 # cache and is not timed
 HBM_BOUND = {"decode_b32"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
-ATTN_SOURCE = os.path.join(ROOT, "kv_cache_eviction_amd", "csrc", "attn_fwd.hip")
+# the attention kernel's source: its file and the device helpers it inlines
+ATTN_SOURCES = [os.path.join(ROOT, "kv_cache_eviction_amd", "csrc", f) for f in ("attn_fwd.hip", "h2o_device.h")]
 
 
 def visible_pairs(w, c, T):
@@ -85,9 +86,12 @@ def attn_bytes(w, c, T):
     return e * (2 * B * Hq * n * d + 2 * B * Hkv * mv * d + 2 * B * Hkv * n * d) + 4 * B * Hq * n
 
 
-def source_digest(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_digest(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def recorded_traffic(kernel, workload):
@@ -101,7 +105,7 @@ def recorded_traffic(kernel, workload):
     pat = re.compile(r"^\|\s*%s\s*\|\s*%s\s*\|\s*([0-9]+)\s*\|\s*([0-9a-f]+)\s*\|" % (
         re.escape(kernel), re.escape(workload)), re.M)
     m = pat.search(text)
-    if not m or m.group(2) != source_digest(ATTN_SOURCE):
+    if not m or m.group(2) != source_digest(ATTN_SOURCES):
         return None
     return int(m.group(1))
 
