@@ -52,8 +52,18 @@ PEAK_HBM_GBS = 8000.0
 # cache and is not timed
 HBM_BOUND = {"decode_b32"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
-# the attention kernel's source: its file and the device helpers it inlines
+# the dominant kernels' sources: each file and the device helpers it inlines
 ATTN_SOURCES = [os.path.join(ROOT, "kv_cache_eviction_amd", "csrc", f) for f in ("attn_fwd.hip", "h2o_device.h")]
+FUSED_SOURCES = [os.path.join(ROOT, "kv_cache_eviction_amd", "csrc", f) for f in ("decode.hip", "h2o_device.h")]
+
+
+def takes_fused_kernel(w, policy):
+    """True when the chunk steps run the attention and the column masses in
+    one kernel: the library's rule for an H2O step (bf16, d 64 or 128, at most
+    64 query rows per KV group, at most 72 blocks of 32 keys per head once the
+    cache is full: ceil(M / 32) + ceil(S / 32))."""
+    return (w.dtype == "bf16" and policy == "h2o" and w.head_dim in (64, 128) and w.group * w.chunk <= 64
+            and (w.cache_slots + 31) // 32 + (w.chunk + 31) // 32 <= 72)
 
 
 def visible_pairs(w, c, T):
@@ -94,7 +104,7 @@ def source_digest(paths):
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(kernel, workload):
+def recorded_traffic(kernel, workload, sources=ATTN_SOURCES):
     """HBM bytes per launch from the counter runs recorded in
     profiles/hbm_traffic.md, or None if absent or taken on another version of
     the kernel source."""
@@ -105,7 +115,7 @@ def recorded_traffic(kernel, workload):
     pat = re.compile(r"^\|\s*%s\s*\|\s*%s\s*\|\s*([0-9]+)\s*\|\s*([0-9a-f]+)\s*\|" % (
         re.escape(kernel), re.escape(workload)), re.M)
     m = pat.search(text)
-    if not m or m.group(2) != source_digest(ATTN_SOURCES):
+    if not m or m.group(2) != source_digest(sources):
         return None
     return int(m.group(1))
 
@@ -348,11 +358,21 @@ def main():
             abytes.append(attn_bytes(w, c, T))
             T += w.chunk_bounds(c)[1]
         per_launch = sum(abytes[1:]) / len(abytes[1:])    # the timed launches: the chunk steps'
+        if takes_fused_kernel(w, args.policy):
+            # the kernel also writes one fp32 mass per key of every KV head
+            T, mbytes = 0, []
+            for c in range(w.n_chunks):
+                mbytes.append(4 * w.batch * w.n_kv_heads * (min(T, w.cache_slots) + w.chunk_bounds(c)[1]))
+                T += w.chunk_bounds(c)[1]
+            per_launch += sum(mbytes[1:]) / len(mbytes[1:])
+            kernel, scope, srcs = "decode_fused_kernel", "attention and column-mass kernel", FUSED_SOURCES
+        else:
+            kernel, scope, srcs = "attn_fwd_bf16_kernel", "attention kernel only", ATTN_SOURCES
         achieved = per_launch / (attn_avg_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "attn_fwd_bf16_kernel", "scope": "attention kernel only",
+        roof = {"bound": "hbm", "kernel": kernel, "scope": scope,
                 "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": recorded_traffic("attn_fwd_bf16_kernel", w.name),
+                "traffic": recorded_traffic(kernel, w.name, srcs),
                 "avg_launch_us": round(attn_avg_ms * 1e3, 3), "algorithmic_bytes_per_launch": round(per_launch)}
         metric = "H2O decode-step algorithmic HBM GB/s of the chunk steps (B32, S16, M2048)"
         unit = "GB/s"

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libh2o.so")
-SOURCES = ["attn_fwd.hip", "score.hip", "select_scatter.hip", "attn_bwd.hip", "recurrence.hip", "api.hip"]
+SOURCES = ["attn_fwd.hip", "decode.hip", "score.hip", "select_scatter.hip", "attn_bwd.hip", "recurrence.hip", "api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

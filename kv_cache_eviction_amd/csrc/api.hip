@@ -159,14 +159,24 @@ h2o_status run_step(h2o_cache* c, const void* q, const void* k, const void* v, i
 
   float* split_part = c->lay.split_bytes ? reinterpret_cast<float*>(c->ws + c->lay.split_off) : nullptr;
   h2o::AttnArgs aa{q, c->k_cache, c->v_cache, c->pos, k, v, out, lse_buf, split_part};
-  h2o_status r = timed(c, 0, st, [&] { return h2o::launch_attn_fwd(sh, aa, dtype, st); });
-  if (r != H2O_OK) return r;
-  // the position policies keep no score: no mass pass
-  const int R = sh.policy == H2O_POLICY_H2O ? h2o::score_row_splits(sh, dtype) : 0;
-  if (sh.policy == H2O_POLICY_H2O) {
-    h2o::ScoreArgs sa{q, c->k_cache, k, lse_buf, partial, R};
-    r = timed(c, 1, st, [&] { return h2o::launch_score(sh, sa, dtype, st); });
+  // short chunks: attention and masses in one pass (row splits = the halves)
+  const int halves = h2o::decode_fused_halves(sh, dtype);
+  h2o_status r;
+  int R = 0;
+  if (halves > 0) {
+    R = halves;
+    r = timed(c, 0, st, [&] { return h2o::launch_decode_fused(sh, aa, partial, st); });
     if (r != H2O_OK) return r;
+  } else {
+    r = timed(c, 0, st, [&] { return h2o::launch_attn_fwd(sh, aa, dtype, st); });
+    if (r != H2O_OK) return r;
+    // the position policies keep no score: no mass pass
+    if (sh.policy == H2O_POLICY_H2O) {
+      R = h2o::score_row_splits(sh, dtype);
+      h2o::ScoreArgs sa{q, c->k_cache, k, lse_buf, partial, R};
+      r = timed(c, 1, st, [&] { return h2o::launch_score(sh, sa, dtype, st); });
+      if (r != H2O_OK) return r;
+    }
   }
   int32_t* targets = reinterpret_cast<int32_t*>(c->ws + c->lay.targets_off);
   h2o::SelectArgs xa{c->k_cache, c->v_cache, c->scores, c->pos, k, v, partial, R, targets,

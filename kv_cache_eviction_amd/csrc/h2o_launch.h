@@ -100,6 +100,11 @@ struct RecurrenceArgs {
 enum Dtype { kBF16 = 0, kFP32 = 1 };
 
 hipError_t launch_attn_fwd(const StepShape& sh, const AttnArgs& a, int dtype, hipStream_t st);
+// Short-chunk H2O steps (decode.hip): the attention and the column masses in
+// one pass over the keys.  decode_fused_halves returns the row splits the
+// kernel writes into the masses (1 or 2), or 0 when the step does not take it.
+int decode_fused_halves(const StepShape& sh, int dtype);
+hipError_t launch_decode_fused(const StepShape& sh, const AttnArgs& a, float* partial, hipStream_t st);
 hipError_t launch_score(const StepShape& sh, const ScoreArgs& a, int dtype, hipStream_t st);
 hipError_t launch_select(const StepShape& sh, const SelectArgs& a, int dtype, hipStream_t st);
 bool select_copies_rows(const StepShape& sh);   // the select kernel also writes the K/V rows
