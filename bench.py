@@ -60,9 +60,9 @@ FUSED_SOURCES = [os.path.join(ROOT, "kv_cache_eviction_amd", "csrc", f) for f in
 def takes_fused_kernel(w, policy):
     """True when the chunk steps run the attention and the column masses in
     one kernel: the library's rule for an H2O step (bf16, d 64 or 128, at most
-    64 query rows per KV group, at most 72 blocks of 32 keys per head once the
+    512 query rows per KV group, at most 72 blocks of 32 keys per head once the
     cache is full: ceil(M / 32) + ceil(S / 32))."""
-    return (w.dtype == "bf16" and policy == "h2o" and w.head_dim in (64, 128) and w.group * w.chunk <= 64
+    return (w.dtype == "bf16" and policy == "h2o" and w.head_dim in (64, 128) and w.group * w.chunk <= 512
             and (w.cache_slots + 31) // 32 + (w.chunk + 31) // 32 <= 72)
 
 
@@ -385,9 +385,14 @@ def main():
         per_launch = sum(attn_fl) / len(attn_fl)
         achieved = per_launch / (attn_avg_ms * 1e-3) / 1e12
         peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
-        roof = {"bound": "mfma", "kernel": "attn_fwd_bf16_kernel" if w.dtype == "bf16" else "attn_fwd_f32_kernel",
-                "scope": "attention kernel only", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": recorded_traffic("attn_fwd_bf16_kernel", w.name),
+        if takes_fused_kernel(w, args.policy):
+            kernel, scope, srcs = "decode_fused_kernel", "attention and column-mass kernel", FUSED_SOURCES
+        else:
+            kernel = "attn_fwd_bf16_kernel" if w.dtype == "bf16" else "attn_fwd_f32_kernel"
+            scope, srcs = "attention kernel only", ATTN_SOURCES
+        roof = {"bound": "mfma", "kernel": kernel,
+                "scope": scope, "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": recorded_traffic(kernel, w.name, srcs),
                 "avg_launch_us": round(attn_avg_ms * 1e3, 3), "algorithmic_flops_per_launch": round(per_launch)}
         metric = "H2O chunk-step TFLOP/s + tokens/s at 64k ctx, 8B-GQA shape; % of roofline"
         if rec:

@@ -6,11 +6,13 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <initializer_list>
 #include <mutex>
 #include <vector>
 
 #include "h2o.h"
+
 #include "h2o_launch.h"
 
 // Scratch of h2o_chunk_backward_static (see below).
@@ -48,7 +50,11 @@ Layout layout_of(const h2o_config* c) {
   const size_t heads = static_cast<size_t>(c->batch) * c->n_kv_heads;
   const size_t smax = static_cast<size_t>(max_len(c));
   L.partial_off = 0;
-  L.partial_bytes = align_up(heads * h2o::score_row_splits_max() * (c->cache_slots + smax) * sizeof(float));
+  // row splits of the masses: the score kernel's, or the fused short-chunk
+  // kernel's 32-row parts
+  const size_t n_splits = static_cast<size_t>(std::max(
+      h2o::score_row_splits_max(), h2o::decode_fused_max_splits(c->n_q_heads / c->n_kv_heads, static_cast<int>(smax))));
+  L.partial_bytes = align_up(heads * n_splits * (c->cache_slots + smax) * sizeof(float));
   L.lse_off = L.partial_off + L.partial_bytes;
   L.lse_bytes = align_up(static_cast<size_t>(c->batch) * c->n_q_heads * smax * sizeof(float));
   L.targets_off = L.lse_off + L.lse_bytes;

@@ -1,6 +1,6 @@
 // Attention and H2O column masses of a short-chunk step in one pass over the
 // keys (steps 1 and 2 of h2o_chunk_step when the G*S query rows of a KV
-// group fit two 32-row halves and the head's keys fit the register stash).
+// group fit 16 parts of 32 rows and the head's keys fit the register stash).
 //
 // Method: "Learning how to Forget: Fine-tuning for Long-Context Sparse
 // Attention" (arXiv 2608.19920) -- §1 ¶1 (fixed-size KV cache), §1 ¶3
@@ -33,9 +33,9 @@
 //      gfx950 transpose load), P as the B operand straight from registers.
 //   5. The 8 waves' O^T partials are summed through LDS in wave order and
 //      the rows written; lse as the natural log.
-// The two halves of a head are dispatched 8 workgroup ids apart, so that
-// both land on one XCD (round-robin dispatch) and their identical K/V
-// streams share that XCD's L2 fills.  Every block's copy goes through
+// All halves of a head are dispatched to one XCD (round-robin dispatch,
+// ids 8 apart), so that their identical K/V streams share that XCD's L2
+// fills.  Every block's copy goes through
 // buffer_load ... lds with the row order and XOR swizzle applied on the
 // source side; rows past the end of a block re-read its last valid row
 // (masked), so masked probabilities always meet finite V.
@@ -49,6 +49,7 @@ namespace h2o {
 namespace {
 
 constexpr int kDW = 8;          // waves per workgroup
+constexpr int kDMaxHalves = 16; // 32-row parts of a KV group's rows (G*S <= 512)
 constexpr int kDNB = 9;         // 32-key blocks per wave at most (2304 keys per head)
 constexpr float kDNoMax = -1e30f;
 
@@ -83,11 +84,15 @@ __global__ __launch_bounds__(kDW * 64, 1) void decode_fused_kernel(
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, hf = lane >> 5, col = lane & 31;
+  // workgroup -> (head, half).  With 8 | n_heads, head h's halves all run on
+  // XCD h % 8 (dispatch is round-robin over the 8 XCDs), so that their
+  // identical K/V streams share that XCD's L2 fills.
   int bh, half;
-  if (halves == 2 && (n_heads & 7) == 0) {
-    const int w = blockIdx.x;
-    bh = (w >> 4) * 8 + (w & 7);
-    half = (w >> 3) & 1;
+  if ((n_heads & 7) == 0) {
+    const int w = blockIdx.x, x = w & 7, k = w >> 3;
+    const int lh = k / halves;
+    half = k - lh * halves;
+    bh = 8 * lh + x;
   } else {
     bh = static_cast<int>(blockIdx.x) / halves;
     half = static_cast<int>(blockIdx.x) - bh * halves;
@@ -464,9 +469,14 @@ int decode_fused_halves(const StepShape& sh, int dtype) {
   if (dtype != kBF16 || sh.policy != 0) return 0;
   if (sh.D != 64 && sh.D != 128) return 0;
   const int rows = sh.Hq / sh.Hkv * sh.S;
-  if (rows > 64) return 0;
+  if (rows > 32 * kDMaxHalves) return 0;
   const int nblk = (sh.n_cache + 31) / 32 + (sh.S + 31) / 32;
   if (nblk > kDW * kDNB) return 0;
+  return (rows + 31) / 32;
+}
+
+int decode_fused_max_splits(int G, int s_max) {
+  const int rows = std::min(G * s_max, 32 * kDMaxHalves);
   return (rows + 31) / 32;
 }
 

@@ -102,8 +102,10 @@ enum Dtype { kBF16 = 0, kFP32 = 1 };
 hipError_t launch_attn_fwd(const StepShape& sh, const AttnArgs& a, int dtype, hipStream_t st);
 // Short-chunk H2O steps (decode.hip): the attention and the column masses in
 // one pass over the keys.  decode_fused_halves returns the row splits the
-// kernel writes into the masses (1 or 2), or 0 when the step does not take it.
+// kernel writes into the masses (1 to 16), or 0 when the step does not take
+// it; decode_fused_max_splits bounds them over every S <= s_max.
 int decode_fused_halves(const StepShape& sh, int dtype);
+int decode_fused_max_splits(int G, int s_max);
 hipError_t launch_decode_fused(const StepShape& sh, const AttnArgs& a, float* partial, hipStream_t st);
 hipError_t launch_score(const StepShape& sh, const ScoreArgs& a, int dtype, hipStream_t st);
 hipError_t launch_select(const StepShape& sh, const SelectArgs& a, int dtype, hipStream_t st);

@@ -43,7 +43,7 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWavesSel = kThreads / 64;
-constexpr int kMaxSplits = 8;  // upper bound of the score kernel's row splits
+constexpr int kMaxSplits = 16; // upper bound of the row splits of the masses
 constexpr int kDigitBits = 11; // radix digit: 2048-bin histograms
 constexpr int kBins = 1 << kDigitBits;
 // chunks up to this length copy their K/V rows inside the select kernel (one
@@ -120,7 +120,7 @@ __device__ void block_excl_scan2(int a, int b, int* tmp, int& pa, int& pb) {
 
 // Thread t owns the SPT consecutive slots t*SPT .. t*SPT+SPT-1 (SPT*512 >= M)
 // and keeps their keys and classes in registers through every phase.
-// RMAX bounds the score pass's row splits R (1, 2, 4 or 8; R <= RMAX, splits
+// RMAX bounds the row splits R of the masses (1, 2, 4, 8 or 16; R <= RMAX, splits
 // past R re-read split R-1 and are not added); RMAX = 0 selects a position
 // policy (no masses).  VEC: M and S are multiples of 4 and the buffers are
 // 16-byte aligned, so slot rows and chunk masses move in 16-byte pieces.
@@ -595,6 +595,7 @@ hipError_t launch_select(const StepShape& sh, const SelectArgs& a, int dtype, hi
     if (a.R <= 1) return by_spt(std::integral_constant<int, 1>{}, vv);
     if (a.R <= 2) return by_spt(std::integral_constant<int, 2>{}, vv);
     if (a.R <= 4) return by_spt(std::integral_constant<int, 4>{}, vv);
+    if (a.R <= 8) return by_spt(std::integral_constant<int, 8>{}, vv);
     return by_spt(std::integral_constant<int, kMaxSplits>{}, vv);
   };
   return vec ? by_r(std::true_type{}) : by_r(std::false_type{});

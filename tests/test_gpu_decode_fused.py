@@ -1,9 +1,9 @@
 """GPU parity of short-chunk H2O steps, whose attention and column masses run
-in one kernel (at most 64 query rows G*S per KV group, at most 72 blocks of 32
-keys per head: the cache's, then the chunk's), against the fp64 oracle: every
-step, every head.
+in one kernel (at most 512 query rows G*S per KV group, in up to 16 parts of
+32 rows; at most 72 blocks of 32 keys per head: the cache's, then the
+chunk's), against the fp64 oracle: every step, every head.
 
-Shapes cover one and two 32-row halves of a group, d = 64 and 128, filled
+Shapes cover 1, 2, 7, 9 and 16 row parts of a group, d = 64 and 128, filled
 lengths that are not multiples of 32 (partial key blocks) through the fill
 phase into eviction, both workgroup-to-head mappings (head counts that are and
 are not multiples of 8), the largest cache the kernel takes and one slot more
@@ -43,6 +43,15 @@ SHAPES = {
     # single-token steps, G = 1
     "g1_s1_d64": dict(batch=2, n_q_heads=2, n_kv_heads=2, head_dim=64, prefill=33, chunk=1,
                       total_len=33 + 1 * 16, cache_slots=40, recent_window=4, qk_std=1.0),
+    # 16 row parts (128-token chunks, G = 4), 8 heads: each head's parts on one XCD
+    "g4_s128_d128_h8": dict(batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, prefill=256, chunk=128,
+                            total_len=256 + 128 * 5, cache_slots=512, recent_window=64, qk_std=1.0),
+    # 7 row parts, the last partial (200 rows)
+    "g2_s100_d64": dict(batch=2, n_q_heads=4, n_kv_heads=2, head_dim=64, prefill=150, chunk=100,
+                        total_len=150 + 100 * 4, cache_slots=300, recent_window=30, qk_std=1.0),
+    # 9 row parts (264 rows): the select sums 9 splits
+    "g8_s33_d128": dict(batch=1, n_q_heads=16, n_kv_heads=2, head_dim=128, prefill=100, chunk=33,
+                        total_len=100 + 33 * 5, cache_slots=180, recent_window=20, qk_std=1.0),
     # the largest cache the fused kernel takes: 71 cache blocks of 32 slots and
     # the chunk's block, 72 = 8 waves x 9 blocks
     "g4_s16_m2272_d64": dict(batch=1, n_q_heads=4, n_kv_heads=1, head_dim=64, prefill=2272, chunk=16,
