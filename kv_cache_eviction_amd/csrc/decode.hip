@@ -353,55 +353,60 @@ __global__ __launch_bounds__(kDW * 64, 1) void decode_fused_kernel(
   using kXor1 = std::integral_constant<int, 0xb1>;         // quad_perm [1, 0, 3, 2]
   const bool b3 = (lane & 8) != 0, b2 = (lane & 4) != 0, b1 = (lane & 2) != 0, b0 = (lane & 1) != 0;
   bf16x8 pb[kDNB][2];
+  // block i: p, its masses (written) and the bf16 B operand of PV
+  auto masses = [&](int i) __attribute__((always_inline)) {
+    const float f = fast_exp2(mb[i] - m) * inv_l;
+    float p[16];
 #pragma unroll
-  for (int i = 0; i < kDNB; ++i) {
-    if (i < nbw) {
-      const float f = fast_exp2(mb[i] - m) * inv_l;
-      float p[16];
+    for (int r = 0; r < 16; ++r) p[r] = z[i][r] * f;
+    f32x8 t0, t1;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) p[r] = z[i][r] * f;
-      f32x8 t0, t1;
+    for (int e = 0; e < 8; ++e) {
+      t0[e] = p[e];
+      t1[e] = p[8 + e];
+    }
+    pb[i][0] = to_bf16x8(t0);
+    pb[i][1] = to_bf16x8(t1);
+    float v8[8], v4[4], v2[2], v1;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        t0[e] = p[e];
-        t1[e] = p[8 + e];
-      }
-      pb[i][0] = to_bf16x8(t0);
-      pb[i][1] = to_bf16x8(t1);
-      float v8[8], v4[4], v2[2], v1;
+    for (int e = 0; e < 8; ++e) {
+      const float keep = b3 ? p[8 + e] : p[e], send = b3 ? p[e] : p[8 + e];
+      v8[e] = keep + dpp_f(send, kMirror{});
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float keep = b3 ? p[8 + e] : p[e], send = b3 ? p[e] : p[8 + e];
-        v8[e] = keep + dpp_f(send, kMirror{});
-      }
+    for (int e = 0; e < 4; ++e) {
+      const float keep = b2 ? v8[4 + e] : v8[e], send = b2 ? v8[e] : v8[4 + e];
+      v4[e] = keep + dpp_f(send, kHalfMirror{});
+    }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float keep = b2 ? v8[4 + e] : v8[e], send = b2 ? v8[e] : v8[4 + e];
-        v4[e] = keep + dpp_f(send, kHalfMirror{});
-      }
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const float keep = b1 ? v4[2 + e] : v4[e], send = b1 ? v4[e] : v4[2 + e];
-        v2[e] = keep + dpp_f(send, kXor2{});
-      }
-      {
-        const float keep = b0 ? v2[1] : v2[0], send = b0 ? v2[0] : v2[1];
-        v1 = keep + dpp_f(send, kXor1{});
-      }
-      v1 += __shfl_xor(v1, 16);
-      const int bi = wave + kDW * i;
-      const int k = 16 * hf + (lane & 15);                // key of the block this lane holds
-      if ((lane & 16) == 0) {
-        if (bi < ncb) {
-          const int slot = 32 * bi + k;
-          if (slot < n_cache) out[slot] = v1;
-        } else {
-          const int j = 32 * (bi - ncb) + k;
-          if (j < S) out[M + j] = v1;
-        }
+    for (int e = 0; e < 2; ++e) {
+      const float keep = b1 ? v4[2 + e] : v4[e], send = b1 ? v4[e] : v4[2 + e];
+      v2[e] = keep + dpp_f(send, kXor2{});
+    }
+    {
+      const float keep = b0 ? v2[1] : v2[0], send = b0 ? v2[0] : v2[1];
+      v1 = keep + dpp_f(send, kXor1{});
+    }
+    v1 += __shfl_xor(v1, 16);
+    const int bi = wave + kDW * i;
+    const int k = 16 * hf + (lane & 15);                // key of the block this lane holds
+    if ((lane & 16) == 0) {
+      if (bi < ncb) {
+        const int slot = 32 * bi + k;
+        if (slot < n_cache) out[slot] = v1;
+      } else {
+        const int j = 32 * (bi - ncb) + k;
+        if (j < S) out[M + j] = v1;
       }
     }
-  }
+  };
+  // the first kEarly blocks here; the rest inside the V pass, each before
+  // its block's wait, so that their VALU work runs while V blocks are in
+  // flight (the stash of the later blocks and O^T then share the registers)
+  constexpr int kEarly = 3;
+#pragma unroll
+  for (int i = 0; i < kEarly; ++i)
+    if (i < nbw) masses(i);
 
   // ---- 4. V pass: O^T += V^T P^T over the wave's blocks
   f32x16 o[DB];
@@ -410,6 +415,7 @@ __global__ __launch_bounds__(kDW * 64, 1) void decode_fused_kernel(
 #pragma unroll
   for (int i = 0; i < kDNB; ++i) {
     if (i < nbw) {
+      if (i >= kEarly) masses(i);
       wait_for(nbw + i);
       const char* vt = ring[wave][(nbw + i) & 1];
 #pragma unroll
