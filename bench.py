@@ -10,9 +10,13 @@ timing, so they are resident in HBM when the timed region starts.
 Reported (one JSON line): algorithmic TFLOP/s of the attention (4 d flops per
 visible (query, key) pair per query head forward, 10 d backward; the score
 pass's recompute is not counted), tokens/s, the roofline of the dominant
-kernel (attention forward: bf16 MFMA, or HBM for the decode workload) from
-HIP events recorded by the library on the launch stream, and the fp64 CPU
-oracle timed on a bounded sample of the same workload.
+kernel (attention forward, or attention and masses in one kernel for short
+chunks: bf16 MFMA, or HBM for the decode workload) from HIP events recorded
+by the library on the launch stream around the prefill's launch and every
+--event-stride-th chunk step's launch of the timed passes (a pair of event
+records costs ~5 us of GPU time, so bracketing every launch would slow the
+timed job itself), and the fp64 CPU oracle timed on a bounded sample of the
+same workload.
 
 With --recurrence (workloads with a backward): one step = the forward over
 the whole row with every chunk step's buffer delta recorded, then the
@@ -25,6 +29,7 @@ position eviction policy (no score pass; the oldest unprotected tokens go).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--recurrence]
                        [--policy h2o|recent|sink_recent] [--n-sink N] [--no-cpu-baseline]
+                       [--event-stride K]
        python bench.py --copy-probe MB    (plain copy of known size, for
                                            scaling the HBM byte counters)
 """
@@ -181,6 +186,9 @@ def main():
                     help="forward over the row, then the backward walk through the buffer")
     ap.add_argument("--policy", default="h2o", choices=["h2o", "recent", "sink_recent"])
     ap.add_argument("--n-sink", type=int, default=4, help="sink tokens of the sink_recent policy")
+    ap.add_argument("--event-stride", type=int, default=8, metavar="K",
+                    help="in the timed passes, bracket every K-th chunk step's attention launch with events "
+                         "(a pair of event records costs ~5 us of GPU time on the part)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the H2O step shards by batch or KV head with no "
@@ -270,6 +278,8 @@ def main():
             marks[0].record(stream)
         for c in range(1, w.n_chunks):
             q, k, v = chunks[c]
+            if marks is not None and timing and args.event_stride > 1:
+                h2o.h2o_set_timing(handle, timing if c % args.event_stride == 0 else False)
             if rec:
                 sl, ko, vo, po = deltas[c]
                 h2o.h2o_chunk_step(handle, cfg, q, k, v, outs[c], lses[c], slots_out=sl, k_old=ko, v_old=vo,
@@ -346,7 +356,14 @@ def main():
 
     fl = algorithmic_flops(w, backward, prefill_backward=rec)
     attn_fl = [f for kind, f in fl if kind != "backward"]
+    # the attention launches the timed passes bracketed: the prefill's (not
+    # on the HBM-bound workload) and every event_stride-th chunk step's
+    timed_c = ([] if hbm else [0]) + [c for c in range(1, w.n_chunks) if c % max(args.event_stride, 1) == 0]
     attn_avg_ms = attn_ms / max(attn_n, 1)
+    if attn_n != len(timed_c) * args.steps:
+        print(f"bench.py: {attn_n} bracketed attention launches, expected {len(timed_c) * args.steps}",
+              file=sys.stderr)
+        sys.exit(3)
     if hbm:
         # the prefill only fills the cache: time and count the chunk steps
         ms_per_step = sum(chunk_ms) / args.steps
@@ -357,14 +374,14 @@ def main():
         for c in range(w.n_chunks):
             abytes.append(attn_bytes(w, c, T))
             T += w.chunk_bounds(c)[1]
-        per_launch = sum(abytes[1:]) / len(abytes[1:])    # the timed launches: the chunk steps'
+        per_launch = sum(abytes[c] for c in timed_c) / len(timed_c)    # the bracketed chunk steps'
         if takes_fused_kernel(w, args.policy):
             # the kernel also writes one fp32 mass per key of every KV head
             T, mbytes = 0, []
             for c in range(w.n_chunks):
                 mbytes.append(4 * w.batch * w.n_kv_heads * (min(T, w.cache_slots) + w.chunk_bounds(c)[1]))
                 T += w.chunk_bounds(c)[1]
-            per_launch += sum(mbytes[1:]) / len(mbytes[1:])
+            per_launch += sum(mbytes[c] for c in timed_c) / len(timed_c)
             kernel, scope, srcs = "decode_fused_kernel", "attention and column-mass kernel", FUSED_SOURCES
         else:
             kernel, scope, srcs = "attn_fwd_bf16_kernel", "attention kernel only", ATTN_SOURCES
@@ -373,7 +390,8 @@ def main():
                 "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": recorded_traffic(kernel, w.name, srcs),
-                "avg_launch_us": round(attn_avg_ms * 1e3, 3), "algorithmic_bytes_per_launch": round(per_launch)}
+                "avg_launch_us": round(attn_avg_ms * 1e3, 3), "algorithmic_bytes_per_launch": round(per_launch),
+                "bracketed_launches": f"every {args.event_stride}th chunk step's, {attn_n} in the timed passes"}
         metric = "H2O decode-step algorithmic HBM GB/s of the chunk steps (B32, S16, M2048)"
         unit = "GB/s"
         value = round(sum(abytes[1:]) / (ms_per_step * 1e-3) / 1e9, 1)
@@ -382,7 +400,7 @@ def main():
         ms_median = None
         tflops = sum(f for _, f in fl) / (ms_per_step * 1e-3) / 1e12
         tokens = w.batch * w.total_len
-        per_launch = sum(attn_fl) / len(attn_fl)
+        per_launch = sum(attn_fl[c] for c in timed_c) / len(timed_c)
         achieved = per_launch / (attn_avg_ms * 1e-3) / 1e12
         peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
         if takes_fused_kernel(w, args.policy):
@@ -393,7 +411,9 @@ def main():
         roof = {"bound": "mfma", "kernel": kernel,
                 "scope": scope, "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": recorded_traffic(kernel, w.name, srcs),
-                "avg_launch_us": round(attn_avg_ms * 1e3, 3), "algorithmic_flops_per_launch": round(per_launch)}
+                "avg_launch_us": round(attn_avg_ms * 1e3, 3), "algorithmic_flops_per_launch": round(per_launch),
+                "bracketed_launches": f"the prefill's and every {args.event_stride}th chunk step's, "
+                                      f"{attn_n} in the timed passes"}
         metric = "H2O chunk-step TFLOP/s + tokens/s at 64k ctx, 8B-GQA shape; % of roofline"
         if rec:
             metric = ("H2O row TFLOP/s + tokens/s at %dk ctx, G=%d d=%d: forward, then the backward walk "
