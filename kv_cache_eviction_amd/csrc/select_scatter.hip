@@ -50,10 +50,6 @@ constexpr int kBins = 1 << kDigitBits;
 // workgroup per head keeps up with that little data, and a launch is saved);
 // longer chunks use the many-workgroup scatter kernel
 constexpr int kSelectCopyRows = 256;
-// 16-byte pieces of the chunk's K (and of V) rows per thread whose loads the
-// select kernel issues at its start (chunks of up to 4 * 512 pieces: 128
-// tokens at d = 128 in bf16)
-constexpr int kPreRows = 4;
 
 enum : uint8_t { kFree = 0, kCand = 1, kKeep = 2, kTarget = 4 };
 constexpr int32_t kWasFree = 0x40000000;   // flag bit of a target-list entry
@@ -238,24 +234,6 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
         for (int r = 1; r < NR; ++r) mu += (r < R) ? part[r] : 0.f;
         s_mu[jj] = mu;
       }
-    }
-  }
-
-  // Short chunks copy their K/V rows at the end (below).  When the rows fit
-  // kPreRows 16-byte pieces of K and of V per thread, their loads go out
-  // here, behind the loads above (so no wait above covers them), and land
-  // while the selection runs; only the stores remain on the critical path.
-  const int cpr = row_bytes >> 4;
-  const int n_pieces = S * cpr;
-  const bool pre = SPT <= 8 && row_bytes > 0 && n_pieces <= kPreRows * kThreads;   // (the widest variants keep their registers)
-  u32x4 kpre[kPreRows], vpre[kPreRows];
-  if (pre) {
-    const size_t src0 = static_cast<size_t>(bh) * S * row_bytes;
-#pragma unroll
-    for (int u = 0; u < kPreRows; ++u) {
-      const int idx = min(tid + u * kThreads, n_pieces - 1);
-      kpre[u] = load_u32x4(kn + src0 + 16 * static_cast<size_t>(idx));
-      vpre[u] = load_u32x4(vn + src0 + 16 * static_cast<size_t>(idx));
     }
   }
 
@@ -499,12 +477,15 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   // target list is complete in LDS after the barrier)
   if (row_bytes > 0) {
     barrier_lds();
-    auto put = [&](int idx, const u32x4& kv, const u32x4& vv) __attribute__((always_inline)) {
+    const int cpr = row_bytes >> 4;
+    for (int idx = tid; idx < S * cpr; idx += kThreads) {
       const int jj = idx / cpr, c = idx - jj * cpr;
       const int t = s_R[jj];
       const int slot = t & ~kWasFree;
       const size_t src = (static_cast<size_t>(bh) * S + jj) * row_bytes + 16 * c;
       const size_t dst = (static_cast<size_t>(bh) * M + slot) * row_bytes + 16 * c;
+      const u32x4 kv = load_u32x4(kn + src);
+      const u32x4 vv = load_u32x4(vn + src);
       if (k_old) {
         const u32x4 z = {0, 0, 0, 0};
         const bool was_free = (t & kWasFree) != 0;
@@ -513,18 +494,6 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       }
       store_u32x4(kc + dst, kv);
       store_u32x4(vc + dst, vv);
-    };
-    if (pre) {
-#pragma unroll
-      for (int u = 0; u < kPreRows; ++u) {
-        const int idx = tid + u * kThreads;
-        if (idx < n_pieces) put(idx, kpre[u], vpre[u]);
-      }
-    } else {
-      for (int idx = tid; idx < n_pieces; idx += kThreads) {
-        const size_t src = static_cast<size_t>(bh) * S * row_bytes + 16 * static_cast<size_t>(idx);
-        put(idx, load_u32x4(kn + src), load_u32x4(vn + src));
-      }
     }
   }
 }
