@@ -39,6 +39,22 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const bf16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
 }
 
+// LDS byte address of a __shared__ location, hidden from constant folding.
+// A read at lds_addr(p) + a constant then carries the constant in its 16-bit
+// offset field; without the barrier the compiler folds the array's own
+// position into that constant, and for arrays above 64 KB of LDS it then
+// spends one address add per read.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const void*)(p)));
+  asm volatile("" : "+v"(a));
+  return a;
+}
+// ds_read_b64_tr_b16 at LDS byte address a (see lds_read_tr16)
+__device__ __forceinline__ bf16x4 lds_read_tr16_at(uint32_t a) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(a));
+}
+
 // Raw buffer resource over [base, base + bytes) (gfx9 word 3): a load whose
 // offset falls past `bytes` returns zeros instead of touching memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
