@@ -227,6 +227,27 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
         }
       }
     }
+    if constexpr (D == 128) {
+      // Issue order of a tile's LDS reads against its MFMAs: 4 reads first,
+      // then 2 behind every S^T/dP^T MFMA pair and 2 behind every dQ MFMA,
+      // so that fragments are requested ahead of use (the compiler's own
+      // order waits for each one).  Measured on the wide-GQA workload: the
+      // backward per row 128.9 -> 127.6 ms.
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);       // LDS reads
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);     // MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+      }
+    }
   };
 
   using I0 = std::integral_constant<int, 0>;
