@@ -231,8 +231,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
       // Issue order of a tile's LDS reads against its MFMAs: 4 reads first,
       // then 2 behind every S^T/dP^T MFMA pair and 2 behind every dQ MFMA,
       // so that fragments are requested ahead of use (the compiler's own
-      // order waits for each one).  Measured on the wide-GQA workload: the
-      // backward per row 128.9 -> 127.6 ms.
+      // order waits for each one).  Measured at 128k context (G = 8,
+      // 2048-token chunks, 8192 slots): the backward of a row of chunks
+      // 128.9 -> 127.6 ms.
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);       // LDS reads
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
