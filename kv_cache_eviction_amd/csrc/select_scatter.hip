@@ -365,11 +365,15 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       // two levels: lane l sums bins kPer l .. kPer l + kPer - 1 and the
       // lane holding the cut is found; then its bins, one per lane, give the
       // digit (the cumulative counts are monotone: exactly one bin holds it)
+      // (each lane walks its 16-byte pieces starting at piece lane % 8: with
+      // the natural order the 64 lanes' reads, 128 bytes apart, fall in two
+      // LDS banks and serialise 32-way)
       constexpr int kPer = kBins / 64;
       int sum = 0;
 #pragma unroll
       for (int v = 0; v < kPer / 4; ++v) {
-        const uint4 x = *reinterpret_cast<const uint4*>(&h[kPer * lane + 4 * v]);
+        const int pc = (v + lane) & (kPer / 4 - 1);
+        const uint4 x = *reinterpret_cast<const uint4*>(&h[kPer * lane + 4 * pc]);
         sum += static_cast<int>(x.x + x.y + x.z + x.w);
       }
       const int run = wave_incl_scan(sum) - sum;
