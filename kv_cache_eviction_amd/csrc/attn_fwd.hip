@@ -52,6 +52,16 @@
 namespace h2o {
 namespace {
 
+// buffer_load_dword ... lds: lane i copies the 4 bytes at voff + soff of the
+// resource to LDS address lds_base + 4 i; untracked by the compiler like
+// dma16 (h2o_device.h), so only the kernel's own vmcnt waits order it.
+__device__ __forceinline__ void dma4_lds(__amdgpu_buffer_rsrc_t r, const void* lds_base, uint32_t voff,
+                                         uint32_t soff) {
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const void*)(lds_base)));
+  asm volatile("buffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(m0) : "memory");
+}
+
 constexpr int kKT = 64;        // keys per tile
 constexpr int kRowBlocks = 4;  // row blocks (32 queries of one head) per workgroup
 constexpr int kMaxKeySplits = 4;
@@ -106,6 +116,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
     constexpr int GG = decltype(g)::value, SL = decltype(sl)::value;
     return GG == 0 ? (SL == 0 ? v00 : v01) : (SL == 0 ? v10 : v11);
   };
+  // positions of the cache tiles, per wave: a ring of 4 tiles of its group
+  // (slot (local tile / 2) & 3), copied with the tile's K
+  __shared__ int s_pos[2][kRowBlocks][4][kKT];
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
 
@@ -180,7 +193,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   const bf16_t* vc_head = Vc + static_cast<size_t>(bh) * M * D;
   const bf16_t* kn_head = Kn + static_cast<size_t>(bh) * S * D;
   const bf16_t* vn_head = Vn + static_cast<size_t>(bh) * S * D;
-  const int32_t* pos_head = pos + static_cast<size_t>(bh) * M;
+  const __amdgpu_buffer_rsrc_t r_pos = make_rsrc(pos + static_cast<size_t>(bh) * M, static_cast<uint32_t>(M) * 4);
   const __amdgpu_buffer_rsrc_t rk_c = make_rsrc(kc_head, static_cast<uint32_t>(M) * RB);
   const __amdgpu_buffer_rsrc_t rv_c = make_rsrc(vc_head, static_cast<uint32_t>(M) * RB);
   const __amdgpu_buffer_rsrc_t rk_n = make_rsrc(kn_head, static_cast<uint32_t>(S) * RB);
@@ -280,10 +293,20 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
       for (int j = 0; j < NDMA; ++j) dma16(r, dst + j * 1024, clamp_row(vl + dv_soff(j), n), soff);
     }
   };
+  // Positions of local tile T's keys into this wave's ring slot, issued just
+  // before the tile's K copies (so they complete no later than K, which the
+  // tile's QK^T already waits for; the mask reads them after that).  A
+  // position read through an ordinary load would be tracked by the
+  // compiler, whose wait for it would also wait for the untracked tile
+  // copies issued after it (vmcnt retires in order).
+  auto issue_pos = [&](int T) __attribute__((always_inline)) {
+    const int Tc = T0 + min(T, n_tiles - 1);
+    dma4_lds(r_pos, s_pos[grp][rbw][(T >> 1) & 3], 4u * static_cast<uint32_t>(min(Tc * kKT + lane, M - 1)), 0u);
+  };
   // position of this lane's key in local tile T (cache tiles; -1 = free or past the end)
-  auto load_pos = [&](int T) __attribute__((always_inline)) {
+  auto pos_of = [&](int T) __attribute__((always_inline)) {
     const int key = (T0 + T) * kKT + lane;
-    const int p = pos_head[min(key, M - 1)];
+    const int p = s_pos[grp][rbw][(T >> 1) & 3][lane];
     return key < n_cache ? p : -1;
   };
 
@@ -441,9 +464,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   constexpr int kWaitPrev = 0x0f70 | (kLoadsPerIter & 15) | ((kLoadsPerIter >> 4) << 14);
   auto run_group = [&](auto g) __attribute__((always_inline)) {
     constexpr int GG = decltype(g)::value;
-    const int pos0 = load_pos(GG);
-    const int pos1 = load_pos(2 + GG);
+    issue_pos(GG);
     issue_k(GG, g, I0{});
+    issue_pos(2 + GG);
     issue_k(2 + GG, g, I1{});
     issue_v(GG, g, I0{});
     issue_v(2 + GG, g, I1{});
@@ -451,6 +474,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
     barrier_lds();
     if (!skip_tile(GG)) qk(g, I0{}, sc0, sc1);
     barrier_lds();
+    issue_pos(4 + GG);
     issue_k(4 + GG, g, I0{});
     // S^T of tile tq (K slot PN) and O += P V of tile tp (V slot par)
     auto m_phase = [&](auto par, int tq, int tp) __attribute__((always_inline)) {
@@ -479,23 +503,21 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
         pv(g, par, pb);
       }
     };
-    auto v_phase = [&](int T, int posv) __attribute__((always_inline)) {
+    auto v_phase = [&](int T) __attribute__((always_inline)) {
       if (skip_tile(T)) return;
-      mask_and_check(sc0, sc1, tile_max(sc0, sc1), T, posv);
+      mask_and_check(sc0, sc1, tile_max(sc0, sc1), T, pos_of(T));
       softmax(sc0, sc1, pb);
     };
     if constexpr (GG == 0) {
-      v_phase(0, pos0);                 // P(0)
-      int pos_n = pos1;                 // position of tile t+1
+      v_phase(0);                       // P(0)
       auto iteration = [&](int t, auto par) __attribute__((always_inline)) {
         using PN = std::integral_constant<int, decltype(par)::value ^ 1>;
         m_phase(par, 2 * (t + 1), 2 * t);
         barrier_lds();
-        const int pn = load_pos(2 * (t + 2));
+        issue_pos(2 * (t + 3));
         issue_k(2 * (t + 3), g, PN{});
         issue_v(2 * (t + 2), g, par);
-        v_phase(2 * (t + 1), pos_n);
-        pos_n = pn;
+        v_phase(2 * (t + 1));
         __builtin_amdgcn_s_waitcnt(kWaitPrev);
         barrier_lds();
       };
@@ -504,16 +526,14 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
         iteration(t + 1, I1{});
       }
     } else {
-      int pos_c = pos0, pos_n = pos1;   // positions of tiles t and t+1
       auto iteration = [&](int t, auto par) __attribute__((always_inline)) {
         using PN = std::integral_constant<int, decltype(par)::value ^ 1>;
-        v_phase(2 * t + 1, pos_c);
+        v_phase(2 * t + 1);
         __builtin_amdgcn_s_waitcnt(kWaitPrev);
         barrier_lds();
         m_phase(par, 2 * (t + 1) + 1, 2 * t + 1);
         barrier_lds();
-        pos_c = pos_n;
-        pos_n = load_pos(2 * (t + 2) + 1);
+        issue_pos(2 * (t + 3) + 1);
         issue_k(2 * (t + 3) + 1, g, PN{});
         issue_v(2 * (t + 2) + 1, g, par);
       };
