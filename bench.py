@@ -101,6 +101,16 @@ def attn_bytes(w, c, T):
     return e * (2 * B * Hq * n * d + 2 * B * Hkv * mv * d + 2 * B * Hkv * n * d) + 4 * B * Hq * n
 
 
+def state_bytes(w, c):
+    """Algorithmic HBM bytes of one step's H2O state beyond the attention:
+    every slot's score read and written back (each gains its mass), every
+    slot's position read once (filled or free, protected or not), and the
+    chunk's K/V rows and positions written into their slots."""
+    _, n = w.chunk_bounds(c)
+    e, B, Hkv, d, M = w.elem_bytes, w.batch, w.n_kv_heads, w.head_dim, w.cache_slots
+    return B * Hkv * (4 * M + 4 * M + 4 * M + 4 * n + 2 * n * d * e)
+
+
 def source_digest(paths):
     h = hashlib.sha256()
     for path in paths:
@@ -157,6 +167,20 @@ def oracle_sample(w, seed, budget_s=20.0, policy="h2o", n_sink=0):
                 tokens_per_s=tokens / elapsed)
 
 
+def plan_groups(batch, n_kv_heads, n):
+    """How N independent caches divide the workload: ("batch", B / N) when the
+    batch splits evenly and B > 1, ("heads", Hkv / N) when B == 1 and the KV
+    heads split evenly, else None.  Every (sequence, KV head) pair runs its
+    own eviction, so the groups share nothing."""
+    if n < 1:
+        return None
+    if n == 1:
+        return ("batch", batch)
+    if batch > 1:
+        return ("batch", batch // n) if batch % n == 0 else None
+    return ("heads", n_kv_heads // n) if n_kv_heads % n == 0 else None
+
+
 def copy_probe(mb):
     """A plain elementwise copy of a known size (reads mb MiB, writes mb MiB,
     three launches), so that HBM byte counters can be scaled to bytes."""
@@ -189,6 +213,9 @@ def main():
     ap.add_argument("--event-stride", type=int, default=8, metavar="K",
                     help="in the timed passes, bracket every K-th chunk step's attention launch with events "
                          "(a pair of event records costs ~5 us of GPU time on the part)")
+    ap.add_argument("--streams", type=int, default=1, metavar="N",
+                    help="run the workload's independent (sequence, KV head) pairs as N caches on N streams: "
+                         "the batch split N ways when B > 1, the KV heads when B == 1 (forward steps only)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the H2O step shards by batch or KV head with no "
@@ -210,6 +237,17 @@ def main():
         print(f"--recurrence needs a workload with a backward (not {w.name})", file=sys.stderr)
         sys.exit(2)
     n_sink = args.n_sink if args.policy == "sink_recent" else 0
+    ns = args.streams
+    split = None
+    if ns > 1:
+        if rec or backward:
+            print("--streams applies to forward-only workloads", file=sys.stderr)
+            sys.exit(2)
+        split = plan_groups(w.batch, w.n_kv_heads, ns)
+        if split is None:
+            print(f"--streams {ns} divides neither the batch ({w.batch}) nor the KV heads ({w.n_kv_heads})",
+                  file=sys.stderr)
+            sys.exit(2)
     cfg = h2o.H2OConfig(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.cache_slots,
                         w.recent_window, w.chunk, w.prefill, w.dtype, policy=args.policy, n_sink=n_sink)
     dev = torch.device("cuda:0")
@@ -320,8 +358,84 @@ def main():
             marks[1].record(stream)
         return handle
 
+    if split is not None:
+        # N caches, one per group, each on its own stream (default priority);
+        # each group's steps stay in order on its stream, the groups meet only
+        # at the pass's start and end
+        kind, per = split
+        G = w.n_q_heads // w.n_kv_heads
+        if kind == "batch":
+            cfgs = [h2o.H2OConfig(per, w.n_q_heads, w.n_kv_heads, w.head_dim, w.cache_slots, w.recent_window,
+                                  w.chunk, w.prefill, w.dtype, policy=args.policy, n_sink=n_sink)] * ns
+
+            def gview(t, g, heads):
+                return t[g * per:(g + 1) * per]
+        else:
+            cfgs = [h2o.H2OConfig(1, per * G, per, w.head_dim, w.cache_slots, w.recent_window,
+                                  w.chunk, w.prefill, w.dtype, policy=args.policy, n_sink=n_sink)] * ns
+
+            def gview(t, g, heads):
+                h = per * G if heads == "q" else per
+                return t[:, g * h:(g + 1) * h]
+        gstate = []
+        for g in range(ns):
+            cg = cfgs[g]
+            kc = torch.zeros((cg.batch, cg.n_kv_heads, M, d), dtype=cfg.torch_dtype, device=dev)
+            gstate.append(dict(
+                k_cache=kc, v_cache=torch.zeros_like(kc),
+                scores=torch.empty((cg.batch, cg.n_kv_heads, M), dtype=torch.float32, device=dev),
+                positions=torch.empty((cg.batch, cg.n_kv_heads, M), dtype=torch.int32, device=dev),
+                workspace=torch.empty(h2o.h2o_workspace_bytes(cg), dtype=torch.uint8, device=dev),
+                stream=torch.cuda.Stream(device=dev),
+                chunks=[(gview(q, g, "q"), gview(k, g, "kv"), gview(v, g, "kv"), gview(outs[c], g, "q"),
+                         gview(lses[c], g, "q")) for c, (q, k, v) in enumerate(chunks)]))
+
+        def fork():
+            ev = torch.cuda.Event()
+            ev.record(stream)
+            for gs in gstate:
+                gs["stream"].wait_event(ev)
+
+        def join():
+            for gs in gstate:
+                ev = torch.cuda.Event()
+                ev.record(gs["stream"])
+                stream.wait_event(ev)
+
+        def one_pass(timing, marks=None, bwd_timing=False):
+            fork()
+            hds = []
+            for g, gs in enumerate(gstate):
+                hd = h2o.h2o_cache_init(cfgs[g], gs["k_cache"], gs["v_cache"], gs["scores"], gs["positions"],
+                                        gs["workspace"], stream=gs["stream"])
+                if timing and not hbm:
+                    h2o.h2o_set_timing(hd, timing)
+                q, k, v, o, l = gs["chunks"][0]
+                h2o.h2o_prefill(hd, cfgs[g], q, k, v, o, l, gs["stream"])
+                if timing and hbm:
+                    h2o.h2o_set_timing(hd, timing)
+                hds.append(hd)
+            if marks is not None:
+                join()
+                marks[0].record(stream)
+                fork()
+            for c in range(1, w.n_chunks):
+                for g, gs in enumerate(gstate):
+                    if marks is not None and timing and args.event_stride > 1:
+                        h2o.h2o_set_timing(hds[g], timing if c % args.event_stride == 0 else False)
+                    q, k, v, o, l = gs["chunks"][c]
+                    h2o.h2o_chunk_step(hds[g], cfgs[g], q, k, v, o, l, stream=gs["stream"])
+            join()
+            if marks is not None:
+                marks[1].record(stream)
+            return hds
+
+    def handles_of(r):
+        return r if isinstance(r, list) else [r]
+
     for _ in range(args.warmup):
-        h2o.h2o_cache_destroy(one_pass(None))
+        for hd in handles_of(one_pass(None)):
+            h2o.h2o_cache_destroy(hd)
     torch.cuda.synchronize()
     # timed region: only the attention kernel is bracketed with library events
     # (two extra stream records per step); the chunk steps of each pass are
@@ -331,7 +445,7 @@ def main():
     handles = []
     t0 = time.perf_counter()
     for i in range(args.steps):
-        handles.append(one_pass(["attn_fwd"], marks[i]))
+        handles.extend(handles_of(one_pass(["attn_fwd"], marks[i])))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     chunk_ms = sorted(a.elapsed_time(b) for a, b in marks)     # chunk steps of each pass
@@ -344,13 +458,13 @@ def main():
 
     # per-kernel breakdown: one more pass with every kernel bracketed (outside
     # the timed region; its event records slow that pass slightly)
-    hd = one_pass(True, bwd_timing=backward)
+    hds = handles_of(one_pass(True, bwd_timing=backward))
     torch.cuda.synchronize()
     step_ms = {}
     for name in ("attn_fwd", "score", "select", "scatter", "reset"):
-        ms, _ = h2o.h2o_get_timing(hd, name)
-        step_ms[name] = ms
-    h2o.h2o_cache_destroy(hd)
+        step_ms[name] = sum(h2o.h2o_get_timing(hd, name)[0] for hd in hds)
+    for hd in hds:
+        h2o.h2o_cache_destroy(hd)
     if backward:
         step_ms["backward"] = sum(a.elapsed_time(b) for a, b in bwd_marks)
 
@@ -360,8 +474,8 @@ def main():
     # on the HBM-bound workload) and every event_stride-th chunk step's
     timed_c = ([] if hbm else [0]) + [c for c in range(1, w.n_chunks) if c % max(args.event_stride, 1) == 0]
     attn_avg_ms = attn_ms / max(attn_n, 1)
-    if attn_n != len(timed_c) * args.steps:
-        print(f"bench.py: {attn_n} bracketed attention launches, expected {len(timed_c) * args.steps}",
+    if attn_n != len(timed_c) * args.steps * ns:
+        print(f"bench.py: {attn_n} bracketed attention launches, expected {len(timed_c) * args.steps * ns}",
               file=sys.stderr)
         sys.exit(3)
     if hbm:
@@ -385,22 +499,31 @@ def main():
             kernel, scope, srcs = "decode_fused_kernel", "attention and column-mass kernel", FUSED_SOURCES
         else:
             kernel, scope, srcs = "attn_fwd_bf16_kernel", "attention kernel only", ATTN_SOURCES
+        per_launch /= ns                   # each group's launch covers 1/N of the pairs
         achieved = per_launch / (attn_avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": kernel, "scope": scope,
                 "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": recorded_traffic(kernel, w.name, srcs),
+                "traffic": recorded_traffic(kernel, w.name, srcs) if ns == 1 else None,
                 "avg_launch_us": round(attn_avg_ms * 1e3, 3), "algorithmic_bytes_per_launch": round(per_launch),
-                "bracketed_launches": f"every {args.event_stride}th chunk step's, {attn_n} in the timed passes"}
+                "bracketed_launches": f"every {args.event_stride}th chunk step's, {attn_n} in the timed passes",
+                **({"concurrent_streams": ns} if ns > 1 else {})}
         metric = "H2O decode-step algorithmic HBM GB/s of the chunk steps (B32, S16, M2048)"
         unit = "GB/s"
         value = round(sum(abytes[1:]) / (ms_per_step * 1e-3) / 1e9, 1)
+        # the same steps with the H2O state they read and write counted too
+        step_bytes = sum(abytes[1:]) + sum(state_bytes(w, c) for c in range(1, w.n_chunks))
+        with_state = {"value": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1), "unit": "GB/s",
+                      "bytes_per_step": round(step_bytes / w.n_steps),
+                      "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                      "counts": "the attention's bytes plus every slot's score read and written, every "
+                                "slot's position read, the chunk's K/V rows and positions written"}
     else:
         ms_per_step = wall * 1e3 / args.steps
         ms_median = None
         tflops = sum(f for _, f in fl) / (ms_per_step * 1e-3) / 1e12
         tokens = w.batch * w.total_len
-        per_launch = sum(attn_fl[c] for c in timed_c) / len(timed_c)
+        per_launch = sum(attn_fl[c] for c in timed_c) / len(timed_c) / ns
         achieved = per_launch / (attn_avg_ms * 1e-3) / 1e12
         peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
         if takes_fused_kernel(w, args.policy):
@@ -410,10 +533,11 @@ def main():
             scope, srcs = "attention kernel only", ATTN_SOURCES
         roof = {"bound": "mfma", "kernel": kernel,
                 "scope": scope, "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": recorded_traffic(kernel, w.name, srcs),
+                "frac": round(achieved / peak, 4), "traffic": recorded_traffic(kernel, w.name, srcs) if ns == 1 else None,
                 "avg_launch_us": round(attn_avg_ms * 1e3, 3), "algorithmic_flops_per_launch": round(per_launch),
                 "bracketed_launches": f"the prefill's and every {args.event_stride}th chunk step's, "
-                                      f"{attn_n} in the timed passes"}
+                                      f"{attn_n} in the timed passes",
+                **({"concurrent_streams": ns} if ns > 1 else {})}
         metric = "H2O chunk-step TFLOP/s + tokens/s at 64k ctx, 8B-GQA shape; % of roofline"
         if rec:
             metric = ("H2O row TFLOP/s + tokens/s at %dk ctx, G=%d d=%d: forward, then the backward walk "
@@ -452,6 +576,8 @@ def main():
             "head_dim": w.head_dim, "prefill": w.prefill, "chunk": w.chunk, "total_len": w.total_len,
             "cache_slots": w.cache_slots, "recent_window": w.recent_window, "policy": args.policy,
             **({"n_sink": n_sink} if n_sink else {}),
+            **({"streams": ns, "groups": "%d caches of %s" % (ns, "%d sequences" % split[1] if split[0] == "batch"
+                                                              else "%d KV heads" % split[1])} if ns > 1 else {}),
             "step": ("cache reset + prefill + %d chunk steps recording their buffer deltas, then the "
                      "backward walk over all %d steps (last first)" % (w.n_steps, w.n_chunks)) if rec else
                     "%s + %d chunk steps%s" % (
@@ -463,6 +589,7 @@ def main():
         "roofline": roof,
         # the whole step against the same peak (roofline.frac covers the attention kernel only)
         "step_roofline_frac": round(value / (PEAK_HBM_GBS if hbm else roof["peak"]), 4),
+        **({"step_with_state": with_state} if hbm else {}),
         **({"backward_executed": {
             "kernels": "bwd_dq + bwd_dkdv + chunk reduce" + (" + undo + route" if rec else ""),
             "ms_per_step": round(step_ms["backward"], 3),

@@ -90,3 +90,43 @@ def test_recorded_traffic_requires_the_counted_source(tmp_path, monkeypatch):
     assert bench.recorded_traffic("attn_fwd_bf16_kernel", "llama8b_64k") == 123456
     assert bench.recorded_traffic("attn_fwd_bf16_kernel", "llama8b_128k") is None    # other source
     assert bench.recorded_traffic("attn_fwd_bf16_kernel", "decode_b32") is None      # not recorded
+
+
+@pytest.mark.parametrize("batch,heads,n,expect", [
+    (32, 8, 1, ("batch", 32)),
+    (32, 8, 2, ("batch", 16)),
+    (32, 8, 4, ("batch", 8)),
+    (32, 8, 3, None),              # 32 sequences do not split 3 ways
+    (1, 8, 2, ("heads", 4)),       # one sequence: its KV heads split
+    (1, 8, 8, ("heads", 1)),
+    (1, 8, 3, None),
+    (2, 8, 4, None),               # B > 1 splits the batch only
+    (4, 8, 0, None),
+])
+def test_stream_groups_partition_the_pairs(batch, heads, n, expect):
+    assert bench.plan_groups(batch, heads, n) == expect
+    if expect is not None:
+        kind, per = expect
+        # the groups cover every (sequence, KV head) pair once
+        total = per * n * (heads if kind == "batch" else batch) if n > 1 else batch * heads
+        assert total == batch * heads
+
+
+def test_streams_refuse_workloads_with_a_backward():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "widegqa_128k",
+                        "--streams", "2"], capture_output=True, text=True, timeout=300,
+                       env={**os.environ, "HIP_VISIBLE_DEVICES": ""})
+    assert r.returncode == 2
+    assert "forward-only" in r.stderr
+
+
+def test_state_bytes_count_each_state_tensor_once():
+    w = wl.workload("decode_b32", total_len=2048 + 3 * 16)
+    for c in range(1, w.n_chunks):
+        _, n = w.chunk_bounds(c)
+        per_head = (w.cache_slots * 4          # scores read
+                    + w.cache_slots * 4        # scores written back
+                    + w.cache_slots * 4        # positions read
+                    + n * 4                    # the chunk's positions written
+                    + 2 * n * w.head_dim * 2)  # its K and V rows written (bf16)
+        assert bench.state_bytes(w, c) == w.batch * w.n_kv_heads * per_head
