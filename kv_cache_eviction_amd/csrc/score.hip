@@ -22,7 +22,12 @@
 //   * Rows: a cache-key tile takes every (query head, query) row of the KV
 //     group; a chunk-key tile only the rows whose query index reaches its
 //     first key, so no staged block is wasted.  Rows are numbered g * L + i
-//     over the needed queries and split into R contiguous ranges.
+//     over the needed queries and split into contiguous ranges: R for a
+//     cache tile, and for a chunk tile the share of R its rows call for
+//     (chunk_tile_splits), so that every workgroup holds about the same
+//     number of blocks.  The last split of a chunk tile writes zeros into
+//     the partial rows it does not use, so the select still adds R partials
+//     per column.
 //   * Query blocks reach LDS through direct copies (buffer_load ... lds)
 //     into a 3-stage ring, the row swizzle applied on the source side; the
 //     rows' lse values are staged one block ahead through registers.
@@ -45,6 +50,16 @@ constexpr int kRB = 64;         // query rows per staged block (2 MFMA row block
 constexpr int kStages = 3;
 constexpr int kRowSplitsMax = 8;     // the select kernel sums up to this many splits
 
+// Row splits of chunk tile tp (keys 256 tp ..) when a cache tile takes R:
+// R scaled by the tile's share of the 64-row blocks of a cache tile (whose
+// G * S rows are the most any tile has), rounded up, at least 1.
+__host__ __device__ inline int chunk_tile_splits(int R, int G, int S, int tp) {
+  const int n_c = (G * S + kRB - 1) / kRB;
+  const int n_t = (G * (S - kCT * tp) + kRB - 1) / kRB;
+  const int r = (R * n_t + n_c - 1) / n_c;
+  return r < 1 ? 1 : (r > R ? R : r);
+}
+
 template <int CPR>
 __device__ __forceinline__ int q_chunk(int row, int c) { return c ^ (row & (CPR - 1)); }
 
@@ -53,7 +68,7 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc,
     const bf16_t* __restrict__ Kn, const float* __restrict__ lse,
     float* __restrict__ partial, int Hq, int Hkv, int S, int M, int n_cache, float c2,
-    int n_heads, int n_ct, int n_tiles, int R) {
+    int n_heads, int n_ct, int n_jt, int R) {
   constexpr int DS = D / 16;
   constexpr int CPR = D / 8;
   constexpr int RBY = 2 * D;                  // bytes per query row
@@ -71,10 +86,31 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, hf = lane >> 5, col = lane & 31;
   const int bh = blockIdx.x % n_heads;
-  const int rest = static_cast<int>(blockIdx.x) / n_heads;
-  const int tile = rest % n_tiles, split = rest / n_tiles;
   const int b = bh / Hkv, kvh = bh - b * Hkv;
   const int G = Hq / Hkv;
+  // workgroup -> (tile, split): the n_ct cache tiles' R splits each, then
+  // the chunk tiles' chunk_tile_splits each (the host sized the grid so)
+  int tile, split, n_split;
+  {
+    int u = static_cast<int>(blockIdx.x) / n_heads;
+    if (u < n_ct * R) {
+      tile = u / R;
+      split = u - tile * R;
+      n_split = R;
+    } else {
+      u -= n_ct * R;
+      int tp = 0;
+      n_split = chunk_tile_splits(R, G, S, 0);
+      while (u >= n_split && tp + 1 < n_jt) {
+        u -= n_split;
+        ++tp;
+        n_split = chunk_tile_splits(R, G, S, tp);
+      }
+      tile = n_ct + tp;
+      split = u;
+    }
+  }
+  if (split >= n_split) return;
   const bool is_cache = tile < n_ct;
   const int base = (is_cache ? tile : tile - n_ct) * kCT;
   const int lim = is_cache ? n_cache : S;
@@ -101,8 +137,8 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
   const int L = S - i_off;
   const int n_need = G * L;
   const int n_blk = (n_need + kRB - 1) / kRB;
-  const int blk_lo = static_cast<int>(static_cast<int64_t>(split) * n_blk / R);
-  const int blk_hi = static_cast<int>(static_cast<int64_t>(split + 1) * n_blk / R);
+  const int blk_lo = static_cast<int>(static_cast<int64_t>(split) * n_blk / n_split);
+  const int blk_hi = static_cast<int>(static_cast<int64_t>(split + 1) * n_blk / n_split);
   const float invL = 1.f / static_cast<float>(L);
   // row u (< n_need) -> row g * S + i of the group's Q / lse
   // (u < G L <= 2^20 and every product stays below 2^24: 24-bit multiplies)
@@ -325,6 +361,14 @@ __global__ __launch_bounds__(256, 2) void score_bf16_kernel(
     const int k0 = key0 + col, k1 = key0 + 32 + col;
     if (k0 < lim) out[k0] = t0;
     if (k1 < lim) out[k1] = t1;
+    // a chunk tile with fewer splits than R: its unused partial rows are zero
+    if (split == n_split - 1) {
+      for (int s2 = n_split; s2 < R; ++s2) {
+        float* z = out + static_cast<size_t>(s2 - split) * PS;
+        if (k0 < lim) z[k0] = 0.f;
+        if (k1 < lim) z[k1] = 0.f;
+      }
+    }
   }
 }
 
@@ -530,22 +574,33 @@ int score_tiles(const StepShape& sh, int dtype) {
   return (sh.n_cache + ct - 1) / ct + (sh.S + ct - 1) / ct;
 }
 
+// Workgroups of one (b, KV head) of the bf16 score kernel for row splits R:
+// R per cache tile, chunk_tile_splits per chunk tile.
+int64_t score_head_workgroups(const StepShape& sh, int R) {
+  const int G = sh.Hq / sh.Hkv;
+  const int n_ct = (sh.n_cache + kCT - 1) / kCT, n_jt = (sh.S + kCT - 1) / kCT;
+  int64_t n = static_cast<int64_t>(n_ct) * R;
+  for (int tp = 0; tp < n_jt; ++tp) n += chunk_tile_splits(R, G, sh.S, tp);
+  return n;
+}
+
 // Row splits R: a workgroup costs a start-up of about kStartBlocks block
 // times (K fragments, first copies) plus one block time per 64-row block
 // when it has its CU to itself, two per block beside a second resident
 // workgroup.  R minimises the start-ups of the rounds of two workgroups per
-// CU plus the blocks queued on the busiest CU (measured on 256 CUs: the 64k
-// shape's best R is 5, 128-token chunks' 3).
+// CU plus the blocks queued on the busiest CU, the largest workgroup (a cache
+// tile's, or a chunk tile's when there is no cache yet) times the
+// workgroups per CU.
 int score_row_splits(const StepShape& sh, int dtype) {
   if (dtype != kBF16) return 1;
   constexpr int kStartBlocks = 4;
   const int64_t n_cu = sh.n_cu;
-  const int64_t ht = static_cast<int64_t>(sh.B) * sh.Hkv * score_tiles(sh, dtype);
+  const int64_t heads = static_cast<int64_t>(sh.B) * sh.Hkv;
   const int n_blk = (sh.Hq / sh.Hkv * sh.S + kRB - 1) / kRB;
   int best = 1;
   int64_t best_cost = INT64_MAX;
   for (int R = 1; R <= kRowSplitsMax && R <= n_blk; ++R) {
-    const int64_t n_wg = ht * R;
+    const int64_t n_wg = heads * score_head_workgroups(sh, R);
     const int64_t cost = kStartBlocks * ((n_wg + 2 * n_cu - 1) / (2 * n_cu)) +
                          static_cast<int64_t>((n_blk + R - 1) / R) * ((n_wg + n_cu - 1) / n_cu);
     if (cost < best_cost) {
@@ -572,13 +627,13 @@ hipError_t launch_score(const StepShape& sh, const ScoreArgs& a, int dtype, hipS
 #undef H2O_LAUNCH_SCORE_DEC
   } else if (dtype == kBF16) {
     const int n_ct = (sh.n_cache + kCT - 1) / kCT;
-    const int n_tiles = n_ct + (sh.S + kCT - 1) / kCT;
-    const dim3 grid(n_heads * n_tiles * a.R), block(256);
+    const int n_jt = (sh.S + kCT - 1) / kCT;
+    const dim3 grid(static_cast<unsigned>(n_heads * score_head_workgroups(sh, a.R))), block(256);
 #define H2O_LAUNCH_SCORE(DD)                                                                      \
   hipLaunchKernelGGL(score_bf16_kernel<DD>, grid, block, 0, st, static_cast<const bf16_t*>(a.q), \
                      static_cast<const bf16_t*>(a.k_cache), static_cast<const bf16_t*>(a.k_new), \
                      a.lse, a.partial, sh.Hq, sh.Hkv, sh.S, sh.M, sh.n_cache, c2, n_heads, n_ct, \
-                     n_tiles, a.R)
+                     n_jt, a.R)
     if (sh.D == 128) H2O_LAUNCH_SCORE(128);
     else H2O_LAUNCH_SCORE(64);
 #undef H2O_LAUNCH_SCORE
