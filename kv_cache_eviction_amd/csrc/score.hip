@@ -569,14 +569,9 @@ __global__ __launch_bounds__(64) void score_f32_kernel(
 
 int score_row_splits_max() { return kRowSplitsMax; }
 
-int score_tiles(const StepShape& sh, int dtype) {
-  const int ct = dtype == kBF16 ? kCT : 64;
-  return (sh.n_cache + ct - 1) / ct + (sh.S + ct - 1) / ct;
-}
-
 // Workgroups of one (b, KV head) of the bf16 score kernel for row splits R:
 // R per cache tile, chunk_tile_splits per chunk tile.
-int64_t score_head_workgroups(const StepShape& sh, int R) {
+static int64_t score_head_workgroups(const StepShape& sh, int R) {
   const int G = sh.Hq / sh.Hkv;
   const int n_ct = (sh.n_cache + kCT - 1) / kCT, n_jt = (sh.S + kCT - 1) / kCT;
   int64_t n = static_cast<int64_t>(n_ct) * R;
