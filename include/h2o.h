@@ -291,8 +291,17 @@ H2O_API size_t h2o_recurrence_workspace_bytes(const h2o_config* cfg, int32_t s);
 /* Tokens seen so far (T). */
 H2O_API int64_t h2o_tokens_seen(const h2o_cache* c);
 
-/* Synchronises `stream`, returns the device status word in *flags (bit 0:
- * an adopted state had too few evictable slots) and clears it. */
+/* Synchronises `stream`, returns the device status word in *flags and
+ * clears it.  Bit 0: an adopted state had too few evictable slots.  Bit 1:
+ * in a step whose selection ran in several workgroups per (b, KV head)
+ * (chunks of 257..4096 tokens), the workgroup that rewrites the head's scores
+ * and positions waited past its bound (about a second) for the others to
+ * finish reading them, and wrote anyway; that step's eviction is then not
+ * guaranteed.  Normal steps never set it.  For tests of that bounded wait
+ * only, h2o_cache_init reads two environment variables: H2O_SELECT_SPIN_LIMIT
+ * (polls before giving up; unset or 0: the default) and H2O_SELECT_SYNC_SKEW
+ * (added to the count of reads the wait expects, which makes it wait out its
+ * bound). */
 H2O_API h2o_status h2o_device_status(h2o_cache* c, void* stream, int32_t* flags);
 
 /* Per-kernel timing with HIP events recorded on the launch stream around

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <initializer_list>
 #include <mutex>
 #include <vector>
@@ -37,7 +38,7 @@ struct Layout {
   size_t partial_off, partial_bytes;
   size_t lse_off, lse_bytes;
   size_t targets_off, targets_bytes;     // target slot list of the current step
-  size_t counters_off, counters_bytes;   // the device status word
+  size_t counters_off, counters_bytes;   // the device status word, then one read counter per (b, KV head)
   size_t split_off, split_bytes;         // attention key-split partial states
   size_t n_counters;                     // ints cleared at init
   size_t total;
@@ -60,7 +61,7 @@ Layout layout_of(const h2o_config* c) {
   L.targets_off = L.lse_off + L.lse_bytes;
   L.targets_bytes = align_up(heads * smax * sizeof(int32_t));
   L.counters_off = L.targets_off + L.targets_bytes;
-  L.n_counters = 1;
+  L.n_counters = 1 + heads;
   L.counters_bytes = align_up(L.n_counters * sizeof(int32_t));
   L.split_off = L.counters_off + L.counters_bytes;
   L.split_bytes = c->dtype == H2O_BF16 ? align_up(h2o::attn_split_bytes(c->batch, c->n_q_heads, static_cast<int>(smax), c->head_dim)) : 0;
@@ -88,6 +89,9 @@ struct h2o_cache {
   int n_cu;            // compute units of the device current at h2o_cache_init
   int32_t last_hip_error;
   uint32_t timing_mask;      // bit k: bracket kernel id k with events
+  uint32_t sync_target;      // running total of the select parts' reads (see select_scatter.hip)
+  uint32_t spin_limit;       // bound of the select's wait (0: the library default)
+  uint32_t sync_skew;        // added to the expected total (tests of the bounded wait only)
   std::vector<TimedLaunch> pending;
   std::vector<hipEvent_t> event_pool;
   double total_ms[kTimedKernels];
@@ -186,7 +190,11 @@ h2o_status run_step(h2o_cache* c, const void* q, const void* k, const void* v, i
   }
   int32_t* targets = reinterpret_cast<int32_t*>(c->ws + c->lay.targets_off);
   h2o::SelectArgs xa{c->k_cache, c->v_cache, c->scores, c->pos, k, v, partial, R, targets,
-                     slots_out, pos_old, step_mass, k_old, v_old, status, static_cast<int32_t>(c->T)};
+                     slots_out, pos_old, step_mass, k_old, v_old, status, static_cast<int32_t>(c->T),
+                     reinterpret_cast<uint32_t*>(status + 1), 0u, c->spin_limit};
+  // every part but the first adds one read to its head's counter
+  c->sync_target += static_cast<uint32_t>(h2o::select_parts(sh) - 1);
+  xa.sync_target = c->sync_target + c->sync_skew;
   r = timed(c, 2, st, [&] { return h2o::launch_select(sh, xa, dtype, st); });
   if (r != H2O_OK) return r;
   if (!h2o::select_copies_rows(sh)) {
@@ -326,6 +334,12 @@ h2o_status h2o_cache_init(const h2o_config* cfg, void* k_cache, void* v_cache, f
   c->filled = adopt ? -1 : 0;
   c->last_hip_error = 0;
   c->timing_mask = 0;
+  c->sync_target = 0;
+  // test-only knobs of the select's bounded wait (unset in normal use)
+  c->spin_limit = 0;
+  c->sync_skew = 0;
+  if (const char* e = getenv("H2O_SELECT_SPIN_LIMIT")) c->spin_limit = static_cast<uint32_t>(strtoul(e, nullptr, 10));
+  if (const char* e = getenv("H2O_SELECT_SYNC_SKEW")) c->sync_skew = static_cast<uint32_t>(strtoul(e, nullptr, 10));
   for (int i = 0; i < kTimedKernels; ++i) {
     c->total_ms[i] = 0.0;
     c->launches[i] = 0;

@@ -59,6 +59,9 @@ struct SelectArgs {
   void* v_old;          // nullable
   int32_t* status;      // device status word
   int32_t T;            // tokens seen before the chunk
+  uint32_t* sync;       // [B*Hkv] counters of the parts' reads (workspace, zeroed at init)
+  uint32_t sync_target; // running total of those reads once this step's are done
+  uint32_t spin_limit;  // bound of part 0's wait (0: the library's default)
 };
 
 struct BackwardArgs {
@@ -110,6 +113,7 @@ hipError_t launch_decode_fused(const StepShape& sh, const AttnArgs& a, float* pa
 hipError_t launch_score(const StepShape& sh, const ScoreArgs& a, int dtype, hipStream_t st);
 hipError_t launch_select(const StepShape& sh, const SelectArgs& a, int dtype, hipStream_t st);
 bool select_copies_rows(const StepShape& sh);   // the select kernel also writes the K/V rows
+int select_parts(const StepShape& sh);          // select workgroups per (b, KV head)
 hipError_t launch_scatter(const StepShape& sh, const SelectArgs& a, int dtype, hipStream_t st);
 hipError_t launch_backward(const StepShape& sh, const BackwardArgs& a, hipStream_t st);
 size_t backward_workspace_bytes(int B, int Hq, int Hkv, int S, int D);

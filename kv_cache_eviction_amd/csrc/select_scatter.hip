@@ -17,9 +17,8 @@
 // the key, so the oldest candidates go; positions below n_sink are never
 // candidates; no score is read, and a written slot gets score 0.
 //
-// Two kernels.  The select kernel runs one 512-thread workgroup per
-// (b, KV head): no other workgroup reads or writes that head's scores,
-// positions or slots, so it needs no inter-workgroup synchronisation.  It
+// Two kernels.  The select kernel runs P 512-thread workgroups ("parts")
+// per (b, KV head), each of which
 //   1. adds the score kernel's R per-split masses to the filled slots'
 //      scores (fixed split order: deterministic);
 //   2. selects the targets: scores map to order-preserving 32-bit keys, the
@@ -29,10 +28,19 @@
 //      whole) find the n_e-th smallest key; equal keys resolve to the lowest
 //      slot through one exclusive scan in slot order;
 //   3. writes scores, positions and the target list R (with a flag for
-//      targets that were free).
-// The scatter kernel then copies the chunk's K/V rows into their slots with
-// many workgroups per head (a pure bandwidth copy, 16-byte accesses); chunks
-// of at most kSelectCopyRows tokens are copied by the select kernel itself.
+//      targets that were free) -- part 0 only;
+//   4. copies its share of the chunk's K/V rows (tokens part * S / P ..)
+//      into their target slots.
+// Every part computes the whole selection from the same inputs, so they
+// agree bit for bit; the only exchange between them is a per-head counter:
+// part p > 0 adds one to it once its reads of the old scores and positions
+// are done, and part 0 rewrites those arrays only after the counter has
+// reached the running total of reads the host expects.  That wait is
+// bounded: past kSelectSpin polls part 0 sets bit 1 of the status word and
+// writes anyway.  Chunks longer than kSelectPartRows tokens (whose target
+// lists would not fit LDS) keep one part that copies no rows, and the
+// scatter kernel copies them with many workgroups per head.
+#include <algorithm>
 #include <type_traits>
 
 #include "h2o_device.h"
@@ -50,6 +58,16 @@ constexpr int kBins = 1 << kDigitBits;
 // workgroup per head keeps up with that little data, and a launch is saved);
 // longer chunks use the many-workgroup scatter kernel
 constexpr int kSelectCopyRows = 256;
+// longer chunks, up to this length, are selected by several parts per head
+// that each copy a share of the rows; beyond it the scatter kernel copies
+constexpr int kSelectPartRows = 4096;
+// bound of part 0's wait for the other parts' reads: polls of a device-scope
+// load and a short sleep, about 1 us each, so about a second in all (in a
+// normal step the other parts have read long before part 0 asks; they only
+// need a CU slot, and none of them waits on anything)
+constexpr uint32_t kSelectSpin = 1u << 20;
+// 16-byte pieces of chunk rows per thread loaded at the start of the select
+constexpr int kRowPre = 4;
 
 enum : uint8_t { kFree = 0, kCand = 1, kKeep = 2, kTarget = 4 };
 constexpr int32_t kWasFree = 0x40000000;   // flag bit of a target-list entry
@@ -131,7 +149,8 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     int32_t* __restrict__ pos_old, float* __restrict__ step_mass, int32_t* __restrict__ status, int T, int W,
     int S, int M, int n_cache, int n_floor, char* __restrict__ kc, char* __restrict__ vc,
     const char* __restrict__ kn, const char* __restrict__ vn, char* __restrict__ k_old,
-    char* __restrict__ v_old, int row_bytes) {
+    char* __restrict__ v_old, int row_bytes, int parts, uint32_t* __restrict__ sync, uint32_t sync_target,
+    uint32_t spin_limit) {
   constexpr bool POS = RMAX == 0;
   constexpr int NR = POS ? 1 : RMAX;
   constexpr bool VSLOT = VEC && SPT % 4 == 0;
@@ -143,13 +162,39 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   __shared__ int s_scan[2 * kWavesSel];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int bh = blockIdx.x;
+  // workgroup -> (head, part): the parts of a head share its XCD when the
+  // head count is a multiple of 8 (round-robin dispatch), so their reads of
+  // the same scores and masses hit one L2
+  const int n_heads = static_cast<int>(gridDim.x) / parts;
+  const int bh = static_cast<int>(blockIdx.x) % n_heads;
+  const int part = static_cast<int>(blockIdx.x) / n_heads;
   const size_t PS = static_cast<size_t>(M) + S;
   const float* ph = partial + static_cast<size_t>(bh) * R * PS;
   float* sc_h = scores + static_cast<size_t>(bh) * M;
   int32_t* pos_h = pos + static_cast<size_t>(bh) * M;
   const int m0 = tid * SPT;
   auto split_of = [&](int r) __attribute__((always_inline)) { return static_cast<size_t>(min(r, R - 1)) * PS; };
+
+  // this part's tokens and their K/V rows' 16-byte pieces; the first
+  // kRowPre * kThreads pieces are loaded now (the sources do not depend on
+  // the selection), so that only their stores are left at the end
+  const int cpr = row_bytes >> 4;
+  const int j_lo = static_cast<int>(static_cast<int64_t>(part) * S / parts);
+  const int j_hi = static_cast<int>(static_cast<int64_t>(part + 1) * S / parts);
+  const int n_items = row_bytes > 0 ? (j_hi - j_lo) * cpr : 0;
+  auto item_src = [&](int idx) __attribute__((always_inline)) {
+    const int jj = j_lo + idx / cpr, c = idx - (idx / cpr) * cpr;
+    return (static_cast<size_t>(bh) * S + jj) * row_bytes + 16 * c;
+  };
+  u32x4 rk[kRowPre], rv[kRowPre];
+#pragma unroll
+  for (int u = 0; u < kRowPre; ++u) {
+    const int idx = tid + u * kThreads;
+    if (idx < n_items) {
+      rk[u] = load_u32x4(kn + item_src(idx));
+      rv[u] = load_u32x4(vn + item_src(idx));
+    }
+  }
 
   // 0. loads.  The thread's slots first (position, score, the per-split
   // masses), then the chunk keys' masses, summed in split order into s_mu;
@@ -256,7 +301,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       if (exists) fmask |= 1u << i;
     }
     if (!exists) cmask &= ~(1u << i);
-    if (step_mass && exists) step_mass[static_cast<size_t>(bh) * PS + m] = ds;
+    if (step_mass && exists && part == 0) step_mass[static_cast<size_t>(bh) * PS + m] = ds;
     key[i] = POS ? static_cast<uint32_t>(pv[i]) : order_key(sc);
     if ((cmask >> i) & 1u) {
       k_and &= key[i];
@@ -278,7 +323,29 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       s_red[2][wave] = static_cast<int>(wo);
     }
   }
+  wait_vmem_all();
   barrier_lds();
+  // every thread's reads of the old scores, positions and masses are done:
+  // a part other than 0 says so
+  if (part > 0 && tid == 0) __hip_atomic_fetch_add(sync + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // part 0, before it rewrites scores or positions: wait until every other
+  // part has read them (the host's running total of such reads), bounded
+  auto wait_readers = [&]() __attribute__((always_inline)) {
+    if (parts > 1) {
+      if (tid == 0) {
+        uint32_t it = 0;
+        while (static_cast<int32_t>(__hip_atomic_load(sync + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+                                    sync_target) < 0) {
+          if (++it > spin_limit) {
+            atomicOr(status, 2);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      barrier_lds();
+    }
+  };
   int tot = 0;
   uint32_t all_and = 0xffffffffu, all_or = 0u;
 #pragma unroll
@@ -294,7 +361,10 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     // infeasible adopted state: no slot is written.  Every optional output
     // is still defined: slot and old position -1 (outside [0, M), so the
     // backward walk skips the token), the chunk keys' masses as computed,
-    // zero old rows (the scatter kernel zeroes them for longer chunks)
+    // zero old rows (the scatter kernel zeroes them for longer chunks).
+    // Part 0 writes all of it.
+    if (part != 0) return;
+    wait_readers();
     if constexpr (!POS) {
 #pragma unroll
       for (int i = 0; i < SPT; ++i)
@@ -445,14 +515,19 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       nsc[i] = mu;
       npos[i] = T + jj;
       tmask |= 1u << i;
-      targets[r] = v;
-      if (slots_out) slots_out[r] = m;
-      if (pos_old) pos_old[r] = pv[i];
-      if (step_mass) step_mass[static_cast<size_t>(bh) * PS + M + jj] = mu;
+      if (part == 0) {
+        targets[r] = v;
+        if (slots_out) slots_out[r] = m;
+        if (pos_old) pos_old[r] = pv[i];
+        if (step_mass) step_mass[static_cast<size_t>(bh) * PS + M + jj] = mu;
+      }
       if (row_bytes > 0) s_R[jj] = v;
     }
   }
-  if constexpr (POS) {
+  if (part == 0) wait_readers();
+  if (part != 0) {
+    // only part 0 rewrites the head's scores and positions
+  } else if constexpr (POS) {
     // scores are not kept: a written slot's score is 0, the rest untouched
 #pragma unroll
     for (int i = 0; i < SPT; ++i)
@@ -476,20 +551,18 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     }
   }
 
-  // short chunks (row_bytes > 0): the chunk's K/V rows go to their targets
-  // here, as scatter_kernel would copy them (each slot has one writer; the
-  // target list is complete in LDS after the barrier)
+  // chunks up to kSelectPartRows (row_bytes > 0): this part's share of the
+  // chunk's K/V rows goes to their targets here, as scatter_kernel would copy
+  // them (each slot has one writer; the target list is complete in LDS after
+  // the barrier)
   if (row_bytes > 0) {
     barrier_lds();
-    const int cpr = row_bytes >> 4;
-    for (int idx = tid; idx < S * cpr; idx += kThreads) {
-      const int jj = idx / cpr, c = idx - jj * cpr;
+    auto put = [&](int idx, const u32x4& kv, const u32x4& vv) __attribute__((always_inline)) {
+      const int jj = j_lo + idx / cpr, c = idx - (idx / cpr) * cpr;
       const int t = s_R[jj];
       const int slot = t & ~kWasFree;
-      const size_t src = (static_cast<size_t>(bh) * S + jj) * row_bytes + 16 * c;
+      const size_t src = item_src(idx);
       const size_t dst = (static_cast<size_t>(bh) * M + slot) * row_bytes + 16 * c;
-      const u32x4 kv = load_u32x4(kn + src);
-      const u32x4 vv = load_u32x4(vn + src);
       if (k_old) {
         const u32x4 z = {0, 0, 0, 0};
         const bool was_free = (t & kWasFree) != 0;
@@ -498,7 +571,14 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       }
       store_u32x4(kc + dst, kv);
       store_u32x4(vc + dst, vv);
+    };
+#pragma unroll
+    for (int u = 0; u < kRowPre; ++u) {
+      const int idx = tid + u * kThreads;
+      if (idx < n_items) put(idx, rk[u], rv[u]);
     }
+    for (int idx = tid + kRowPre * kThreads; idx < n_items; idx += kThreads)
+      put(idx, load_u32x4(kn + item_src(idx)), load_u32x4(vn + item_src(idx)));
   }
 }
 
@@ -554,7 +634,18 @@ __global__ void reset_kernel(float* scores, int32_t* pos, int64_t n, int32_t* co
 
 }  // namespace
 
-bool select_copies_rows(const StepShape& sh) { return sh.S <= kSelectCopyRows; }
+bool select_copies_rows(const StepShape& sh) { return sh.S <= kSelectPartRows; }
+
+// Parts per head: one up to kSelectCopyRows tokens (one workgroup keeps up
+// with that little data); for longer chunks that the select copies, enough
+// for about half a workgroup per CU over all heads, at least 32 rows each.
+int select_parts(const StepShape& sh) {
+  if (sh.S <= kSelectCopyRows || sh.S > kSelectPartRows) return 1;
+  const int n_heads = sh.B * sh.Hkv;
+  int p = (sh.n_cu + 2 * n_heads - 1) / (2 * n_heads);
+  p = std::min(p, (sh.S + 31) / 32);
+  return std::max(p, 1);
+}
 
 // dynamic LDS of the select kernel: the chunk keys' masses (H2O), then the
 // target list of a chunk whose rows it copies
@@ -566,6 +657,7 @@ size_t select_lds_bytes(const StepShape& sh) {
 hipError_t launch_select(const StepShape& sh, const SelectArgs& a, int dtype, hipStream_t st) {
   const int row_bytes = select_copies_rows(sh) ? sh.D * (dtype == kBF16 ? 2 : 4) : 0;
   const int n_heads = sh.B * sh.Hkv;
+  const int parts = select_parts(sh);
   const size_t lds = select_lds_bytes(sh);
   auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
   const bool vec = sh.M % 4 == 0 && sh.S % 4 == 0 && al16(a.scores) && al16(a.pos) && al16(a.partial);
@@ -575,12 +667,13 @@ hipError_t launch_select(const StepShape& sh, const SelectArgs& a, int dtype, hi
                                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3(n_heads), dim3(kThreads), lds, st, a.scores, a.pos, a.partial, a.R,
+    hipLaunchKernelGGL(kern, dim3(n_heads * parts), dim3(kThreads), lds, st, a.scores, a.pos, a.partial, a.R,
                        a.targets, a.slots_out, a.pos_old, a.step_mass, a.status, a.T, sh.W, sh.S, sh.M, sh.n_cache,
                        sh.policy == 2 ? sh.n_sink : 0, static_cast<char*>(a.k_cache),
                        static_cast<char*>(a.v_cache), static_cast<const char*>(a.k_new),
                        static_cast<const char*>(a.v_new), static_cast<char*>(a.k_old),
-                       static_cast<char*>(a.v_old), row_bytes);
+                       static_cast<char*>(a.v_old), row_bytes, parts, a.sync, a.sync_target,
+                       a.spin_limit ? a.spin_limit : kSelectSpin);
     return hipGetLastError();
   };
   // slots per thread: the smallest power of two with 512 * SPT >= M (M <= 16384);

@@ -312,11 +312,12 @@ def test_scores_snapshot_and_timing_counters():
     assert e.value.status == h2o.H2O_ERR_SHAPE
 
 
-@pytest.mark.parametrize("S,M", [(16, 64), (300, 640)])
+@pytest.mark.parametrize("S,M", [(16, 64), (300, 640), (4160, 4352)])
 def test_infeasible_adopted_state_sets_device_status(S, M):
     """An adopted state with nothing evictable: no slot is written, the status
-    bit is set, and every optional output is still defined (S = 16: rows
-    handled by the select kernel; S = 300: by the scatter kernel)."""
+    bit is set, and every optional output is still defined (S = 16: one
+    select workgroup per head handles the rows; S = 300: several select
+    parts per head; S = 4160: the scatter kernel)."""
     h2o = h2o_mod()
     B, Hq, Hkv, d, W = 1, 2, 1, 64, 8
     cfg = h2o.H2OConfig(B, Hq, Hkv, d, M, W, S, M, "bf16")
