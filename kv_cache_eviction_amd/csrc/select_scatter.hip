@@ -142,7 +142,9 @@ __device__ void block_excl_scan2(int a, int b, int* tmp, int& pa, int& pb) {
 // past R re-read split R-1 and are not added); RMAX = 0 selects a position
 // policy (no masses).  VEC: M and S are multiples of 4 and the buffers are
 // 16-byte aligned, so slot rows and chunk masses move in 16-byte pieces.
-template <int SPT, int RMAX, bool VEC>
+// MP: several parts per head (the template keeps the single-part kernel free
+// of the parts' registers and handshake).
+template <int SPT, int RMAX, bool VEC, bool MP>
 __global__ __launch_bounds__(kThreads) void select_kernel(
     float* __restrict__ scores, int32_t* __restrict__ pos, const float* __restrict__ partial,
     int R, int32_t* __restrict__ targets, int32_t* __restrict__ slots_out,
@@ -165,9 +167,10 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   // workgroup -> (head, part): the parts of a head share its XCD when the
   // head count is a multiple of 8 (round-robin dispatch), so their reads of
   // the same scores and masses hit one L2
-  const int n_heads = static_cast<int>(gridDim.x) / parts;
-  const int bh = static_cast<int>(blockIdx.x) % n_heads;
-  const int part = static_cast<int>(blockIdx.x) / n_heads;
+  const int n_parts = MP ? parts : 1;
+  const int n_heads = static_cast<int>(gridDim.x) / n_parts;
+  const int bh = MP ? static_cast<int>(blockIdx.x) % n_heads : static_cast<int>(blockIdx.x);
+  const int pid = MP ? static_cast<int>(blockIdx.x) / n_heads : 0;
   const size_t PS = static_cast<size_t>(M) + S;
   const float* ph = partial + static_cast<size_t>(bh) * R * PS;
   float* sc_h = scores + static_cast<size_t>(bh) * M;
@@ -175,22 +178,26 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   const int m0 = tid * SPT;
   auto split_of = [&](int r) __attribute__((always_inline)) { return static_cast<size_t>(min(r, R - 1)) * PS; };
 
-  // this part's tokens and their K/V rows' 16-byte pieces; the first
-  // kRowPre * kThreads pieces are loaded now (the sources do not depend on
-  // the selection), so that only their stores are left at the end
+  // this part's tokens and their K/V rows' 16-byte pieces; with several
+  // parts the first kRowPre * kThreads pieces are loaded now (the sources do
+  // not depend on the selection), so that only their stores are left at the
+  // end (a single part per head, i.e. a chunk of at most 256 tokens, loads
+  // them at the end)
   const int cpr = row_bytes >> 4;
-  const int j_lo = static_cast<int>(static_cast<int64_t>(part) * S / parts);
-  const int j_hi = static_cast<int>(static_cast<int64_t>(part + 1) * S / parts);
+  const int j_lo = static_cast<int>(static_cast<int64_t>(pid) * S / n_parts);
+  const int j_hi = static_cast<int>(static_cast<int64_t>(pid + 1) * S / n_parts);
   const int n_items = row_bytes > 0 ? (j_hi - j_lo) * cpr : 0;
   auto item_src = [&](int idx) __attribute__((always_inline)) {
     const int jj = j_lo + idx / cpr, c = idx - (idx / cpr) * cpr;
     return (static_cast<size_t>(bh) * S + jj) * row_bytes + 16 * c;
   };
-  u32x4 rk[kRowPre], rv[kRowPre];
+  constexpr int NPRE = MP ? kRowPre : 1;
+  const int n_pre = MP ? min(n_items, kRowPre * kThreads) : 0;
+  u32x4 rk[NPRE], rv[NPRE];
 #pragma unroll
-  for (int u = 0; u < kRowPre; ++u) {
+  for (int u = 0; u < NPRE; ++u) {
     const int idx = tid + u * kThreads;
-    if (idx < n_items) {
+    if (idx < n_pre) {
       rk[u] = load_u32x4(kn + item_src(idx));
       rv[u] = load_u32x4(vn + item_src(idx));
     }
@@ -301,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       if (exists) fmask |= 1u << i;
     }
     if (!exists) cmask &= ~(1u << i);
-    if (step_mass && exists && part == 0) step_mass[static_cast<size_t>(bh) * PS + m] = ds;
+    if (step_mass && exists && pid == 0) step_mass[static_cast<size_t>(bh) * PS + m] = ds;
     key[i] = POS ? static_cast<uint32_t>(pv[i]) : order_key(sc);
     if ((cmask >> i) & 1u) {
       k_and &= key[i];
@@ -323,15 +330,17 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       s_red[2][wave] = static_cast<int>(wo);
     }
   }
-  wait_vmem_all();
+  if constexpr (MP) wait_vmem_all();
   barrier_lds();
   // every thread's reads of the old scores, positions and masses are done:
   // a part other than 0 says so
-  if (part > 0 && tid == 0) __hip_atomic_fetch_add(sync + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if constexpr (MP) {
+    if (pid > 0 && tid == 0) __hip_atomic_fetch_add(sync + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   // part 0, before it rewrites scores or positions: wait until every other
   // part has read them (the host's running total of such reads), bounded
   auto wait_readers = [&]() __attribute__((always_inline)) {
-    if (parts > 1) {
+    if constexpr (MP) {
       if (tid == 0) {
         uint32_t it = 0;
         while (static_cast<int32_t>(__hip_atomic_load(sync + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
@@ -363,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     // backward walk skips the token), the chunk keys' masses as computed,
     // zero old rows (the scatter kernel zeroes them for longer chunks).
     // Part 0 writes all of it.
-    if (part != 0) return;
+    if (pid != 0) return;
     wait_readers();
     if constexpr (!POS) {
 #pragma unroll
@@ -515,7 +524,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       nsc[i] = mu;
       npos[i] = T + jj;
       tmask |= 1u << i;
-      if (part == 0) {
+      if (pid == 0) {
         targets[r] = v;
         if (slots_out) slots_out[r] = m;
         if (pos_old) pos_old[r] = pv[i];
@@ -524,8 +533,8 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       if (row_bytes > 0) s_R[jj] = v;
     }
   }
-  if (part == 0) wait_readers();
-  if (part != 0) {
+  if (pid == 0) wait_readers();
+  if (pid != 0) {
     // only part 0 rewrites the head's scores and positions
   } else if constexpr (POS) {
     // scores are not kept: a written slot's score is 0, the rest untouched
@@ -573,11 +582,11 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       store_u32x4(vc + dst, vv);
     };
 #pragma unroll
-    for (int u = 0; u < kRowPre; ++u) {
+    for (int u = 0; u < NPRE; ++u) {
       const int idx = tid + u * kThreads;
-      if (idx < n_items) put(idx, rk[u], rv[u]);
+      if (idx < n_pre) put(idx, rk[u], rv[u]);
     }
-    for (int idx = tid + kRowPre * kThreads; idx < n_items; idx += kThreads)
+    for (int idx = n_pre + tid; idx < n_items; idx += kThreads)
       put(idx, load_u32x4(kn + item_src(idx)), load_u32x4(vn + item_src(idx)));
   }
 }
@@ -634,13 +643,18 @@ __global__ void reset_kernel(float* scores, int32_t* pos, int64_t n, int32_t* co
 
 }  // namespace
 
-bool select_copies_rows(const StepShape& sh) { return sh.S <= kSelectPartRows; }
+// Several parts need the 16-byte slot and mass loads (M and S multiples of
+// 4; the buffers are 16-byte aligned by validation); other shapes keep one
+// part and the scatter kernel above kSelectCopyRows.
+static bool parts_shape(const StepShape& sh) { return sh.M % 4 == 0 && sh.S % 4 == 0 && sh.S <= kSelectPartRows; }
+
+bool select_copies_rows(const StepShape& sh) { return sh.S <= kSelectCopyRows || parts_shape(sh); }
 
 // Parts per head: one up to kSelectCopyRows tokens (one workgroup keeps up
 // with that little data); for longer chunks that the select copies, enough
 // for about half a workgroup per CU over all heads, at least 32 rows each.
 int select_parts(const StepShape& sh) {
-  if (sh.S <= kSelectCopyRows || sh.S > kSelectPartRows) return 1;
+  if (sh.S <= kSelectCopyRows || !parts_shape(sh)) return 1;
   const int n_heads = sh.B * sh.Hkv;
   int p = (sh.n_cu + 2 * n_heads - 1) / (2 * n_heads);
   p = std::min(p, (sh.S + 31) / 32);
@@ -678,25 +692,31 @@ hipError_t launch_select(const StepShape& sh, const SelectArgs& a, int dtype, hi
   };
   // slots per thread: the smallest power of two with 512 * SPT >= M (M <= 16384);
   // split bound: the smallest power of two >= R (0: position policy)
-  auto by_spt = [&](auto rmax, auto vv) -> hipError_t {
+  auto by_spt = [&](auto rmax, auto vv, auto mp) -> hipError_t {
     constexpr int RM = decltype(rmax)::value;
     constexpr bool V = decltype(vv)::value;
-    if (sh.M <= kThreads) return go(select_kernel<1, RM, V>);
-    if (sh.M <= 2 * kThreads) return go(select_kernel<2, RM, V>);
-    if (sh.M <= 4 * kThreads) return go(select_kernel<4, RM, V>);
-    if (sh.M <= 8 * kThreads) return go(select_kernel<8, RM, V>);
-    if (sh.M <= 16 * kThreads) return go(select_kernel<16, RM, V>);
-    return go(select_kernel<32, RM, V>);
+    constexpr bool MPv = decltype(mp)::value;
+    if (sh.M <= kThreads) return go(select_kernel<1, RM, V, MPv>);
+    if (sh.M <= 2 * kThreads) return go(select_kernel<2, RM, V, MPv>);
+    if (sh.M <= 4 * kThreads) return go(select_kernel<4, RM, V, MPv>);
+    if (sh.M <= 8 * kThreads) return go(select_kernel<8, RM, V, MPv>);
+    if (sh.M <= 16 * kThreads) return go(select_kernel<16, RM, V, MPv>);
+    return go(select_kernel<32, RM, V, MPv>);
   };
-  auto by_r = [&](auto vv) -> hipError_t {
-    if (sh.policy != 0) return by_spt(std::integral_constant<int, 0>{}, vv);
-    if (a.R <= 1) return by_spt(std::integral_constant<int, 1>{}, vv);
-    if (a.R <= 2) return by_spt(std::integral_constant<int, 2>{}, vv);
-    if (a.R <= 4) return by_spt(std::integral_constant<int, 4>{}, vv);
-    if (a.R <= 8) return by_spt(std::integral_constant<int, 8>{}, vv);
-    return by_spt(std::integral_constant<int, kMaxSplits>{}, vv);
+  auto by_r = [&](auto vv, auto mp) -> hipError_t {
+    if (sh.policy != 0) return by_spt(std::integral_constant<int, 0>{}, vv, mp);
+    if (a.R <= 1) return by_spt(std::integral_constant<int, 1>{}, vv, mp);
+    if (a.R <= 2) return by_spt(std::integral_constant<int, 2>{}, vv, mp);
+    if (a.R <= 4) return by_spt(std::integral_constant<int, 4>{}, vv, mp);
+    if (a.R <= 8) return by_spt(std::integral_constant<int, 8>{}, vv, mp);
+    return by_spt(std::integral_constant<int, kMaxSplits>{}, vv, mp);
   };
-  return vec ? by_r(std::true_type{}) : by_r(std::false_type{});
+  // several parts only with the 16-byte loads (parts_shape)
+  if (parts > 1) {
+    if (!vec) return hipErrorInvalidValue;
+    return by_r(std::true_type{}, std::true_type{});
+  }
+  return vec ? by_r(std::true_type{}, std::false_type{}) : by_r(std::false_type{}, std::false_type{});
 }
 
 hipError_t launch_scatter(const StepShape& sh, const SelectArgs& a, int dtype, hipStream_t st) {
