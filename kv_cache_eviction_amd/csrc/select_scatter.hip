@@ -37,9 +37,11 @@
 // are done, and part 0 rewrites those arrays only after the counter has
 // reached the running total of reads the host expects.  That wait is
 // bounded: past kSelectSpin polls part 0 sets bit 1 of the status word and
-// writes anyway.  Chunks longer than kSelectPartRows tokens (whose target
-// lists would not fit LDS) keep one part that copies no rows, and the
-// scatter kernel copies them with many workgroups per head.
+// writes anyway.  Chunks of at most kSelectCopyRows tokens take one part
+// per head.  Chunks longer than kSelectPartRows tokens (whose target lists
+// would not fit LDS), or whose slot count or length is not a multiple of 4,
+// keep one part that copies no rows, and the scatter kernel copies them with
+// many workgroups per head.
 #include <algorithm>
 #include <type_traits>
 

@@ -302,6 +302,8 @@ def h2o_tokens_seen(handle) -> int:
 
 
 def h2o_device_status(handle, stream=None) -> int:
+    """Device status word (bit 0: an adopted state had too few evictable
+    slots; bit 1: the select's bounded wait gave up), cleared by the read."""
     flags = ctypes.c_int32()
     _check(_lib.h2o_device_status(handle, _stream(stream), ctypes.byref(flags)), "h2o_device_status")
     return flags.value
