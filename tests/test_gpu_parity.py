@@ -95,6 +95,13 @@ SMALL_BF16 = {
                         total_len=600 + 64 * 4, cache_slots=700, recent_window=50, qk_std=1.0),
     "g1_m8200_d64": dict(batch=1, n_q_heads=1, n_kv_heads=1, head_dim=64, prefill=8192, chunk=40,
                          total_len=8192 + 40 * 3, cache_slots=8200, recent_window=64, qk_std=1.0),
+    # chunks of 257..4096 tokens: several select workgroups per head, each
+    # copying a share of the rows (M and S multiples of 4) ...
+    "g4_s300_parts": dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=64, prefill=320, chunk=300,
+                          total_len=320 + 300 * 4, cache_slots=704, recent_window=40, qk_std=1.0),
+    # ... or one select workgroup and the scatter kernel (S not a multiple of 4)
+    "g2_s301_scatter": dict(batch=1, n_q_heads=4, n_kv_heads=2, head_dim=128, prefill=258, chunk=301,
+                            total_len=258 + 301 * 4, cache_slots=700, recent_window=30, qk_std=1.0),
 }
 
 
