@@ -40,8 +40,9 @@
 // writes anyway.  Chunks of at most kSelectCopyRows tokens take one part
 // per head.  Chunks longer than kSelectPartRows tokens (whose target lists
 // would not fit LDS), or whose slot count or length is not a multiple of 4,
-// keep one part that copies no rows, and the scatter kernel copies them with
-// many workgroups per head.
+// or whose heads are so many that one part per head already fills half the
+// CUs, keep one part that copies no rows, and the scatter kernel copies them
+// with many workgroups per head.
 #include <algorithm>
 #include <type_traits>
 
@@ -650,11 +651,11 @@ __global__ void reset_kernel(float* scores, int32_t* pos, int64_t n, int32_t* co
 // part and the scatter kernel above kSelectCopyRows.
 static bool parts_shape(const StepShape& sh) { return sh.M % 4 == 0 && sh.S % 4 == 0 && sh.S <= kSelectPartRows; }
 
-bool select_copies_rows(const StepShape& sh) { return sh.S <= kSelectCopyRows || parts_shape(sh); }
-
 // Parts per head: one up to kSelectCopyRows tokens (one workgroup keeps up
-// with that little data); for longer chunks that the select copies, enough
-// for about half a workgroup per CU over all heads, at least 32 rows each.
+// with that little data); for longer chunks, enough for about half a
+// workgroup per CU over all heads, at least 32 rows each.  A long chunk left
+// with one part (many heads) is copied by the scatter kernel instead: one
+// workgroup per head would be bound by its own copy bandwidth.
 int select_parts(const StepShape& sh) {
   if (sh.S <= kSelectCopyRows || !parts_shape(sh)) return 1;
   const int n_heads = sh.B * sh.Hkv;
@@ -662,6 +663,8 @@ int select_parts(const StepShape& sh) {
   p = std::min(p, (sh.S + 31) / 32);
   return std::max(p, 1);
 }
+
+bool select_copies_rows(const StepShape& sh) { return sh.S <= kSelectCopyRows || select_parts(sh) > 1; }
 
 // dynamic LDS of the select kernel: the chunk keys' masses (H2O), then the
 // target list of a chunk whose rows it copies
