@@ -155,6 +155,9 @@ h2o::StepShape shape_of(const h2o_cache* c, int s) {
   sh.policy = g.policy;
   sh.n_sink = g.n_sink;
   sh.n_cu = c->n_cu;
+  // slots never become free again in forward steps: once the count of filled
+  // slots reached M (known unless the state was adopted), all are filled
+  sh.all_filled = c->filled == g.cache_slots;
   return sh;
 }
 

@@ -83,7 +83,10 @@ __device__ __forceinline__ int v_chunk(int row, int c) {
   return c ^ ((row & 3) << (CPR == 16 ? 2 : 1));
 }
 
-template <int D, bool DEC, bool SKIP>
+// ALLF: every cache slot holds a token (known on the host once the cache has
+// filled), so no tile needs its keys' positions: no position copies, and
+// only keys past the last slot are masked.
+template <int D, bool DEC, bool SKIP, bool ALLF>
 __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc,
     const bf16_t* __restrict__ Vc, const int32_t* __restrict__ pos,
@@ -300,12 +303,15 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   // compiler, whose wait for it would also wait for the untracked tile
   // copies issued after it (vmcnt retires in order).
   auto issue_pos = [&](int T) __attribute__((always_inline)) {
-    const int Tc = T0 + min(T, n_tiles - 1);
-    dma4_lds(r_pos, s_pos[grp][rbw][(T >> 1) & 3], 4u * static_cast<uint32_t>(min(Tc * kKT + lane, M - 1)), 0u);
+    if constexpr (!ALLF) {
+      const int Tc = T0 + min(T, n_tiles - 1);
+      dma4_lds(r_pos, s_pos[grp][rbw][(T >> 1) & 3], 4u * static_cast<uint32_t>(min(Tc * kKT + lane, M - 1)), 0u);
+    }
   };
   // position of this lane's key in local tile T (cache tiles; -1 = free or past the end)
   auto pos_of = [&](int T) __attribute__((always_inline)) {
     const int key = (T0 + T) * kKT + lane;
+    if constexpr (ALLF) return key < n_cache ? 0 : -1;
     const int p = s_pos[grp][rbw][(T >> 1) & 3][lane];
     return key < n_cache ? p : -1;
   };
@@ -460,7 +466,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void attn_fwd_bf16_kernel(
   // slots it just read, three phases before their use.  Each group runs its
   // own loop (same barrier count), so that each carries only its own state
   // across iterations (group 0 P, group 1 S) and its buffers are fixed.
-  constexpr int kLoadsPerIter = 1 + 2 * NDMA;
+  constexpr int kLoadsPerIter = (ALLF ? 0 : 1) + 2 * NDMA;
   constexpr int kWaitPrev = 0x0f70 | (kLoadsPerIter & 15) | ((kLoadsPerIter >> 4) << 14);
   auto run_group = [&](auto g) __attribute__((always_inline)) {
     constexpr int GG = decltype(g)::value;
@@ -761,17 +767,18 @@ hipError_t launch_attn_fwd(const StepShape& sh, const AttnArgs& a, int dtype, hi
       while (n_split > 1 && static_cast<int64_t>(sh.B) * sh.Hq * sh.S * n_split > kSplitRows) --n_split;
     }
     const dim3 grid(n_heads * wgp * n_split), block(kFwdThreads);
-#define H2O_LAUNCH_FWD1(DD, DEC, SK)                                                                \
-  hipLaunchKernelGGL(HIP_KERNEL_NAME(attn_fwd_bf16_kernel<DD, DEC, SK>), grid, block, 0, st,        \
+#define H2O_LAUNCH_FWD1(DD, DEC, SK, AF)                                                            \
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(attn_fwd_bf16_kernel<DD, DEC, SK, AF>), grid, block, 0, st,    \
                      static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k_cache),        \
                      static_cast<const bf16_t*>(a.v_cache), a.pos,                                  \
                      static_cast<const bf16_t*>(a.k_new), static_cast<const bf16_t*>(a.v_new),      \
                      static_cast<bf16_t*>(a.out), a.lse, sh.Hq, sh.Hkv, sh.S, sh.M, sh.n_cache, c2, \
                      n_heads, wgp, n_split, a.part)
-#define H2O_LAUNCH_FWD(DD)                          \
-  if (dec) H2O_LAUNCH_FWD1(DD, true, false);        \
-  else if (n_split > 1) H2O_LAUNCH_FWD1(DD, false, true); \
-  else H2O_LAUNCH_FWD1(DD, false, false)
+#define H2O_LAUNCH_FWD(DD)                                    \
+  if (dec) H2O_LAUNCH_FWD1(DD, true, false, false);           \
+  else if (n_split > 1) H2O_LAUNCH_FWD1(DD, false, true, false); \
+  else if (sh.all_filled) H2O_LAUNCH_FWD1(DD, false, false, true); \
+  else H2O_LAUNCH_FWD1(DD, false, false, false)
     if (sh.D == 128) {
       H2O_LAUNCH_FWD(128);
     } else {

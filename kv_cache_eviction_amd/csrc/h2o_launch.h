@@ -15,6 +15,7 @@ struct StepShape {
   int policy = 0;   // 0 H2O (score key), 1 recent, 2 sink_recent (position key)
   int n_sink = 0;   // sink_recent: positions below n_sink are never evicted
   int n_cu = 256;   // compute units of the device (sizes the grids of small steps)
+  bool all_filled = false;   // every one of the M slots holds a token (known on the host)
 };
 
 struct AttnArgs {
