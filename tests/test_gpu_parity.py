@@ -358,3 +358,39 @@ def test_infeasible_adopted_state_sets_device_status(S, M):
     assert (m > 0).all()
     assert torch.allclose(m.sum(-1), torch.full((B, Hkv), float(S * Hq // Hkv), dtype=torch.float64), rtol=1e-5)
     assert torch.allclose(m[..., :M], (state[2] - before[2]).double().cpu(), rtol=1e-6, atol=0)
+
+
+def test_filled_cache_attention_equals_the_general_one():
+    """Once the cache has filled, the forward skips the per-tile position
+    copies; an adopted copy of the same state (whose fill the library cannot
+    know) takes the general forward.  The two must agree bit for bit: every
+    output, logsumexp and the final state (64k shape, 3 evicting steps)."""
+    h2o = h2o_mod()
+    w = wl.workload("llama8b_64k", total_len=2048 + 1024 * 3)
+    cfg = cfg_of(w)
+    hh = wl.heavy_hitters(w, 0)
+    chunks = [tuple(to_device(x) for x in wl.chunk_inputs(w, 0, c, hh=hh)) for c in range(w.n_chunks)]
+
+    def steps(cache):
+        res = []
+        for q, k, v in chunks[1:]:
+            lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+            out = cache.chunk_step(q, k, v, lse=lse)
+            res.append((out, lse))
+        torch.cuda.synchronize()
+        return res
+
+    filled = h2o.H2OCache(cfg)
+    filled.prefill(*chunks[0])
+    torch.cuda.synchronize()
+    state = tuple(t.clone() for t in (filled.k_cache, filled.v_cache, filled.scores, filled.positions))
+    assert int(state[3].min()) >= 0                   # the prefill filled every slot
+    adopted = h2o.H2OCache(cfg, adopt_state=state, tokens_seen=filled.tokens_seen)
+    a, b = steps(filled), steps(adopted)
+    for c, ((o1, l1), (o2, l2)) in enumerate(zip(a, b)):
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), ("out", c)
+        assert torch.equal(l1.view(torch.int32), l2.view(torch.int32)), ("lse", c)
+    for t in ("k_cache", "v_cache", "scores", "positions"):
+        x, y = getattr(filled, t), getattr(adopted, t)
+        bits = torch.int16 if x.dtype == torch.bfloat16 else torch.int32
+        assert torch.equal(x.view(bits), y.view(bits)), t
