@@ -59,7 +59,7 @@ constexpr int kDigitBits = 11; // radix digit: 2048-bin histograms
 constexpr int kBins = 1 << kDigitBits;
 // chunks up to this length copy their K/V rows inside the select kernel (one
 // workgroup per head keeps up with that little data, and a launch is saved);
-// longer chunks use the many-workgroup scatter kernel
+// longer chunks take several parts or the many-workgroup scatter kernel
 constexpr int kSelectCopyRows = 256;
 // longer chunks, up to this length, are selected by several parts per head
 // that each copy a share of the rows; beyond it the scatter kernel copies
