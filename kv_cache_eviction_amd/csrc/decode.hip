@@ -62,7 +62,9 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, const void* lds_b
   asm volatile("buffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(m0) : "memory");
 }
 
-template <int D>
+// ALLF: every cache slot holds a token (known on the host once the cache has
+// filled): no position copies, and only keys past the last slot are masked.
+template <int D, bool ALLF>
 __global__ __launch_bounds__(kDW * 64, 1) void decode_fused_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
     const int32_t* __restrict__ pos, const bf16_t* __restrict__ Kn, const bf16_t* __restrict__ Vn,
@@ -150,7 +152,8 @@ __global__ __launch_bounds__(kDW * 64, 1) void decode_fused_kernel(
     const uint32_t soff = static_cast<uint32_t>(base) * RB;
     // the block's positions (lane k < 32: slot base + k; chunk blocks copy
     // positions they never read)
-    dma4(r_pos, s_pos[wave][slot], 4u * static_cast<uint32_t>(min(base + (lane & 31), M - 1)), 0u);
+    if constexpr (!ALLF)
+      dma4(r_pos, s_pos[wave][slot], 4u * static_cast<uint32_t>(min(base + (lane & 31), M - 1)), 0u);
     if (n_valid >= 32) {
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
@@ -210,14 +213,15 @@ __global__ __launch_bounds__(kDW * 64, 1) void decode_fused_kernel(
   // its LDS reads are done), s + 2 goes into its slot.  Every global read
   // is a copy into LDS, so the compiler inserts no waits of its own and each
   // wait below is exact: the copies of the items issued after s.
-  auto ops = [&](int s) { return s < nbw ? NC + 1 : NC; };
+  constexpr int KOPS = NC + (ALLF ? 0 : 1);              // copies of a K item (rows, positions)
+  auto ops = [&](int s) { return s < nbw ? KOPS : NC; };
   auto issue = [&](int s) __attribute__((always_inline)) {
     if (s < nbw) issue_k(s, s & 1);
     else if (s < 2 * nbw) issue_v(s - nbw, s & 1);
   };
   auto wait_for = [&](int s) __attribute__((always_inline)) {
     if (s + 1 < 2 * nbw) {
-      if (ops(s + 1) == NC + 1) __builtin_amdgcn_s_waitcnt(0x0f70 | ((NC + 1) & 15) | (((NC + 1) >> 4) << 14));
+      if (ops(s + 1) == KOPS) __builtin_amdgcn_s_waitcnt(0x0f70 | (KOPS & 15) | ((KOPS >> 4) << 14));
       else __builtin_amdgcn_s_waitcnt(0x0f70 | (NC & 15) | ((NC >> 4) << 14));
     } else {
       wait_vmem_all();
@@ -238,12 +242,12 @@ __global__ __launch_bounds__(kDW * 64, 1) void decode_fused_kernel(
   }
   issue(0);
   issue(1);
-  if (nbw >= 2) {
-    const int n = ops(0) + ops(1);
-    if (n == 2 * NC + 2) __builtin_amdgcn_s_waitcnt(0x0f70 | ((2 * NC + 2) & 15) | (((2 * NC + 2) >> 4) << 14));
-    else __builtin_amdgcn_s_waitcnt(0x0f70 | ((2 * NC + 1) & 15) | (((2 * NC + 1) >> 4) << 14));
-  } else if (nbw == 1) {
-    __builtin_amdgcn_s_waitcnt(0x0f70 | ((2 * NC + 1) & 15) | (((2 * NC + 1) >> 4) << 14));   // items 0 (K) and 1 (V)
+  if (nbw >= 2) {                                            // items 0 and 1 (both K)
+    constexpr int N2 = 2 * KOPS;
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (N2 & 15) | ((N2 >> 4) << 14));
+  } else if (nbw == 1) {                                     // items 0 (K) and 1 (V)
+    constexpr int N2 = KOPS + NC;
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (N2 & 15) | ((N2 >> 4) << 14));
   } else {
     wait_vmem_all();
   }
@@ -278,8 +282,11 @@ __global__ __launch_bounds__(kDW * 64, 1) void decode_fused_kernel(
       uint32_t vis;                                       // bit k: key k of the block is visible to this row
       if (bi < ncb) {
         const int n_valid = n_cache - 32 * bi;
-        const int pk = s_pos[wave][i & 1][lane];
-        const uint32_t filled = static_cast<uint32_t>(__ballot(lane < 32 && pk >= 0));
+        uint32_t filled = 0xffffffffu;
+        if constexpr (!ALLF) {
+          const int pk = s_pos[wave][i & 1][lane];
+          filled = static_cast<uint32_t>(__ballot(lane < 32 && pk >= 0));
+        }
         vis = filled & (n_valid >= 32 ? 0xffffffffu : ((1u << n_valid) - 1u));
       } else {
         const int j0 = 32 * (bi - ncb);
@@ -492,15 +499,22 @@ hipError_t launch_decode_fused(const StepShape& sh, const AttnArgs& a, float* pa
   const int n_heads = sh.B * sh.Hkv;
   const float c2 = sh.scale * kLog2e;
   const dim3 grid(n_heads * halves), block(kDW * 64);
-#define H2O_LAUNCH_DEC(DD)                                                                               \
-  hipLaunchKernelGGL(decode_fused_kernel<DD>, grid, block, 0, st, static_cast<const bf16_t*>(a.q),      \
+#define H2O_LAUNCH_DEC1(DD, AF)                                                                          \
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(decode_fused_kernel<DD, AF>), grid, block, 0, st, static_cast<const bf16_t*>(a.q), \
                      static_cast<const bf16_t*>(a.k_cache), static_cast<const bf16_t*>(a.v_cache), a.pos, \
                      static_cast<const bf16_t*>(a.k_new), static_cast<const bf16_t*>(a.v_new),          \
                      static_cast<bf16_t*>(a.out), a.lse, partial, sh.Hq, sh.Hkv, sh.S, sh.M, sh.n_cache, c2, \
                      n_heads, halves)
-  if (sh.D == 128) H2O_LAUNCH_DEC(128);
-  else H2O_LAUNCH_DEC(64);
+#define H2O_LAUNCH_DEC(DD)                  \
+  if (sh.all_filled) H2O_LAUNCH_DEC1(DD, true); \
+  else H2O_LAUNCH_DEC1(DD, false)
+  if (sh.D == 128) {
+    H2O_LAUNCH_DEC(128);
+  } else {
+    H2O_LAUNCH_DEC(64);
+  }
 #undef H2O_LAUNCH_DEC
+#undef H2O_LAUNCH_DEC1
   return hipGetLastError();
 }
 

@@ -360,13 +360,19 @@ def test_infeasible_adopted_state_sets_device_status(S, M):
     assert torch.allclose(m[..., :M], (state[2] - before[2]).double().cpu(), rtol=1e-6, atol=0)
 
 
-def test_filled_cache_attention_equals_the_general_one():
-    """Once the cache has filled, the forward skips the per-tile position
-    copies; an adopted copy of the same state (whose fill the library cannot
-    know) takes the general forward.  The two must agree bit for bit: every
-    output, logsumexp and the final state (64k shape, 3 evicting steps)."""
+@pytest.mark.parametrize("name,overrides", [
+    ("llama8b_64k", dict(total_len=2048 + 1024 * 3)),            # long-chunk forward
+    ("decode_b32", dict(batch=4, total_len=2048 + 16 * 6)),        # fused short-chunk kernel
+    ("llama8b_64k_s128", dict(total_len=2048 + 128 * 4)),          # fused kernel, 16 row parts
+])
+def test_filled_cache_attention_equals_the_general_one(name, overrides):
+    """Once the cache has filled, the forward (and the fused short-chunk
+    kernel) skips the per-tile position copies; an adopted copy of the same
+    state (whose fill the library cannot know) takes the general kernels.
+    The two must agree bit for bit: every output, logsumexp and the final
+    state."""
     h2o = h2o_mod()
-    w = wl.workload("llama8b_64k", total_len=2048 + 1024 * 3)
+    w = wl.workload(name, **overrides)
     cfg = cfg_of(w)
     hh = wl.heavy_hitters(w, 0)
     chunks = [tuple(to_device(x) for x in wl.chunk_inputs(w, 0, c, hh=hh)) for c in range(w.n_chunks)]
